@@ -1,0 +1,103 @@
+"""Seeded synthetic inputs for exact attention (shared by tests, bench and smoke).
+
+This module holds no attention arithmetic: it only draws random numbers,
+rounds them to bfloat16 and names the workload shapes.  Both the HIP path and
+the CPU oracle receive exactly the arrays produced here.
+
+Recipe (every workload):
+  * ``numpy.random.Generator(PCG64(seed))``; draws in a fixed order Q, K, V, dO,
+    each ``standard_normal(shape, float32) * sigma``;
+  * each float32 value is rounded once to bfloat16 with round-to-nearest-even
+    on its bit pattern (``round_to_bf16_bits``);
+  * the "spike" workload then draws one row index r[b, h] ~ U{0..N-1} per
+    (batch, head) from the same generator and multiplies row r of Q and of K
+    by 8 before rounding (a power of two, so exact), widening the score range
+    the softmax must handle.
+
+Workload shapes follow the attention benchmark sweeps on the "FlashAttention-2:
+Faster Attention with Better Parallelism and Work Partitioning" page (Figures
+4-7: head dimension 64 / 128, causal and non-causal, sequence lengths up to
+16k) and the GPT-3 2.7B-shaped layer of its Table 1 (hidden 2560, 32 heads of
+80).  Arrays are uint16 bit patterns ``[B, H, N, d]`` (d fastest).
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    sigma: float = 1.0
+    spike: bool = False
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    def flops(self, phase: str) -> float:
+        """Conventional attention flop count: 4*B*H*N^2*d forward, 2.5x that
+        backward, halved when causal."""
+        fwd = 4.0 * self.B * self.H * self.N * self.N * self.d
+        if self.causal:
+            fwd /= 2.0
+        return {"fwd": fwd, "bwd": 2.5 * fwd, "fwdbwd": 3.5 * fwd}[phase]
+
+
+WORKLOADS = {
+    "c1": Workload("c1", "single-head B1 H1 N128 d64 non-causal", 1, 1, 128, 64, False),
+    "c2": Workload("c2", "B8 H16 N2048 d128 non-causal (hidden 2048)", 8, 16, 2048, 128, False),
+    "c3": Workload("c3", "B4 H32 N4096 d64 causal (hidden 2048)", 4, 32, 4096, 64, True),
+    "c4": Workload("c4", "long-sequence B1 H16 N16384 d128 causal", 1, 16, 16384, 128, True),
+    "c5": Workload("c5", "GPT-2.7B-shaped B2 H32 N8192 d80 causal, sigma 0.5 + one x8 row/head",
+                   2, 32, 8192, 80, True, sigma=0.5, spike=True),
+}
+
+
+def round_to_bf16_bits(x) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    NaN stays a quiet NaN; values past the largest finite bfloat16 round to
+    infinity as IEEE round-to-nearest requires.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    nan = np.isnan(x)
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out = np.where(nan, ((u >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16), out)
+    return out
+
+
+def make_arrays(B, H, N, d, seed=0, sigma=1.0, spike=False):
+    """Q, K, V, dO as uint16 bf16 patterns [B,H,N,d] plus the spike rows (or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    draws = []
+    for _ in range(4):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        draws.append(x)
+    rows = None
+    if spike:
+        rows = rng.integers(0, N, size=(B, H))
+        bi, hi = np.meshgrid(np.arange(B), np.arange(H), indexing="ij")
+        draws[0][bi, hi, rows] *= np.float32(8.0)
+        draws[1][bi, hi, rows] *= np.float32(8.0)
+    q, k, v, do = (round_to_bf16_bits(x) for x in draws)
+    return {"q": q, "k": k, "v": v, "do": do, "spike_rows": rows}
+
+
+def make_workload(key, seed=0):
+    w = WORKLOADS[key]
+    return w, make_arrays(w.B, w.H, w.N, w.d, seed=seed, sigma=w.sigma, spike=w.spike)

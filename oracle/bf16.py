@@ -1,0 +1,20 @@
+"""Exact decoding of bfloat16 bit patterns (oracle side; test infrastructure only).
+
+A bfloat16 value is the upper 16 bits of an IEEE-754 binary32 value, so
+shifting the 16-bit pattern into the top half of a 32-bit word and
+reinterpreting it as float32 recovers the value exactly; widening float32 to
+float64 is exact too.
+"""
+
+import numpy as np
+
+
+def bf16_bits_to_float64(bits) -> np.ndarray:
+    """uint16 (or int16) bfloat16 bit patterns -> float64 values, exactly."""
+    b = np.asarray(bits)
+    if b.dtype == np.int16:
+        b = b.view(np.uint16)
+    if b.dtype != np.uint16:
+        raise TypeError(f"expected uint16/int16 bit patterns, got {b.dtype}")
+    words = b.astype(np.uint32) << np.uint32(16)
+    return words.view(np.float32).astype(np.float64)

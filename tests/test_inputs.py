@@ -1,0 +1,75 @@
+"""The seeded input generator: determinism, rounding, and the workload recipes (no GPU)."""
+
+import numpy as np
+import pytest
+
+import fa2_inputs as gen
+from oracle import bf16_bits_to_float64
+
+
+def test_rne_rounding_ties_and_specials():
+    words = np.array([
+        0x3F800000,  # 1.0 exactly
+        0x3F808000,  # halfway, lower kept bit even -> down to 0x3F80
+        0x3F818000,  # halfway, lower kept bit odd  -> up to 0x3F82
+        0x3F808001,  # just above halfway -> up
+        0x3F807FFF,  # just below halfway -> down
+        0x7F7FFFFF,  # largest float32 -> rounds to +inf in bf16
+        0xFF800000,  # -inf
+        0x00000001,  # tiny denormal -> +0
+    ], dtype=np.uint32)
+    got = gen.round_to_bf16_bits(words.view(np.float32))
+    assert got.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0x3F80, 0x7F80, 0xFF80, 0x0000]
+    nan = gen.round_to_bf16_bits(np.array([np.nan], dtype=np.float32))
+    assert np.isnan(bf16_bits_to_float64(nan)[0])
+
+
+def test_rounding_error_is_at_most_half_ulp():
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32)
+    r = bf16_bits_to_float64(gen.round_to_bf16_bits(x))
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(x.astype(np.float64)))) - 7)
+    assert np.all(np.abs(r - x) <= ulp / 2)
+
+
+def test_deterministic_and_seed_dependent():
+    a = gen.make_arrays(2, 3, 40, 16, seed=5)
+    b = gen.make_arrays(2, 3, 40, 16, seed=5)
+    c = gen.make_arrays(2, 3, 40, 16, seed=6)
+    for key in ("q", "k", "v", "do"):
+        assert a[key].dtype == np.uint16 and a[key].shape == (2, 3, 40, 16)
+        assert np.array_equal(a[key], b[key])
+        assert not np.array_equal(a[key], c[key])
+    assert not np.array_equal(a["q"], a["k"])
+
+
+def test_spike_rows_are_exact_x8_and_sigma():
+    plain = gen.make_arrays(2, 4, 64, 80, seed=3, sigma=0.5, spike=False)
+    spiky = gen.make_arrays(2, 4, 64, 80, seed=3, sigma=0.5, spike=True)
+    rows = spiky["spike_rows"]
+    assert rows.shape == (2, 4)
+    for name in ("q", "k"):
+        p = bf16_bits_to_float64(plain[name])
+        s = bf16_bits_to_float64(spiky[name])
+        for b in range(2):
+            for h in range(4):
+                r = rows[b, h]
+                np.testing.assert_array_equal(s[b, h, r], 8.0 * p[b, h, r])
+                mask = np.ones(64, bool)
+                mask[r] = False
+                np.testing.assert_array_equal(s[b, h, mask], p[b, h, mask])
+    for name in ("v", "do"):
+        assert np.array_equal(plain[name], spiky[name])
+    std = bf16_bits_to_float64(plain["v"]).std()
+    assert std == pytest.approx(0.5, rel=0.02)
+
+
+def test_workload_table():
+    w = gen.WORKLOADS
+    assert [(x.B, x.H, x.N, x.d, x.causal) for x in w.values()] == [
+        (1, 1, 128, 64, False), (8, 16, 2048, 128, False), (4, 32, 4096, 64, True),
+        (1, 16, 16384, 128, True), (2, 32, 8192, 80, True)]
+    assert w["c5"].sigma == 0.5 and w["c5"].spike
+    assert w["c1"].scale == np.float32(0.125)
+    # conventional flop counts: 4 B H N^2 d forward, x2.5 backward, halved when causal
+    assert w["c2"].flops("fwd") == 4 * 8 * 16 * 2048 ** 2 * 128
+    assert w["c4"].flops("fwdbwd") == pytest.approx(3.8483e12, rel=1e-4)
