@@ -1,0 +1,183 @@
+// C ABI entry points (include/fa2.h): argument validation, then kernel launches.
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa2.h"
+#include "fa2_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA2_OK;
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e),
+                hipGetErrorString(e));
+  return FA2_ERR_HIP;
+}
+
+bool ptr_ok(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Sizes: B, H, N >= 1, d supported, element count small enough for the
+// kernels' 32-bit row indices.
+int check_sizes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
+  if (d != 64 && d != 80 && d != 128) return FA2_ERR_UNSUPPORTED;
+  const long long elems = (long long)B * H * N * d;
+  if (elems >= (1LL << 31)) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
+}
+
+int check_scale_causal(float scale, int causal) {
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
+}
+
+// No output span may overlap an input span or another output span.
+bool disjoint(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(outs[i], ins[j])) return false;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j])) return false;
+  }
+  return true;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+            int d, float scale, int causal, void* stream) {
+  int st = check_sizes(B, H, N, d);
+  if (st != FA2_OK) return st;
+  if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse))
+    return FA2_ERR_INVALID_ARG;
+  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+  const Span ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
+  const Span outs[2] = {span(o, tb), span(lse, lb)};
+  if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
+  return hip_status(fa2::launch_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, as_stream(stream)));
+}
+
+size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_sizes(B, H, N, d) != FA2_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return align256(rows * 4) + align256(rows * d * 4);
+}
+
+int fa2_bwd_preprocess(const void* o, const void* dout, float* delta, float* dq_accum, int B,
+                       int H, int N, int d, void* stream) {
+  int st = check_sizes(B, H, N, d);
+  if (st != FA2_OK) return st;
+  if (!ptr_ok(o) || !ptr_ok(dout) || !ptr_ok(delta) || !ptr_ok(dq_accum)) return FA2_ERR_INVALID_ARG;
+  const size_t tb = (size_t)B * H * N * d * 2, rows = (size_t)B * H * N;
+  const Span ins[2] = {span(o, tb), span(dout, tb)};
+  const Span outs[2] = {span(delta, rows * 4), span(dq_accum, rows * d * 4)};
+  if (!disjoint(outs, 2, ins, 2)) return FA2_ERR_INVALID_ARG;
+  return hip_status(fa2::launch_bwd_preprocess(o, dout, delta, dq_accum, B, H, N, d, as_stream(stream)));
+}
+
+int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                 const float* delta, float* dq_accum, void* dk, void* dv, int B, int H, int N,
+                 int d, float scale, int causal, void* stream) {
+  int st = check_sizes(B, H, N, d);
+  if (st != FA2_OK) return st;
+  if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(lse) || !ptr_ok(dout) || !ptr_ok(delta) ||
+      !ptr_ok(dq_accum) || !ptr_ok(dk) || !ptr_ok(dv))
+    return FA2_ERR_INVALID_ARG;
+  const size_t tb = (size_t)B * H * N * d * 2, rows = (size_t)B * H * N;
+  const Span ins[6] = {span(q, tb),          span(k, tb),     span(v, tb),
+                       span(lse, rows * 4), span(dout, tb), span(delta, rows * 4)};
+  const Span outs[3] = {span(dq_accum, rows * d * 4), span(dk, tb), span(dv, tb)};
+  if (!disjoint(outs, 3, ins, 6)) return FA2_ERR_INVALID_ARG;
+  return hip_status(fa2::launch_bwd_dkdv(q, k, v, lse, dout, delta, dq_accum, dk, dv, B, H, N, d,
+                                         scale, causal, as_stream(stream)));
+}
+
+int fa2_bwd_dq_convert(const float* dq_accum, void* dq, int B, int H, int N, int d, float scale,
+                       void* stream) {
+  int st = check_sizes(B, H, N, d);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
+  if (!ptr_ok(dq_accum) || !ptr_ok(dq)) return FA2_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * N;
+  const Span ins[1] = {span(dq_accum, rows * d * 4)};
+  const Span outs[1] = {span(dq, rows * d * 2)};
+  if (!disjoint(outs, 1, ins, 1)) return FA2_ERR_INVALID_ARG;
+  return hip_status(fa2::launch_bwd_dq_convert(dq_accum, dq, B, H, N, d, scale, as_stream(stream)));
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+            float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sizes(B, H, N, d);
+  if (st != FA2_OK) return st;
+  if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dout) ||
+      !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv) || !ptr_ok(workspace))
+    return FA2_ERR_INVALID_ARG;
+  const size_t need = fa2_bwd_workspace_bytes(B, H, N, d);
+  if (workspace_bytes < need) return FA2_ERR_WORKSPACE;
+  const size_t tb = (size_t)B * H * N * d * 2, rows = (size_t)B * H * N;
+  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb),
+                       span(o, tb), span(lse, rows * 4), span(dout, tb)};
+  const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
+  if (!disjoint(outs, 4, ins, 6)) return FA2_ERR_INVALID_ARG;
+
+  float* delta = static_cast<float*>(workspace);
+  float* dq_accum = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * 4));
+  hipStream_t s = as_stream(stream);
+  if ((st = hip_status(fa2::launch_bwd_preprocess(o, dout, delta, dq_accum, B, H, N, d, s))) != FA2_OK)
+    return st;
+  if ((st = hip_status(fa2::launch_bwd_dkdv(q, k, v, lse, dout, delta, dq_accum, dk, dv, B, H, N,
+                                            d, scale, causal, s))) != FA2_OK)
+    return st;
+  return hip_status(fa2::launch_bwd_dq_convert(dq_accum, dq, B, H, N, d, scale, s));
+}
+
+const char* fa2_strerror(int status) {
+  switch (status) {
+    case FA2_OK: return "ok";
+    case FA2_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, size, scale, causal flag or aliasing)";
+    case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (supported: 64, 80, 128)";
+    case FA2_ERR_WORKSPACE: return "workspace too small (see fa2_bwd_workspace_bytes)";
+    case FA2_ERR_HIP: return "HIP launch error (see fa2_last_error)";
+    default: return "unknown status";
+  }
+}
+
+const char* fa2_last_error(void) { return g_last_error; }
+
+int fa2_tile_config(int d, int* fwd_block_q, int* fwd_block_k, int* bwd_block_k, int* bwd_block_q,
+                    int* fwd_waves, int* bwd_waves) {
+  if (d != 64 && d != 80 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if (!fwd_block_q || !fwd_block_k || !bwd_block_k || !bwd_block_q || !fwd_waves || !bwd_waves)
+    return FA2_ERR_INVALID_ARG;
+  fa2::fwd_tiles(d, fwd_block_q, fwd_block_k, fwd_waves);
+  fa2::bwd_tiles(d, bwd_block_k, bwd_block_q, bwd_waves);
+  return FA2_OK;
+}
+
+}  // extern "C"

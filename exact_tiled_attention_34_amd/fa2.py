@@ -1,0 +1,184 @@
+"""Thin Python binding of libfa2.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+declared in ``include/fa2.h``; this module only checks tensor properties,
+allocates outputs with PyTorch (device memory and streams are all PyTorch is
+used for) and forwards raw pointers.  There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+
+Functions mirror the C entry points: ``fwd``, ``bwd``, ``bwd_workspace_bytes``,
+``bwd_preprocess``, ``bwd_dkdv``, ``bwd_dq_convert``, ``tile_config``.
+"""
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+
+FA2_OK = 0
+SUPPORTED_HEAD_DIMS = (64, 80, 128)
+
+_lib = None
+
+_c_ptr = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+_c_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "fa2_fwd": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_workspace_bytes": (_c_size, [_c_int] * 4),
+    "fa2_bwd": (_c_int, [_c_ptr] * 9 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "fa2_bwd_preprocess": (_c_int, [_c_ptr] * 4 + [_c_int] * 4 + [_c_ptr]),
+    "fa2_bwd_dkdv": (_c_int, [_c_ptr] * 9 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_dq_convert": (_c_int, [_c_ptr] * 2 + [_c_int] * 4 + [_c_float, _c_ptr]),
+    "fa2_strerror": (ctypes.c_char_p, [_c_int]),
+    "fa2_last_error": (ctypes.c_char_p, []),
+    "fa2_tile_config": (_c_int, [_c_int] + [ctypes.POINTER(_c_int)] * 6),
+}
+
+
+class FA2Error(RuntimeError):
+    def __init__(self, status, where):
+        lib = load()
+        msg = lib.fa2_strerror(status).decode()
+        detail = lib.fa2_last_error().decode()
+        super().__init__(f"{where}: status {status}: {msg}" + (f" [{detail}]" if detail and status == 4 else ""))
+        self.status = status
+
+
+def load(path=None):
+    """Load libfa2.so (built by ``exact_tiled_attention_34_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} is missing: build it with `python -m exact_tiled_attention_34_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (restype, argtypes) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = restype
+        fn.argtypes = argtypes
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status, where):
+    if status != FA2_OK:
+        raise FA2Error(status, where)
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_qkv(name, t, shape=None):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_f32(name, t, shape):
+    import torch
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {tuple(shape)}")
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """O, L = attention(q, k, v); q/k/v bf16 [B,H,N,d] on the GPU."""
+    import torch
+    _check_qkv("q", q)
+    B, H, N, d = q.shape
+    _check_qkv("k", k, q.shape)
+    _check_qkv("v", v, q.shape)
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_qkv("out", out, q.shape)
+    _check_f32("lse", lse, (B, H, N))
+    st = load().fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    _check(st, "fa2_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(B, H, N, d):
+    return int(load().fa2_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """dQ, dK, dV of sum(do * o); all bf16 [B,H,N,d] except lse fp32 [B,H,N]."""
+    import torch
+    _check_qkv("q", q)
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_qkv(name, t, q.shape)
+    _check_f32("lse", lse, (B, H, N))
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_qkv(name, t, q.shape)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = load().fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        B, H, N, d, scale, int(bool(causal)), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(),
+                        _stream_handle(q.device, stream))
+    _check(st, "fa2_bwd")
+    return dq, dk, dv
+
+
+def bwd_preprocess(o, do, delta, dq_accum, stream=None):
+    B, H, N, d = o.shape
+    st = load().fa2_bwd_preprocess(o.data_ptr(), do.data_ptr(), delta.data_ptr(), dq_accum.data_ptr(),
+                                   B, H, N, d, _stream_handle(o.device, stream))
+    _check(st, "fa2_bwd_preprocess")
+
+
+def bwd_dkdv(q, k, v, lse, do, delta, dq_accum, dk, dv, causal=False, scale=None, stream=None):
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load().fa2_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                             delta.data_ptr(), dq_accum.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    _check(st, "fa2_bwd_dkdv")
+
+
+def bwd_dq_convert(dq_accum, dq, scale=None, stream=None):
+    B, H, N, d = dq.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load().fa2_bwd_dq_convert(dq_accum.data_ptr(), dq.data_ptr(), B, H, N, d, scale,
+                                   _stream_handle(dq.device, stream))
+    _check(st, "fa2_bwd_dq_convert")
+
+
+def tile_config(d):
+    vals = [_c_int() for _ in range(6)]
+    _check(load().fa2_tile_config(d, *[ctypes.byref(x) for x in vals]), "fa2_tile_config")
+    keys = ("fwd_block_q", "fwd_block_k", "bwd_block_k", "bwd_block_q", "fwd_waves", "bwd_waves")
+    return dict(zip(keys, (x.value for x in vals)))

@@ -1,0 +1,141 @@
+/*
+ * fa2.h — C ABI of an MI355X (gfx950) library for exact tiled softmax attention.
+ *
+ * What is computed.  Standard softmax attention and its gradient, exactly (up to
+ * floating-point rounding order): the "FlashAttention (v2)" glossary page says
+ * the method computes attention tile by tile in on-chip memory without
+ * approximating the result and that its output matches standard attention, so
+ * that adopting it is only a choice of backend.  Per (batch b, head h):
+ *
+ *     S    = scale * Q K^T                 (never written to memory)
+ *     S_ij = -inf for key j > query i      when causal (top-left aligned)
+ *     L_i  = log sum_j exp(S_ij)           natural-log logsumexp, fp32
+ *     O    = softmax(S) V
+ *
+ * and, given dO, the gradient of sum(dO * O):  dV = P^T dO, dP = dO V^T,
+ * D_i = sum_k dO_ik O_ik, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q,
+ * with P = exp(S - L) recomputed from L.
+ *
+ * Work split ("FlashAttention-2" summary page, "How It Works" 1 and 3; the
+ * glossary page on splitting one head across thread blocks): every call is
+ * spread over (batch, head) AND over blocks of the sequence, so that a few long
+ * heads still fill all 256 compute units.  With causal=1, key blocks lying
+ * wholly above the diagonal are skipped and only blocks crossing it are masked
+ * element by element ("FlashAttention-2: Faster Attention with Better
+ * Parallelism and Work Partitioning" page, closing sentence).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are DEVICE pointers to contiguous row-major [B, H, N, d] arrays
+ *    (d fastest).  q, k, v, o, dout, dq, dk, dv hold bfloat16 values stored as
+ *    16-bit words.  lse and delta are fp32 [B, H, N]; dq_accum is fp32
+ *    [B, H, N, d].
+ *  - Supported: B, H, N >= 1 with B*H*N*d < 2^31; d in {64, 80, 128};
+ *    causal in {0, 1}; scale finite and > 0 (the usual 1/sqrt(d)).
+ *  - Every pointer must be non-null and 16-byte aligned.  Outputs must not
+ *    overlap inputs or each other.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work and return; results are valid after the stream is
+ *    synchronised.  The library allocates no memory, keeps no pointer after a
+ *    call returns, and is re-entrant: calls on different streams may run
+ *    concurrently (a workspace must not be shared by calls in flight).
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Errors: every argument is checked before any HIP call; a failed check
+ *    returns FA2_ERR_INVALID_ARG, FA2_ERR_UNSUPPORTED or FA2_ERR_WORKSPACE and
+ *    writes nothing.  A failed kernel launch returns FA2_ERR_HIP; the HIP
+ *    error text is kept per thread (fa2_last_error).  No C++ exception crosses
+ *    this interface.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa2_status {
+    FA2_OK = 0,
+    FA2_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, aliasing, bad scale/causal */
+    FA2_ERR_UNSUPPORTED = 2, /* head dimension not in {64, 80, 128} */
+    FA2_ERR_WORKSPACE = 3,   /* workspace too small */
+    FA2_ERR_HIP = 4          /* a HIP launch failed; see fa2_last_error() */
+} fa2_status;
+
+/*
+ * Forward pass: O and L from Q, K, V.
+ * One query row-block per workgroup, its rows split across the workgroup's
+ * wavefronts; an online softmax runs over K/V tiles staged in LDS, and the
+ * division by the row sum happens once, after the last tile ("FlashAttention-2"
+ * summary page, "How It Works" 2).
+ *   q, k, v : in,  bf16 [B,H,N,d]
+ *   o       : out, bf16 [B,H,N,d]
+ *   lse     : out, fp32 [B,H,N], natural-log logsumexp of the scaled masked scores
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Bytes of device workspace fa2_bwd needs: delta (fp32 [B,H,N]) followed by the
+ * fp32 dQ accumulator ([B,H,N,d]), each region 256-byte aligned.  Returns 0
+ * for unsupported or invalid sizes. */
+size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass: dQ, dK, dV from Q, K, V, the forward's O and L, and dO.
+ * Runs, on `stream`, fa2_bwd_preprocess, fa2_bwd_dkdv and fa2_bwd_dq_convert
+ * below (one call each), using `workspace` for delta and the dQ accumulator.
+ *   q, k, v, o, dout : in, bf16 [B,H,N,d];  lse : in, fp32 [B,H,N] from fa2_fwd
+ *   dq, dk, dv       : out, bf16 [B,H,N,d]
+ *   workspace        : device scratch of >= fa2_bwd_workspace_bytes(B,H,N,d)
+ *                      bytes, owned by the caller; its contents on entry do not
+ *                      matter and on return are unspecified.
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv,
+            int B, int H, int N, int d, float scale, int causal,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward phase 1: delta_i = sum_k dout_ik * o_ik (fp32) for every row, and
+ * dq_accum set to zero.  HBM-bound elementwise work.
+ *   o, dout : in, bf16 [B,H,N,d];  delta : out, fp32 [B,H,N];
+ *   dq_accum: out, fp32 [B,H,N,d] (zeroed). */
+int fa2_bwd_preprocess(const void* o, const void* dout, float* delta, float* dq_accum,
+                       int B, int H, int N, int d, void* stream);
+
+/* Backward phase 2: one key/value column-block per workgroup, looping over the
+ * query row-blocks that can see it (causal: from the diagonal on).  Recomputes
+ * P = exp(scale q k^T - L), writes dK and dV (bf16), and adds the unscaled
+ * dS K contributions to dq_accum with fp32 atomics (so dq_accum must start
+ * zeroed, as fa2_bwd_preprocess leaves it).
+ *   q, k, v, dout : in, bf16;  lse, delta : in, fp32 [B,H,N]
+ *   dq_accum      : in/out, fp32 [B,H,N,d];  dk, dv : out, bf16 [B,H,N,d] */
+int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                 const void* dout, const float* delta, float* dq_accum,
+                 void* dk, void* dv,
+                 int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Backward phase 3: dq = bf16(scale * dq_accum), applying the softmax scale
+ * once at the end rather than per tile.
+ *   dq_accum : in, fp32 [B,H,N,d];  dq : out, bf16 [B,H,N,d] */
+int fa2_bwd_dq_convert(const float* dq_accum, void* dq, int B, int H, int N, int d,
+                       float scale, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa2_strerror(int status);
+
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+const char* fa2_last_error(void);
+
+/* Tile geometry used for head dimension d, for reporting: rows of the query
+ * block per forward workgroup, keys per forward K/V tile, keys per backward
+ * workgroup, queries per backward step, wavefronts per workgroup (fwd, bwd).
+ * Returns FA2_ERR_UNSUPPORTED for other d. */
+int fa2_tile_config(int d, int* fwd_block_q, int* fwd_block_k, int* bwd_block_k,
+                    int* bwd_block_q, int* fwd_waves, int* bwd_waves);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,132 @@
+"""The C ABI (no GPU): the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before making any HIP call.
+
+Only invalid argument combinations are passed here: each is rejected by the
+host-side checks, so the fake (never dereferenced) pointers below never reach
+a kernel.  As a second safeguard, the tests that pass fake pointers are skipped
+in any process that can see a GPU: they cover host logic only.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_34_amd import fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+# distinct, 16-byte aligned, far-apart fake device addresses (never dereferenced)
+P = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: host-only checks")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa2.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_strerror"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding declares a signature for each of them
+    assert set(names) == set(fa2._SIGNATURES)
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=128, d=64, scale=0.125, causal=0):
+    return lib.fa2_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+@host_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(causal=2), INVALID), (dict(causal=-1), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-0.125), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(q=None), INVALID), (dict(lse=None), INVALID),
+    (dict(k=P[1] + 8), INVALID), (dict(o=P[3] + 2), INVALID),
+    (dict(o=P[0]), INVALID),                     # output aliases an input
+    (dict(lse=P[3] + 64), INVALID),              # lse inside o
+    (dict(B=1024, H=1024, N=4096, d=128), INVALID),  # too many elements for 32-bit rows
+])
+def test_fwd_rejects(lib, kw, want):
+    assert fwd(lib, **kw) == want
+
+
+def bwd(lib, ws_bytes=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, **ptrs):
+    names = ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"]
+    p = dict(zip(names, P))
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.fa2_bwd_workspace_bytes(B, H, N, d)
+    return lib.fa2_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                       B, H, N, d, scale, causal, p["ws"], ws_bytes, None)
+
+
+@host_only
+def test_bwd_rejects(lib):
+    need = lib.fa2_bwd_workspace_bytes(1, 2, 128, 64)
+    assert need == 1024 + 2 * 128 * 64 * 4
+    assert bwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert bwd(lib, ws_bytes=0) == WORKSPACE
+    assert bwd(lib, d=72) == UNSUPPORTED
+    assert bwd(lib, causal=3) == INVALID
+    assert bwd(lib, scale=-1.0) == INVALID
+    assert bwd(lib, ws=None) == INVALID
+    assert bwd(lib, dq=P[0]) == INVALID          # dq aliases q
+    assert bwd(lib, dk=P[6] + 16) == INVALID     # dk overlaps dq
+    assert bwd(lib, ws=P[8] + 4096) == INVALID   # workspace overlaps dv
+    assert bwd(lib, do=P[5] + 4) == INVALID      # misaligned
+
+
+@host_only
+def test_phase_entry_points_reject(lib):
+    assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[3], 1, 1, 0, 64, None) == INVALID
+    assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[0], 1, 1, 64, 64, None) == INVALID
+    assert lib.fa2_bwd_dkdv(*P[:9], 1, 1, 64, 100, 0.1, 0, None) == UNSUPPORTED
+    assert lib.fa2_bwd_dkdv(*P[:9], 1, 1, 64, 64, 0.0, 0, None) == INVALID
+    assert lib.fa2_bwd_dq_convert(P[0], P[0] + 16, 1, 1, 64, 64, 0.1, None) == INVALID
+    assert lib.fa2_bwd_dq_convert(P[0], P[1], 1, 1, 64, 64, float("nan"), None) == INVALID
+
+
+def test_workspace_size_query(lib):
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 1, 96) == 0
+    assert lib.fa2_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    # delta region and accumulator, each rounded up to 256 bytes
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 3, 80) == 256 + 1024
+    assert lib.fa2_bwd_workspace_bytes(1, 16, 16384, 128) == 16 * 16384 * 4 + 16 * 16384 * 128 * 4
+
+
+def test_strerror_and_tiles(lib):
+    for s in range(5):
+        assert lib.fa2_strerror(s)
+    assert b"unknown" in lib.fa2_strerror(99)
+    assert lib.fa2_last_error() == b""
+    for d in (64, 80, 128):
+        t = fa2.tile_config(d)
+        assert t["fwd_block_q"] % 32 == 0 and t["bwd_block_k"] % 32 == 0
+    with pytest.raises(fa2.FA2Error):
+        fa2.tile_config(96)
