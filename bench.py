@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (forward + backward) on one MI355X.
+
+One step = the whole hot path on one batch of synthetic, seeded bf16 inputs
+already resident in HBM: fa2_fwd (O, L), then the backward phases exactly as
+fa2_bwd enqueues them (fa2_bwd_preprocess, fa2_bwd_dkdv, fa2_bwd_dq_convert).
+The phases are called one by one only so that every kernel is bracketed by its
+own HIP events on the stream it runs on.
+
+Prints ONE JSON line.  ``value`` is forward+backward TFLOP/s with the usual
+attention convention (4*B*H*N^2*d forward, 2.5x that backward, halved for
+causal).  ``roofline`` describes the kernel that takes most of the step time;
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import fa2_inputs as gen  # noqa: E402
+
+METRIC = "attention fwd/bwd/fwd+bwd TFLOP/s and % of bf16 MFMA peak, d=64/128"
+PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_CONFIG = "c2"        # B8 H16 N2048 d128 non-causal
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, arrs, budget_s):
+    """Time the float64 oracle (fwd + bwd, whole heads) for about budget_s seconds."""
+    import numpy as np
+    import oracle
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    heads, t0 = 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            x = {n: oracle.bf16_bits_to_float64(arrs[n][b, h]) for n in ("q", "k", "v", "do")}
+            A.forward_head(x["q"], x["k"], x["v"], w.scale, w.causal)
+            A.backward_head(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops("fwdbwd") / (w.B * w.H) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, fwd+bwd in float64 numpy "
+                      f"({dt:.1f} s); conventional flops of those heads / wall time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard "
+              "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+    from exact_tiled_attention_34_amd import fa2
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w, arrs = gen.make_workload(args.config, seed=args.seed)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v, do = (up(arrs[n]) for n in ("q", "k", "v", "do"))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq_acc = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq_convert"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        fa2.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        mark(1)
+        fa2.bwd_preprocess(o, do, delta, dq_acc, stream=stream)
+        mark(2)
+        fa2.bwd_dkdv(q, k, v, lse, do, delta, dq_acc, dk, dv, causal=w.causal, scale=w.scale, stream=stream)
+        mark(3)
+        fa2.bwd_dq_convert(dq_acc, dq, scale=w.scale, stream=stream)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()            # one process, one GPU: no barrier to wait for
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kern_ms = {n: 0.0 for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            kern_ms[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    f_fwd, f_bwd, f_all = w.flops("fwd"), w.flops("bwd"), w.flops("fwdbwd")
+    value = f_all / (ms_per_step * 1e-3) / 1e12
+    bwd_ms = kern_ms["bwd_preprocess"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq_convert"]
+    phases = {
+        "fwd_tflops": f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12,
+        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+        "fwdbwd_tflops": value,
+    }
+    phases.update({k2 + "_pct_peak": 100.0 * v2 / PEAK_BF16_TFLOPS for k2, v2 in list(phases.items())})
+
+    # dominant kernel and its roofline: both big kernels are dense bf16 MFMA work
+    algo_flops = {"fwd": f_fwd, "bwd_dkdv": f_bwd}
+    dom = max(("fwd", "bwd_dkdv"), key=lambda n: kern_ms[n])
+    achieved = algo_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO)",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "scale": w.scale, "parallelism": "single GPU"},
+        "phases": {k2: round(v2, 2) for k2, v2 in phases.items()},
+        "kernel_ms": {k2: round(v2, 4) for k2, v2 in kern_ms.items()},
+        "roofline": roofline,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, arrs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
