@@ -3,7 +3,7 @@
 
 One step = the whole hot path on one batch of synthetic, seeded bf16 inputs
 already resident in HBM: fa2_fwd (O, L), then the backward phases exactly as
-fa2_bwd enqueues them (fa2_bwd_preprocess, fa2_bwd_dkdv, fa2_bwd_dq_convert).
+fa2_bwd enqueues them (fa2_bwd_preprocess, fa2_bwd_dkdv, fa2_bwd_dq).
 The phases are called one by one only so that every kernel is bracketed by its
 own HIP events on the stream it runs on.
 
@@ -97,10 +97,9 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq_acc = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    delta, lse_log2 = fa2.bwd_row_arrays(B, H, N, dev)
     stream = torch.cuda.current_stream(dev)
-    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq_convert"]
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
 
     def step(ev=None):
         def mark(i):
@@ -109,11 +108,11 @@ def main():
         mark(0)
         fa2.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
         mark(1)
-        fa2.bwd_preprocess(o, do, delta, dq_acc, stream=stream)
+        fa2.bwd_preprocess(o, do, lse, delta, lse_log2, stream=stream)
         mark(2)
-        fa2.bwd_dkdv(q, k, v, lse, do, delta, dq_acc, dk, dv, causal=w.causal, scale=w.scale, stream=stream)
+        fa2.bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=w.causal, scale=w.scale, stream=stream)
         mark(3)
-        fa2.bwd_dq_convert(dq_acc, dq, scale=w.scale, stream=stream)
+        fa2.bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=w.causal, scale=w.scale, stream=stream)
         mark(4)
 
     for _ in range(args.warmup):
@@ -136,7 +135,7 @@ def main():
 
     f_fwd, f_bwd, f_all = w.flops("fwd"), w.flops("bwd"), w.flops("fwdbwd")
     value = f_all / (ms_per_step * 1e-3) / 1e12
-    bwd_ms = kern_ms["bwd_preprocess"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq_convert"]
+    bwd_ms = kern_ms["bwd_preprocess"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
     phases = {
         "fwd_tflops": f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12,
         "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
@@ -144,9 +143,12 @@ def main():
     }
     phases.update({k2 + "_pct_peak": 100.0 * v2 / PEAK_BF16_TFLOPS for k2, v2 in list(phases.items())})
 
-    # dominant kernel and its roofline: both big kernels are dense bf16 MFMA work
-    algo_flops = {"fwd": f_fwd, "bwd_dkdv": f_bwd}
-    dom = max(("fwd", "bwd_dkdv"), key=lambda n: kern_ms[n])
+    # dominant kernel and its roofline: the three big kernels are dense bf16 MFMA
+    # work; conventional flops per launch: fwd 4 B H N^2 d, dK/dV 4/5 of the
+    # backward's 10 B H N^2 d (S, dP, dV, dK), dQ 2/5 of it (its own S and dP
+    # recomputation and dQ: 3 products, one of them the conventional dQ share).
+    algo_flops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.6 * f_bwd}
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kern_ms[n])
     achieved = algo_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -80,53 +80,68 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   return hip_status(fa2::launch_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, as_stream(stream)));
 }
 
+int fa2_bwd_rows_padded(int N) { return N < 1 ? 0 : fa2::bwd_rows_padded(N); }
+
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_sizes(B, H, N, d) != FA2_OK) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return align256(rows * 4) + align256(rows * d * 4);
+  const size_t rows = (size_t)B * H * fa2::bwd_rows_padded(N);
+  return 2 * align256(rows * 4);
 }
 
-int fa2_bwd_preprocess(const void* o, const void* dout, float* delta, float* dq_accum, int B,
-                       int H, int N, int d, void* stream) {
+int fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, float* delta,
+                       float* lse_log2, int B, int H, int N, int d, void* stream) {
   int st = check_sizes(B, H, N, d);
   if (st != FA2_OK) return st;
-  if (!ptr_ok(o) || !ptr_ok(dout) || !ptr_ok(delta) || !ptr_ok(dq_accum)) return FA2_ERR_INVALID_ARG;
+  if (!ptr_ok(o) || !ptr_ok(dout) || !ptr_ok(lse) || !ptr_ok(delta) || !ptr_ok(lse_log2))
+    return FA2_ERR_INVALID_ARG;
   const size_t tb = (size_t)B * H * N * d * 2, rows = (size_t)B * H * N;
-  const Span ins[2] = {span(o, tb), span(dout, tb)};
-  const Span outs[2] = {span(delta, rows * 4), span(dq_accum, rows * d * 4)};
-  if (!disjoint(outs, 2, ins, 2)) return FA2_ERR_INVALID_ARG;
-  return hip_status(fa2::launch_bwd_preprocess(o, dout, delta, dq_accum, B, H, N, d, as_stream(stream)));
+  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(N);
+  const Span ins[3] = {span(o, tb), span(dout, tb), span(lse, rows * 4)};
+  const Span outs[2] = {span(delta, prow * 4), span(lse_log2, prow * 4)};
+  if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
+  return hip_status(fa2::launch_bwd_preprocess(o, dout, lse, delta, lse_log2, B, H, N, d,
+                                               as_stream(stream)));
 }
 
-int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                 const float* delta, float* dq_accum, void* dk, void* dv, int B, int H, int N,
-                 int d, float scale, int causal, void* stream) {
+// Shared checks of the two tile phases: 4 bf16 inputs, the two padded row
+// arrays, and `n_out` bf16 outputs.
+static int check_tile_phase(const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse_log2, const float* delta, const void* out0,
+                            const void* out1, int B, int H, int N, int d, float scale,
+                            int causal) {
   int st = check_sizes(B, H, N, d);
   if (st != FA2_OK) return st;
   if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
-  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(lse) || !ptr_ok(dout) || !ptr_ok(delta) ||
-      !ptr_ok(dq_accum) || !ptr_ok(dk) || !ptr_ok(dv))
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(dout) || !ptr_ok(lse_log2) ||
+      !ptr_ok(delta) || !ptr_ok(out0) || (out1 != nullptr && !ptr_ok(out1)))
     return FA2_ERR_INVALID_ARG;
-  const size_t tb = (size_t)B * H * N * d * 2, rows = (size_t)B * H * N;
-  const Span ins[6] = {span(q, tb),          span(k, tb),     span(v, tb),
-                       span(lse, rows * 4), span(dout, tb), span(delta, rows * 4)};
-  const Span outs[3] = {span(dq_accum, rows * d * 4), span(dk, tb), span(dv, tb)};
-  if (!disjoint(outs, 3, ins, 6)) return FA2_ERR_INVALID_ARG;
-  return hip_status(fa2::launch_bwd_dkdv(q, k, v, lse, dout, delta, dq_accum, dk, dv, B, H, N, d,
-                                         scale, causal, as_stream(stream)));
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(N);
+  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(dout, tb),
+                       span(lse_log2, prow * 4), span(delta, prow * 4)};
+  const Span outs[2] = {span(out0, tb), span(out1, out1 ? tb : 0)};
+  if (!disjoint(outs, out1 ? 2 : 1, ins, 6)) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
 }
 
-int fa2_bwd_dq_convert(const float* dq_accum, void* dq, int B, int H, int N, int d, float scale,
-                       void* stream) {
-  int st = check_sizes(B, H, N, d);
+int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                 const float* lse_log2, const float* delta, void* dk, void* dv, int B, int H,
+                 int N, int d, float scale, int causal, void* stream) {
+  if (dv == nullptr) return FA2_ERR_INVALID_ARG;
+  const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d, scale, causal);
   if (st != FA2_OK) return st;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
-  if (!ptr_ok(dq_accum) || !ptr_ok(dq)) return FA2_ERR_INVALID_ARG;
-  const size_t rows = (size_t)B * H * N;
-  const Span ins[1] = {span(dq_accum, rows * d * 4)};
-  const Span outs[1] = {span(dq, rows * d * 2)};
-  if (!disjoint(outs, 1, ins, 1)) return FA2_ERR_INVALID_ARG;
-  return hip_status(fa2::launch_bwd_dq_convert(dq_accum, dq, B, H, N, d, scale, as_stream(stream)));
+  return hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d, scale,
+                                         causal, as_stream(stream)));
+}
+
+int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+               const float* lse_log2, const float* delta, void* dq, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dq, nullptr, B, H, N, d, scale,
+                                  causal);
+  if (st != FA2_OK) return st;
+  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, N, d, scale,
+                                       causal, as_stream(stream)));
 }
 
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -146,15 +161,17 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
   if (!disjoint(outs, 4, ins, 6)) return FA2_ERR_INVALID_ARG;
 
+  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(N);
   float* delta = static_cast<float*>(workspace);
-  float* dq_accum = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * 4));
+  float* lse_log2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(prow * 4));
   hipStream_t s = as_stream(stream);
-  if ((st = hip_status(fa2::launch_bwd_preprocess(o, dout, delta, dq_accum, B, H, N, d, s))) != FA2_OK)
+  if ((st = hip_status(fa2::launch_bwd_preprocess(o, dout, lse, delta, lse_log2, B, H, N, d, s))) != FA2_OK)
     return st;
-  if ((st = hip_status(fa2::launch_bwd_dkdv(q, k, v, lse, dout, delta, dq_accum, dk, dv, B, H, N,
-                                            d, scale, causal, s))) != FA2_OK)
+  if ((st = hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d,
+                                            scale, causal, s))) != FA2_OK)
     return st;
-  return hip_status(fa2::launch_bwd_dq_convert(dq_accum, dq, B, H, N, d, scale, s));
+  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, N, d, scale,
+                                       causal, s));
 }
 
 const char* fa2_strerror(int status) {

@@ -1,5 +1,6 @@
 // Device helpers for the gfx950 (CDNA4) attention kernels: MFMA wrappers,
-// bf16 packing, fast exp2/log2, and the LDS layouts shared by the kernels.
+// bf16 packing, fast exp2/log2, the LDS tile layout, asynchronous
+// global->LDS tile loads and the two ways MFMA operands are read from LDS.
 //
 // MFMA lane layout (v_mfma_f32_32x32x16_bf16, one 64-lane wavefront):
 //   A (32 x 16): lane l holds A[l % 32][8*(l/32) + j],  j = 0..7
@@ -16,9 +17,11 @@ namespace fa2 {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -46,48 +49,135 @@ __device__ __forceinline__ u32x4 ld_global16(const void* p) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ bf16x8 ld_lds16(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-__device__ __forceinline__ void st_lds16(uint16_t* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
-}
-__device__ __forceinline__ void st_lds8(uint16_t* p, u32x2 v) {
-  *reinterpret_cast<u32x2*>(p) = v;
-}
-
 // Exchange with the lane 32 positions away (the other half of the wavefront).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// Wait until this wavefront's outstanding vector-memory loads (including
+// global->LDS loads) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
-// Transposed tiles in LDS.
+// Row-major tiles in LDS.
 //
-// The P.V product (and, in the backward pass, dO^T.P and Q^T.dS) reduces over
-// the token index, which is the row index of V / dO / Q in memory.  MFMA
-// operands must hold 8 consecutive reduction-index values per lane, so these
-// tiles are stored transposed, [feature row][token], 64 tokens per row.
-//
-// Token order inside a row: the MFMA accumulator that produces P holds, in
-// lane half h, the tokens {4h..4h+3, 8+4h..8+4h+3} of each group of 16 (see the
-// C layout above).  Storing tokens with the middle two groups of four swapped
-// puts exactly those eight tokens side by side, so one 16-byte LDS read feeds
-// the operand.  The summation order of the product is irrelevant, so this
-// permutation changes nothing in the result beyond fp32 rounding order.
-//
-// Bank spreading: rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r
-// is stored at chunk slot c ^ ((r + r/8) & 7).  Readers take 32 consecutive
-// rows at one chunk, writers 8-rows-apart rows at one chunk; both land on
-// different slots.
+// A tile holds ROWS token rows of D bf16 features, in 16-byte chunks.  The
+// chunk order inside a row is permuted per row so that both access patterns
+// used by the kernels spread over the LDS banks:
+//   (a) 16-byte reads of one chunk by 32 consecutive rows (MFMA operands
+//       whose reduction index is the feature: Q K^T, dO V^T), and
+//   (b) transposed reads of 8 rows x 4 chunks (operands whose reduction
+//       index is the token: V^T, dO^T, Q^T, K^T).
+// D = 128 (16 chunks) and D = 64 (8 chunks) use an XOR of the chunk index;
+// D = 80 (10 chunks) pads every row to 11 chunk slots instead.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int tok_perm(int t) {
-  // swap groups 1 and 2 (of four tokens) inside every group of sixteen
-  const int g = (t >> 2) & 3;
-  const int ng = (g == 1) ? 2 : (g == 2) ? 1 : g;
-  return (t & ~15) | (ng << 2) | (t & 3);
+template <int D>
+struct RowTile {
+  static constexpr int CH = D / 8;
+  static constexpr bool PADDED = (CH & (CH - 1)) != 0;
+  static constexpr int SLOTS = PADDED ? CH + 1 : CH;
+  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16), "unsupported head dim");
+
+  // XOR key of a row (an involution on the chunk index).
+  __device__ __forceinline__ static int swz(int row) {
+    if constexpr (PADDED) {
+      return 0;
+    } else if constexpr (CH == 16) {
+      return (4 * (row & 3)) | ((row >> 2) & 3);
+    } else {
+      const int g = (row >> 1) & 7;
+      return (4 * (g & 1)) | (g >> 1);
+    }
+  }
+  // 16-byte slot index of (row, chunk) inside the tile.
+  __device__ __forceinline__ static int slot(int row, int chunk) {
+    return row * SLOTS + (PADDED ? chunk : (chunk ^ swz(row)));
+  }
+  // bf16 element offset of (row, col); col % 4 == 0.
+  __device__ __forceinline__ static int elem(int row, int col) {
+    return slot(row, col >> 3) * 8 + (col & 7);
+  }
+  // bf16 elements to reserve for a tile (transposed reads of the padded
+  // feature block of D = 80 may run 8 elements past the last row).
+  static constexpr int elems(int rows) { return rows * SLOTS * 8 + (PADDED ? 16 : 0); }
+};
+
+// One 16-byte global -> LDS load per lane.  `lds` must be the same for every
+// lane of the wavefront; lane l's 16 bytes land at lds + 16*l bytes.
+__device__ __forceinline__ void global_load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
 }
-__device__ __forceinline__ int tr64_offset(int row, int pos) {
-  const int chunk = (pos >> 3) ^ ((row + (row >> 3)) & 7);
-  return row * 64 + chunk * 8 + (pos & 7);
+
+// Start loading rows [row0, row0 + ROWS) of one head (row-major, D features)
+// into a RowTile in LDS.  Rows past n_rows are clamped to the last row (finite
+// data that the caller masks or weights by zero).  Returns immediately;
+// wait_vmem() + a workgroup barrier make the tile visible.
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void load_tile_async(uint16_t* tile, const uint16_t* head, int row0,
+                                                int n_rows, int tid) {
+  using L = RowTile<D>;
+  constexpr int TOTAL = ROWS * L::SLOTS;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+#pragma unroll
+  for (int t = 0; t < (TOTAL + THREADS - 1) / THREADS; ++t) {
+    const int base = wave * 64 + t * THREADS;   // wavefront-uniform
+    if (base >= TOTAL) break;
+    const int s = base + lane;
+    const int row = s / L::SLOTS;
+    int chunk = s % L::SLOTS;
+    if (L::PADDED) {
+      if (chunk >= L::CH) chunk = 0;   // the pad slot gets a copy of chunk 0
+    } else {
+      chunk ^= L::swz(row);
+    }
+    const int grow = min(row0 + row, n_rows - 1);
+    if (s < TOTAL) global_load_lds16(head + (size_t)grow * D + chunk * 8, tile + base * 8);
+  }
+}
+
+// MFMA operand whose reduction index is the feature: lane l gets 8
+// consecutive features [col, col+8) of tile row `row` (16-byte read).
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int row, int col) {
+  return *reinterpret_cast<const bf16x8*>(tile + RowTile<D>::elem(row, col));
+}
+
+// MFMA operand whose reduction index is the token: the transpose of a
+// 16-token x 32-feature block starting at (tok0, col0).  Lane l gets feature
+// col0 + l%32 and, in its 8 k-slots, tokens tok0 + 4h + {0..3} then
+// tok0 + 8 + 4h + {0..3} (h = l/32) — the same token order in which an MFMA
+// accumulator holds its rows, so a P or dS accumulator feeds the other
+// operand directly.  Two ds_read_b64_tr_b16: inside each 16-lane group the
+// instruction hands lane i element i%4 of source lane 4j + i/4 as its j-th
+// value; source lane s therefore points at row base + s/4, features 4(s%4)+.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int tok0, int col0, int lane) {
+  i16x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int s = lane & 15;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int row = tok0 + 4 * (lane >> 5) + (s >> 2);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((lds_u16*)tile + RowTile<D>::elem(row, col)));
+  hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((lds_u16*)tile + RowTile<D>::elem(row + 8, col)));
+#else
+  (void)tile; (void)tok0; (void)col0; (void)lane;
+#endif
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// bf16x8 B operand for 16 tokens (chunk c of a 32-row accumulator pair) from
+// packed accumulator words w[0..7] (w[t] = rows 2t, 2t+1 of the accumulator).
+__device__ __forceinline__ bf16x8 acc_chunk(const uint32_t* w, int half) {
+  const u32x4 v = {w[4 * half + 0], w[4 * half + 1], w[4 * half + 2], w[4 * half + 3]};
+  return as_bf16x8(v);
 }
 
 }  // namespace fa2

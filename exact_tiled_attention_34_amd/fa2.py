@@ -7,7 +7,7 @@ used for) and forwards raw pointers.  There is no fallback: if the library is
 missing or a call fails, an exception is raised.
 
 Functions mirror the C entry points: ``fwd``, ``bwd``, ``bwd_workspace_bytes``,
-``bwd_preprocess``, ``bwd_dkdv``, ``bwd_dq_convert``, ``tile_config``.
+``bwd_rows_padded``, ``bwd_preprocess``, ``bwd_dkdv``, ``bwd_dq``, ``tile_config``.
 """
 
 import ctypes
@@ -28,11 +28,12 @@ _c_size = ctypes.c_size_t
 
 _SIGNATURES = {
     "fa2_fwd": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_rows_padded": (_c_int, [_c_int]),
     "fa2_bwd_workspace_bytes": (_c_size, [_c_int] * 4),
     "fa2_bwd": (_c_int, [_c_ptr] * 9 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
-    "fa2_bwd_preprocess": (_c_int, [_c_ptr] * 4 + [_c_int] * 4 + [_c_ptr]),
-    "fa2_bwd_dkdv": (_c_int, [_c_ptr] * 9 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
-    "fa2_bwd_dq_convert": (_c_int, [_c_ptr] * 2 + [_c_int] * 4 + [_c_float, _c_ptr]),
+    "fa2_bwd_preprocess": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_ptr]),
+    "fa2_bwd_dkdv": (_c_int, [_c_ptr] * 8 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_dq": (_c_int, [_c_ptr] * 7 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
     "fa2_strerror": (ctypes.c_char_p, [_c_int]),
     "fa2_last_error": (ctypes.c_char_p, []),
     "fa2_tile_config": (_c_int, [_c_int] + [ctypes.POINTER(_c_int)] * 6),
@@ -153,28 +154,41 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None
     return dq, dk, dv
 
 
-def bwd_preprocess(o, do, delta, dq_accum, stream=None):
+def bwd_rows_padded(N):
+    return int(load().fa2_bwd_rows_padded(N))
+
+
+def bwd_row_arrays(B, H, N, device):
+    """Allocate the two padded fp32 row arrays (delta, L*log2 e) of the backward phases."""
+    import torch
+    shape = (B, H, bwd_rows_padded(N))
+    return (torch.empty(shape, dtype=torch.float32, device=device),
+            torch.empty(shape, dtype=torch.float32, device=device))
+
+
+def bwd_preprocess(o, do, lse, delta, lse_log2, stream=None):
     B, H, N, d = o.shape
-    st = load().fa2_bwd_preprocess(o.data_ptr(), do.data_ptr(), delta.data_ptr(), dq_accum.data_ptr(),
-                                   B, H, N, d, _stream_handle(o.device, stream))
+    st = load().fa2_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), delta.data_ptr(),
+                                   lse_log2.data_ptr(), B, H, N, d, _stream_handle(o.device, stream))
     _check(st, "fa2_bwd_preprocess")
 
 
-def bwd_dkdv(q, k, v, lse, do, delta, dq_accum, dk, dv, causal=False, scale=None, stream=None):
+def bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=False, scale=None, stream=None):
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
-    st = load().fa2_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                             delta.data_ptr(), dq_accum.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+    st = load().fa2_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                             lse_log2.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                              B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
     _check(st, "fa2_bwd_dkdv")
 
 
-def bwd_dq_convert(dq_accum, dq, scale=None, stream=None):
-    B, H, N, d = dq.shape
+def bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=False, scale=None, stream=None):
+    B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
-    st = load().fa2_bwd_dq_convert(dq_accum.data_ptr(), dq.data_ptr(), B, H, N, d, scale,
-                                   _stream_handle(dq.device, stream))
-    _check(st, "fa2_bwd_dq_convert")
+    st = load().fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                           lse_log2.data_ptr(), delta.data_ptr(), dq.data_ptr(),
+                           B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    _check(st, "fa2_bwd_dq")
 
 
 def tile_config(d):

@@ -28,8 +28,8 @@
  * ---------------------------------------
  *  - Tensors are DEVICE pointers to contiguous row-major [B, H, N, d] arrays
  *    (d fastest).  q, k, v, o, dout, dq, dk, dv hold bfloat16 values stored as
- *    16-bit words.  lse and delta are fp32 [B, H, N]; dq_accum is fp32
- *    [B, H, N, d].
+ *    16-bit words.  lse is fp32 [B, H, N]; the backward's delta and lse_log2
+ *    are fp32 [B, H, fa2_bwd_rows_padded(N)].
  *  - Supported: B, H, N >= 1 with B*H*N*d < 2^31; d in {64, 80, 128};
  *    causal in {0, 1}; scale finite and > 0 (the usual 1/sqrt(d)).
  *  - Every pointer must be non-null and 16-byte aligned.  Outputs must not
@@ -76,15 +76,19 @@ typedef enum fa2_status {
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int B, int H, int N, int d, float scale, int causal, void* stream);
 
-/* Bytes of device workspace fa2_bwd needs: delta (fp32 [B,H,N]) followed by the
- * fp32 dQ accumulator ([B,H,N,d]), each region 256-byte aligned.  Returns 0
- * for unsupported or invalid sizes. */
+/* Rows per (batch, head) of the padded fp32 row arrays used by the backward
+ * phases: N rounded up to a multiple of 128.  Returns 0 for N < 1. */
+int fa2_bwd_rows_padded(int N);
+
+/* Bytes of device workspace fa2_bwd needs: delta then L*log2(e), each fp32
+ * [B,H,fa2_bwd_rows_padded(N)] and 256-byte aligned.  Returns 0 for
+ * unsupported or invalid sizes. */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
  * Backward pass: dQ, dK, dV from Q, K, V, the forward's O and L, and dO.
- * Runs, on `stream`, fa2_bwd_preprocess, fa2_bwd_dkdv and fa2_bwd_dq_convert
- * below (one call each), using `workspace` for delta and the dQ accumulator.
+ * Runs, on `stream`, fa2_bwd_preprocess, fa2_bwd_dkdv and fa2_bwd_dq below
+ * (one call each), using `workspace` for the two padded row arrays.
  *   q, k, v, o, dout : in, bf16 [B,H,N,d];  lse : in, fp32 [B,H,N] from fa2_fwd
  *   dq, dk, dv       : out, bf16 [B,H,N,d]
  *   workspace        : device scratch of >= fa2_bwd_workspace_bytes(B,H,N,d)
@@ -96,30 +100,30 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             int B, int H, int N, int d, float scale, int causal,
             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward phase 1: delta_i = sum_k dout_ik * o_ik (fp32) for every row, and
- * dq_accum set to zero.  HBM-bound elementwise work.
- *   o, dout : in, bf16 [B,H,N,d];  delta : out, fp32 [B,H,N];
- *   dq_accum: out, fp32 [B,H,N,d] (zeroed). */
-int fa2_bwd_preprocess(const void* o, const void* dout, float* delta, float* dq_accum,
-                       int B, int H, int N, int d, void* stream);
+/* Backward phase 1 (HBM-bound, elementwise): for every row i of every head,
+ * delta_i = sum_k dout_ik * o_ik and lse_log2_i = lse_i * log2(e); rows from N
+ * up to fa2_bwd_rows_padded(N) get delta 0 and lse_log2 +inf.
+ *   o, dout : in, bf16 [B,H,N,d];  lse : in, fp32 [B,H,N]
+ *   delta, lse_log2 : out, fp32 [B,H,Np], Np = fa2_bwd_rows_padded(N) */
+int fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, float* delta,
+                       float* lse_log2, int B, int H, int N, int d, void* stream);
 
-/* Backward phase 2: one key/value column-block per workgroup, looping over the
- * query row-blocks that can see it (causal: from the diagonal on).  Recomputes
- * P = exp(scale q k^T - L), writes dK and dV (bf16), and adds the unscaled
- * dS K contributions to dq_accum with fp32 atomics (so dq_accum must start
- * zeroed, as fa2_bwd_preprocess leaves it).
- *   q, k, v, dout : in, bf16;  lse, delta : in, fp32 [B,H,N]
- *   dq_accum      : in/out, fp32 [B,H,N,d];  dk, dv : out, bf16 [B,H,N,d] */
-int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                 const void* dout, const float* delta, float* dq_accum,
-                 void* dk, void* dv,
+/* Backward phase 2: dK and dV.  One key/value column-block per workgroup,
+ * looping over the query row-blocks that can see it (causal: from the diagonal
+ * on), recomputing P = exp(scale q k^T - L) from lse_log2.
+ *   q, k, v, dout   : in, bf16 [B,H,N,d];  lse_log2, delta : in, from phase 1
+ *   dk, dv          : out, bf16 [B,H,N,d] */
+int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                 const float* lse_log2, const float* delta, void* dk, void* dv,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 
-/* Backward phase 3: dq = bf16(scale * dq_accum), applying the softmax scale
- * once at the end rather than per tile.
- *   dq_accum : in, fp32 [B,H,N,d];  dq : out, bf16 [B,H,N,d] */
-int fa2_bwd_dq_convert(const float* dq_accum, void* dq, int B, int H, int N, int d,
-                       float scale, void* stream);
+/* Backward phase 3: dQ.  One query row-block per workgroup, looping over the
+ * key tiles it can see, recomputing S and dP; no atomics, no accumulator.
+ *   q, k, v, dout   : in, bf16 [B,H,N,d];  lse_log2, delta : in, from phase 1
+ *   dq              : out, bf16 [B,H,N,d] */
+int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+               const float* lse_log2, const float* delta, void* dq,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

@@ -89,7 +89,7 @@ def bwd(lib, ws_bytes=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, **ptrs
 @host_only
 def test_bwd_rejects(lib):
     need = lib.fa2_bwd_workspace_bytes(1, 2, 128, 64)
-    assert need == 1024 + 2 * 128 * 64 * 4
+    assert need == 2 * (2 * 128 * 4)
     assert bwd(lib, ws_bytes=need - 1) == WORKSPACE
     assert bwd(lib, ws_bytes=0) == WORKSPACE
     assert bwd(lib, d=72) == UNSUPPORTED
@@ -104,20 +104,34 @@ def test_bwd_rejects(lib):
 
 @host_only
 def test_phase_entry_points_reject(lib):
-    assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[3], 1, 1, 0, 64, None) == INVALID
-    assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[0], 1, 1, 64, 64, None) == INVALID
-    assert lib.fa2_bwd_dkdv(*P[:9], 1, 1, 64, 100, 0.1, 0, None) == UNSUPPORTED
-    assert lib.fa2_bwd_dkdv(*P[:9], 1, 1, 64, 64, 0.0, 0, None) == INVALID
-    assert lib.fa2_bwd_dq_convert(P[0], P[0] + 16, 1, 1, 64, 64, 0.1, None) == INVALID
-    assert lib.fa2_bwd_dq_convert(P[0], P[1], 1, 1, 64, 64, float("nan"), None) == INVALID
+    # preprocess(o, dout, lse, delta, lse_log2, B, H, N, d, stream)
+    assert lib.fa2_bwd_preprocess(*P[:5], 1, 1, 0, 64, None) == INVALID
+    assert lib.fa2_bwd_preprocess(*P[:5], 1, 1, 64, 96, None) == UNSUPPORTED
+    assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[0], P[4], 1, 1, 64, 64, None) == INVALID
+    assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[3], P[3] + 256, 1, 1, 64, 64, None) == INVALID
+    # dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d, scale, causal, stream)
+    assert lib.fa2_bwd_dkdv(*P[:8], 1, 1, 64, 100, 0.1, 0, None) == UNSUPPORTED
+    assert lib.fa2_bwd_dkdv(*P[:8], 1, 1, 64, 64, 0.0, 0, None) == INVALID
+    assert lib.fa2_bwd_dkdv(*P[:7], None, 1, 1, 64, 64, 0.1, 0, None) == INVALID
+    assert lib.fa2_bwd_dkdv(*P[:7], P[6] + 16, 1, 1, 64, 64, 0.1, 0, None) == INVALID
+    assert lib.fa2_bwd_dkdv(*P[:6], P[0], P[7], 1, 1, 64, 64, 0.1, 0, None) == INVALID
+    # dq(q, k, v, dout, lse_log2, delta, dq, B, H, N, d, scale, causal, stream)
+    assert lib.fa2_bwd_dq(*P[:7], 1, 1, 64, 64, 0.1, 5, None) == INVALID
+    assert lib.fa2_bwd_dq(*P[:6], P[4], 1, 1, 64, 64, 0.1, 0, None) == INVALID
+    assert lib.fa2_bwd_dq(*P[:6], P[6] + 8, 1, 1, 64, 64, 0.1, 0, None) == INVALID
 
 
 def test_workspace_size_query(lib):
+    assert lib.fa2_bwd_rows_padded(1) == 128
+    assert lib.fa2_bwd_rows_padded(128) == 128
+    assert lib.fa2_bwd_rows_padded(129) == 256
+    assert lib.fa2_bwd_rows_padded(0) == 0
     assert lib.fa2_bwd_workspace_bytes(1, 1, 1, 96) == 0
     assert lib.fa2_bwd_workspace_bytes(0, 1, 1, 64) == 0
-    # delta region and accumulator, each rounded up to 256 bytes
-    assert lib.fa2_bwd_workspace_bytes(1, 1, 3, 80) == 256 + 1024
-    assert lib.fa2_bwd_workspace_bytes(1, 16, 16384, 128) == 16 * 16384 * 4 + 16 * 16384 * 128 * 4
+    # delta and L*log2(e), fp32 [B, H, padded rows], each rounded up to 256 bytes
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 3, 80) == 2 * 512
+    assert lib.fa2_bwd_workspace_bytes(1, 16, 16384, 128) == 2 * 16 * 16384 * 4
+    assert lib.fa2_bwd_workspace_bytes(3, 1, 200, 64) == 2 * 3 * 256 * 4
 
 
 def test_strerror_and_tiles(lib):

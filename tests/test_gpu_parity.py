@@ -307,3 +307,30 @@ def test_errors_raise():
     assert e.value.status == 1
     with pytest.raises(ValueError):
         fa2.fwd(q.float(), q, q)
+
+
+@pytest.mark.parametrize("d,causal,N", [(64, True, 200), (80, False, 129), (128, True, 333)])
+def test_phases_compose_to_bwd(d, causal, N):
+    """fa2_bwd == preprocess + dkdv + dq called one by one (the way bench.py times them)."""
+    B, H = 2, 2
+    arrs = gen.make_arrays(B, H, N, d, seed=31)
+    q, k, v, do = (to_dev(arrs[n]) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa2.fwd(q, k, v, causal=causal, scale=scale)
+    dq_a, dk_a, dv_a = fa2.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    delta, lse2 = fa2.bwd_row_arrays(B, H, N, q.device)
+    dq_b, dk_b, dv_b = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    fa2.bwd_preprocess(o, do, lse, delta, lse2)
+    fa2.bwd_dkdv(q, k, v, do, lse2, delta, dk_b, dv_b, causal=causal, scale=scale)
+    fa2.bwd_dq(q, k, v, do, lse2, delta, dq_b, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for name, a, b in (("dq", dq_a, dq_b), ("dk", dk_a, dk_b), ("dv", dv_a, dv_b)):
+        same = torch.equal(a, b)
+        assert same, name
+    npad = fa2.bwd_rows_padded(N)
+    assert tuple(delta.shape) == (B, H, npad)
+    pad_delta = float(delta[:, :, N:].abs().max()) if npad > N else 0.0
+    pad_inf = bool(torch.isinf(lse2[:, :, N:]).all()) if npad > N else True
+    assert pad_delta == 0.0 and pad_inf
+    rel = float(((lse2[:, :, :N] - lse * math.log2(math.e)).abs() / lse.abs().clamp_min(1e-3)).max())
+    assert rel <= 1e-6, rel
