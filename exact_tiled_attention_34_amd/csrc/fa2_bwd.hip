@@ -13,22 +13,27 @@
 //                 S  = Q K^T          P  = 2^(c S - L log2 e),  c = scale log2 e
 //                 dP = dO V^T         dS = P (dP - delta)
 //                 dV^T += dO^T P      dK^T += Q^T dS
-//               P and dS feed their MFMAs straight from registers; dO^T and Q^T
-//               are transposed reads of the row-major Q/dO tiles in LDS.
-//   dq          one workgroup per (128-query row block, batch*head), shaped like the
-//               forward: Q and dO stay in registers, K/V tiles stream through LDS:
+//               P and dS feed their MFMAs straight from registers; Q and dO are
+//               in LDS twice per step, row-major (loaded global -> LDS directly)
+//               and transposed (staged through registers).
+//   dq          one workgroup of 8 wavefronts per (256-query row block, batch*head),
+//               shaped like the forward: Q and dO stay in registers, K/V tiles (and a
+//               transposed copy of K) stream through LDS:
 //                 S^T = K Q^T   dP^T = V dO^T   dS^T = P^T (dP^T - delta)
 //                 dQ^T += K^T dS^T
 //               This second pass recomputes S and dP instead of adding partial dQ
 //               with atomics (it needs no fp32 accumulator and no atomics).
 // The softmax scale of dQ and dK is applied once, in the epilogues
 // ("FlashAttention-2" summary page, "How It Works" 2).
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
 namespace fa2 {
 
-int bwd_rows_padded(int N) { return (N + 127) / 128 * 128; }
+// Multiple of every query block size the backward kernels use (64 and 256).
+int bwd_rows_padded(int N) { return (N + 255) / 256 * 256; }
 
 namespace {
 
@@ -79,6 +84,8 @@ struct DkdvCfg {
   static constexpr int DK = D / 16;
   static constexpr int NQB = BQ / 32;
   static constexpr int TILE = RowTile<D>::elems(BQ);
+  static constexpr int TTILE = TrTile<D, 64>::ELEMS;
+  static_assert(BQ == 64, "transposed tiles hold 64 tokens");
 };
 
 template <int D, bool CAUSAL>
@@ -87,10 +94,13 @@ struct DkdvWave {
   bf16x8 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
+  LaneOffsets<D> off;
 
+  // qt, dot: row-major Q and dO tiles; qtt, dott: their transposes.
   template <bool MASK>
-  __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const float* l2s,
-                                       const float* dls, int q0, int N, float scale_log2) {
+  __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const uint16_t* qtt,
+                                       const uint16_t* dott, const float* l2s, const float* dls,
+                                       int q0, int N, float scale_log2) {
     f32x16 sacc[C::NQB], pacc[C::NQB];
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
@@ -101,8 +111,9 @@ struct DkdvWave {
       }
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
-        sacc[qb] = mfma32x32x16(row_operand<D>(qt, qb * 32 + lr, s * 16 + 8 * lh), kf[s], sacc[qb]);
-        pacc[qb] = mfma32x32x16(row_operand<D>(dot, qb * 32 + lr, s * 16 + 8 * lh), vf[s], pacc[qb]);
+        const int o = off.row[s] + 2 * qb * LaneOffsets<D>::ROW16;
+        sacc[qb] = mfma32x32x16(lds_read16(qt + o), kf[s], sacc[qb]);
+        pacc[qb] = mfma32x32x16(lds_read16(dot + o), vf[s], pacc[qb]);
       }
     }
     uint32_t pw[C::NQB][8], dsw[C::NQB][8];
@@ -135,8 +146,9 @@ struct DkdvWave {
       const bf16x8 bs = acc_chunk(dsw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb) {
-        dvacc[mb] = mfma32x32x16(tr_operand<D>(dot, 16 * c, 32 * mb, lane), bp, dvacc[mb]);
-        dkacc[mb] = mfma32x32x16(tr_operand<D>(qt, 16 * c, 32 * mb, lane), bs, dkacc[mb]);
+        const int o = off.tr + 16 * c + mb * LaneOffsets<D>::TR32;
+        dvacc[mb] = mfma32x32x16(lds_read16(dott + o), bp, dvacc[mb]);
+        dkacc[mb] = mfma32x32x16(lds_read16(qtt + o), bs, dkacc[mb]);
       }
     }
   }
@@ -152,10 +164,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   using C = DkdvCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][C::TTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[2][C::TTILE];
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * C::BQ];   // [L log2e | delta]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  for (int b = 0; b < 2; ++b) {
+    TrTile<D>::zero_pad(qt_lds[b], tid, C::THREADS);
+    TrTile<D>::zero_pad(dot_lds[b], tid, C::THREADS);
+  }
 
   // Linear id -> (key block, batch*head); consecutive ids take different heads
   // (XCD round-robin keeps one head's blocks on one XCD).  Key block 0 sees the
@@ -180,12 +198,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       if (lane < C::BQ / 2) global_load_lds16(src, dst);
     }
   };
+  TrStage<D> qstage, dostage;
   auto load_step = [&](int i, int buf) {
     load_tile_async<D, C::BQ, C::THREADS>(q_lds[buf], Qh, i * C::BQ, N, tid);
     load_tile_async<D, C::BQ, C::THREADS>(do_lds[buf], dOh, i * C::BQ, N, tid);
     load_ld(ld_lds[buf], i * C::BQ);
+    qstage.load(Qh, i * C::BQ, N, tid);
+    dostage.load(dOh, i * C::BQ, N, tid);
+  };
+  auto store_step = [&](int buf) {
+    qstage.store(qt_lds[buf], tid);
+    dostage.store(dot_lds[buf], tid);
   };
   load_step(i_begin, 0);
+  store_step(0);
 
   DkdvWave<D, CAUSAL> w;
   w.lane = tid & 63;
@@ -193,6 +219,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   w.lh = w.lane >> 5;
   w.key_w = key_wg + wave * 32;
   w.key_lane = w.key_w + w.lr;
+  w.off.init(w.lane);
   // K, V as B operands (lane: one key, 8 consecutive features per k-step).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
@@ -212,19 +239,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       w.dvacc[mb][t] = 0.f;
     }
 
-  for (int i = i_begin; i < n_qblk; ++i) {
-    const int buf = (i - i_begin) & 1;
+  // Step i uses buffer (i - i_begin) % 2; unrolled by two so the buffer is a
+  // compile-time offset of every LDS read.
+  auto iteration = [&](auto buf_tag, int i) {
+    constexpr int BUF = decltype(buf_tag)::value;
     wait_vmem();
     __syncthreads();   // step i is in LDS; every wave is done with the other buffer
-    if (i + 1 < n_qblk) load_step(i + 1, buf ^ 1);
+    const bool more = i + 1 < n_qblk;
+    if (more) load_step(i + 1, BUF ^ 1);
     const int q0 = i * C::BQ;
     const bool need_mask = (CAUSAL && w.key_w + 31 > q0) || (w.key_w + 32 > N);
     const bool active = !CAUSAL || w.key_w <= q0 + C::BQ - 1;
     if (!need_mask) {
-      w.template step<false>(q_lds[buf], do_lds[buf], ld_lds[buf], ld_lds[buf] + C::BQ, q0, N, scale_log2);
+      w.template step<false>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
+                             ld_lds[BUF] + C::BQ, q0, N, scale_log2);
     } else if (active) {
-      w.template step<true>(q_lds[buf], do_lds[buf], ld_lds[buf], ld_lds[buf] + C::BQ, q0, N, scale_log2);
+      w.template step<true>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
+                            ld_lds[BUF] + C::BQ, q0, N, scale_log2);
     }
+    if (more) store_step(BUF ^ 1);
+  };
+  for (int i = i_begin; i < n_qblk; i += 2) {
+    iteration(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n_qblk) iteration(std::integral_constant<int, 1>{}, i + 1);
   }
 
   // Epilogue: dK = scale * dS^T Q, dV = P^T dO (bf16).
@@ -253,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
   static constexpr int BC = 64;                   // keys per K/V tile
@@ -261,6 +298,7 @@ struct DqCfg {
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
   static constexpr int TILE = RowTile<D>::elems(BC);
+  static constexpr int TTILE = TrTile<D, 64>::ELEMS;
 };
 
 template <int D, bool CAUSAL>
@@ -270,10 +308,12 @@ struct DqWave {
   f32x16 dqacc[C::NDB];
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
+  LaneOffsets<D> off;
 
+  // kt, vt: row-major K and V tiles; ktt: transposed K tile.
   template <bool MASK>
-  __device__ __forceinline__ void tile(const uint16_t* kt, const uint16_t* vt, int key0, int N,
-                                       float scale_log2) {
+  __device__ __forceinline__ void tile(const uint16_t* kt, const uint16_t* vt, const uint16_t* ktt,
+                                       int key0, int N, float scale_log2) {
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -284,8 +324,9 @@ struct DqWave {
       }
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
-        sacc[kb] = mfma32x32x16(row_operand<D>(kt, kb * 32 + lr, s * 16 + 8 * lh), qf[s], sacc[kb]);
-        pacc[kb] = mfma32x32x16(row_operand<D>(vt, kb * 32 + lr, s * 16 + 8 * lh), dof[s], pacc[kb]);
+        const int o = off.row[s] + 2 * kb * LaneOffsets<D>::ROW16;
+        sacc[kb] = mfma32x32x16(lds_read16(kt + o), qf[s], sacc[kb]);
+        pacc[kb] = mfma32x32x16(lds_read16(vt + o), dof[s], pacc[kb]);
       }
     }
     uint32_t dsw[2][8];
@@ -309,13 +350,14 @@ struct DqWave {
       const bf16x8 b = acc_chunk(dsw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        dqacc[mb] = mfma32x32x16(tr_operand<D>(kt, 16 * c, 32 * mb, lane), b, dqacc[mb]);
+        dqacc[mb] = mfma32x32x16(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D>::TR32), b,
+                                 dqacc[mb]);
     }
   }
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
@@ -323,9 +365,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][C::TTILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  TrTile<D>::zero_pad(kt_lds[0], tid, C::THREADS);
+  TrTile<D>::zero_pad(kt_lds[1], tid, C::THREADS);
   const int nrb = (N + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;
@@ -341,14 +386,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   w.lh = w.lane >> 5;
   w.q_wave = rb * C::BR + wave * 32;
   w.q_lane = w.q_wave + w.lr;
+  w.off.init(w.lane);
 
   const int q_first = rb * C::BR;
   int n_tiles = (N + C::BC - 1) / C::BC;
   if (CAUSAL) n_tiles = min(n_tiles, (q_first + C::BR - 1) / C::BC + 1);
   const int n_full = min(n_tiles, (CAUSAL ? min(q_first + 1, N) : N) / C::BC);
 
+  TrStage<D> kstage;
   load_tile_async<D, C::BC, C::THREADS>(k_lds[0], Kh, 0, N, tid);
   load_tile_async<D, C::BC, C::THREADS>(v_lds[0], Vh, 0, N, tid);
+  kstage.load(Kh, 0, N, tid);
 
   // Q and dO fragments stay in registers (B operands of K Q^T and V dO^T);
   // rows past N read as zero and have L = +inf in the padded L array.
@@ -369,19 +417,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) w.dqacc[mb][i] = 0.f;
 
-  for (int j = 0; j < n_tiles; ++j) {
+  auto iteration = [&](auto buf_tag, int j) {
+    constexpr int BUF = decltype(buf_tag)::value;
     wait_vmem();
     __syncthreads();
-    if (j + 1 < n_tiles) {
-      load_tile_async<D, C::BC, C::THREADS>(k_lds[(j + 1) & 1], Kh, (j + 1) * C::BC, N, tid);
-      load_tile_async<D, C::BC, C::THREADS>(v_lds[(j + 1) & 1], Vh, (j + 1) * C::BC, N, tid);
+    const bool more = j + 1 < n_tiles;
+    if (more) {
+      load_tile_async<D, C::BC, C::THREADS>(k_lds[BUF ^ 1], Kh, (j + 1) * C::BC, N, tid);
+      load_tile_async<D, C::BC, C::THREADS>(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, N, tid);
+      kstage.load(Kh, (j + 1) * C::BC, N, tid);
     }
     const int key0 = j * C::BC;
     if (j < n_full) {
-      w.template tile<false>(k_lds[j & 1], v_lds[j & 1], key0, N, scale_log2);
+      w.template tile<false>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
     } else if (!CAUSAL || key0 <= w.q_wave + 31) {
-      w.template tile<true>(k_lds[j & 1], v_lds[j & 1], key0, N, scale_log2);
+      w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
     }
+    if (more) kstage.store(kt_lds[BUF ^ 1], tid);
+  };
+  kstage.store(kt_lds[0], tid);
+  for (int j = 0; j < n_tiles; j += 2) {
+    iteration(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) iteration(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // Epilogue: dQ = scale * dS K (bf16).

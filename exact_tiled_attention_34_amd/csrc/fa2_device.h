@@ -173,6 +173,116 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int tok0, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---------------------------------------------------------------------------
+// Transposed tiles in LDS.
+//
+// Operands whose reduction index is the token (V^T, K^T, Q^T, dO^T) need 8
+// consecutive tokens per lane, i.e. a column of the row-major tile.  A
+// transposed read instruction exists but costs several times a 16-byte read,
+// so these tiles are transposed once, while being staged: each thread loads
+// a 4-token x 8-feature block into registers, permutes it with v_perm into 8
+// feature rows of 4 tokens and writes those (8 bytes each).  Feature rows hold
+// 64 tokens (+ 8 elements of padding: rows 144 bytes apart, so 16 consecutive
+// rows cover all 64 banks).  Inside each group of 16 tokens the middle two
+// groups of four are swapped: an MFMA accumulator holds, in lane half h, the
+// tokens {4h..4h+3, 8+4h..8+4h+3}, which then lie side by side, so the
+// operand is one 16-byte read and P or dS feeds the other operand directly.
+// Feature rows at or past D (the 80 -> 96 padding) stay zero.
+// ---------------------------------------------------------------------------
+template <int D, int TOK = 64>
+struct TrTile {
+  static_assert(TOK == 32 || TOK == 64, "tokens per transposed tile");
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int ROW = TOK + 8;                // bf16 per feature row
+  static constexpr int ELEMS = DP * ROW;
+  __device__ __forceinline__ static int pos(int tok) {   // swap groups 1 and 2 of each 16
+    const int g = (tok >> 2) & 3;
+    return (tok & ~15) | ((g == 1 ? 2 : g == 2 ? 1 : g) << 2) | (tok & 3);
+  }
+  __device__ __forceinline__ static int elem(int row, int tok) { return row * ROW + pos(tok); }
+  // zero the padding rows [D, DP) (once; staging never writes them)
+  __device__ __forceinline__ static void zero_pad(uint16_t* t, int tid, int nthreads) {
+    if constexpr (DP != D)
+      for (int i = tid; i < (DP - D) * ROW; i += nthreads) t[D * ROW + i] = 0;
+  }
+};
+
+// Stager of one transposed tile of TOK tokens: load() issues the global loads
+// into registers, store() (after the values are needed, typically once the
+// current tile's compute is done) writes the transposed tile.  Thread t
+// handles tokens 4(t%G)..+3 and features 8(t/G)..+7, G = TOK/4.
+template <int D, int TOK = 64>
+struct TrStage {
+  static constexpr int CH = D / 8;
+  static constexpr int G = TOK / 4;
+  u32x4 r[4];
+  __device__ __forceinline__ bool active(int tid) const { return tid < G * CH; }
+  __device__ __forceinline__ void load(const uint16_t* head, int tok0, int n_rows, int tid) {
+    if (!active(tid)) return;
+    const int g = tid % G, ch = tid / G;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = min(tok0 + 4 * g + k, n_rows - 1);
+      r[k] = ld_global16(head + (size_t)row * D + ch * 8);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+    if (!active(tid)) return;
+    const int g = tid % G, ch = tid / G;
+    uint16_t* dst = tile + TrTile<D, TOK>::elem(8 * ch, 4 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      // feature 8 ch + e of tokens 4g..4g+3: low or high halves of word w
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 out;
+      out[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
+      out[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
+      *reinterpret_cast<u32x2*>(dst + e * TrTile<D, TOK>::ROW) = out;
+    }
+  }
+};
+
+// Per-lane LDS element offsets of the two operand reads, computed once per
+// kernel.  The chunk permutation of a RowTile depends only on row % 16, so
+// moving by whole 16-row groups (32-row operand blocks, 16-token chunks) adds
+// a compile-time constant: every read in the hot loops is one precomputed
+// register plus an immediate offset.
+template <int D, int TOK = 64>
+struct LaneOffsets {
+  static constexpr int DK = D / 16;
+  static constexpr int NDB = (D + 31) / 32;
+  static constexpr int ROW16 = 16 * RowTile<D>::SLOTS * 8;   // elements per 16 rows
+  static constexpr int TR32 = 32 * TrTile<D, TOK>::ROW;     // elements per 32 feature rows
+  int row[DK];   // row-major tile: features 16 s + 8 h .. +7 of row lane % 32
+  int tr;        // transposed tile: tokens {4h..4h+3, 8+4h..8+4h+3} of feature row lane % 32
+  __device__ __forceinline__ void init(int lane) {
+    const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < DK; ++s) row[s] = RowTile<D>::elem(lr, s * 16 + 8 * lh);
+    tr = lr * TrTile<D, TOK>::ROW + 8 * lh;   // + 16 c (token chunk) + TR32 mb (feature block)
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed operand from two precomputed addresses (see tr_operand).
+__device__ __forceinline__ bf16x8 lds_read_tr(const uint16_t* lo_p, const uint16_t* hi_p) {
+  i16x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) uint16_t*)lo_p);
+  hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) uint16_t*)hi_p);
+#else
+  (void)lo_p; (void)hi_p;
+#endif
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // bf16x8 B operand for 16 tokens (chunk c of a 32-row accumulator pair) from
 // packed accumulator words w[0..7] (w[t] = rows 2t, 2t+1 of the accumulator).
 __device__ __forceinline__ bf16x8 acc_chunk(const uint32_t* w, int half) {

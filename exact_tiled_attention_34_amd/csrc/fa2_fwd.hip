@@ -17,14 +17,24 @@
 //                          Partitioning" page, closing sentence)
 //   online softmax         m' = max(m, rowmax S); P = 2^(c S - c m'),
 //                          c = scale*log2(e); l = 2^(c(m-m')) l + rowsum P;
-//                          O *= 2^(c(m-m'))
-//   O^T += V^T P^T         bf16 MFMA; V^T comes from the row-major V tile by
-//                          transposed LDS reads, P^T straight from registers
+//                          O *= 2^(c(m-m')).  The rescale of O is skipped for
+//                          the whole wavefront when no row's max grew in this
+//                          tile (then every factor is exactly 1), which after
+//                          the first tiles is the common case
+//                          ("FlashAttention-2" summary page, "How It Works" 2:
+//                          scaling kept out of the inner loop).  The largest P
+//                          of a row is exactly 1, so it is exact in bf16.
+//   O^T += V^T P^T         bf16 MFMA; V^T is a transposed LDS tile, P^T comes
+//                          straight from registers
 // After the last tile, O is divided by l once ("FlashAttention-2" summary page,
 // "How It Works" 2) and L = (c m + log2 l) ln 2 is stored.
 //
-// K/V tiles go global -> LDS directly (no registers), double-buffered: the
-// loads of tile j+1 are issued right after the barrier that opens tile j.
+// K tiles go global -> LDS directly (no registers); V tiles are transposed on
+// the way (global -> registers -> LDS).  Both are double-buffered: the loads
+// of tile j+1 are issued right after the barrier that opens tile j, and the
+// transposed V tile is written once tile j's products are issued.
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -36,11 +46,13 @@ struct FwdCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per K/V tile
+  static constexpr int BC = 64;                   // keys per K/V tile (32 or 64)
+  static constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
   static constexpr int DP = (D + 31) / 32 * 32;   // O^T rows padded to whole 32-row MFMA blocks
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;               // k-steps of K Q^T
   static constexpr int TILE = RowTile<D>::elems(BC);
+  static constexpr int VTILE = TrTile<D, BC>::ELEMS;
 };
 
 template <int D, bool CAUSAL>
@@ -48,26 +60,35 @@ struct FwdWave {
   using C = FwdCfg<D>;
   bf16x8 qf[C::DK];
   f32x16 oacc[C::NDB];
+  f32x16 sc[1][C::KB];  // scores of the current tile
   float m_run, l_run;
   int lane, lr, lh, q_wave, q_lane;
+  LaneOffsets<D, FwdCfg<D>::BC> off;
 
-  // One K/V tile for this wavefront.  MASK: the tile may hold keys past the
-  // end of the sequence or above the diagonal for some of this wave's rows.
-  template <bool MASK>
-  __device__ __forceinline__ void tile(const uint16_t* kt, const uint16_t* vt, int key0, int N,
-                                       float scale_log2) {
-    f32x16 sacc[2];
+  // S^T (64 keys x this wave's 32 queries) of the K tile at kt.
+  __device__ __forceinline__ void scores(const uint16_t* kt, f32x16 (&sacc)[C::KB]) const {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < C::DK; ++s)
-        sacc[kb] = mfma32x32x16(row_operand<D>(kt, kb * 32 + lr, s * 16 + 8 * lh), qf[s], sacc[kb]);
+        sacc[kb] = mfma32x32x16(lds_read16(kt + off.row[s] + 2 * kb * LaneOffsets<D, FwdCfg<D>::BC>::ROW16), qf[s],
+                                sacc[kb]);
     }
+  }
+
+  // Online-softmax step on the scores of the tile starting at key0: P packed to
+  // bf16 (pw), running max and sum updated.  Returns the factor that O must be
+  // multiplied by (exactly 1 in every lane whose max did not grow); `any` tells
+  // whether some lane's factor differs from 1.  MASK: the tile may hold keys past
+  // the end of the sequence or above the diagonal for some of this wave's rows.
+  template <bool MASK>
+  __device__ __forceinline__ float softmax(f32x16 (&sacc)[C::KB], uint32_t (&pw)[C::KB][8], bool& any,
+                                           int key0, int N, float scale_log2) {
     if (MASK) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
@@ -76,24 +97,17 @@ struct FwdWave {
     }
     float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx);
+    const bool grow = mx > m_run;          // the first tile always grows (from -inf)
+    const float m_new = grow ? mx : m_run;
     const float alpha = exp2_fast((m_run - m_new) * scale_log2);
     const float mc = m_new * scale_log2;
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int mb = 0; mb < C::NDB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
-
-    uint32_t pw[2][8];
     float rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -mc));
@@ -101,18 +115,73 @@ struct FwdWave {
         rs += p0 + p1;
         pw[kb][i >> 1] = pack_bf16x2(p0, p1);
       }
-    l_run += rs;
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    any = __any(grow);
+    return alpha;
+  }
 
-    // O^T (d x query) += V^T (d x 16 keys) P^T (16 keys x query), four key chunks.
+  __device__ __forceinline__ void rescale(float alpha) {
+#pragma unroll
+    for (int mb = 0; mb < C::NDB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
+  }
+
+  // O^T (d x query) += V^T (d x 16 keys) P^T (16 keys x query), four key chunks.
+  __device__ __forceinline__ void pv(const uint16_t* vt, const uint32_t (&pw)[C::KB][8]) {
 #pragma unroll
     for (int c = 0; c < C::BC / 16; ++c) {
       const bf16x8 b = acc_chunk(pw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        oacc[mb] = mfma32x32x16(tr_operand<D>(vt, 16 * c, 32 * mb, lane), b, oacc[mb]);
+        oacc[mb] = mfma32x32x16(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D>::BC>::TR32), b,
+                                oacc[mb]);
     }
   }
 };
+
+// Tile j (PAR = j % 2, a compile-time constant so that LDS buffers are
+// immediate offsets): issue the loads of tile j+1, then scores, softmax, the
+// rare rescale and O += V(j) P(j), then the transposed store of V(j+1).
+template <int D, bool CAUSAL, int PAR, bool MASK>
+__device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+                                         uint16_t (*k_lds)[FwdCfg<D>::TILE],
+                                         uint16_t (*v_lds)[FwdCfg<D>::VTILE], const uint16_t* Kh,
+                                         const uint16_t* Vh, int j, int n_tiles, int N, int tid,
+                                         float scale_log2) {
+  using C = FwdCfg<D>;
+  wait_vmem();
+  __syncthreads();   // tile j is in LDS; every wave is done with the other buffer
+  const bool more = j + 1 < n_tiles;
+  if (more) {
+    load_tile_async<D, C::BC, C::THREADS>(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, N, tid);
+    vstage.load(Vh, (j + 1) * C::BC, N, tid);
+  }
+  // a wavefront whose rows all precede the tile's first key has nothing to do
+  if (!MASK || !CAUSAL || j * C::BC <= w.q_wave + 31) {
+    w.scores(k_lds[PAR], w.sc[0]);
+    uint32_t pw[C::KB][8];
+    bool any;
+    const float alpha = w.template softmax<MASK>(w.sc[0], pw, any, j * C::BC, N, scale_log2);
+    if (any) w.rescale(alpha);
+    w.pv(v_lds[PAR], pw);
+  }
+  if (more) vstage.store(v_lds[PAR ^ 1], tid);
+}
+
+template <int D, bool CAUSAL, int PAR>
+__device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+                                             uint16_t (*k_lds)[FwdCfg<D>::TILE],
+                                             uint16_t (*v_lds)[FwdCfg<D>::VTILE],
+                                             const uint16_t* Kh, const uint16_t* Vh, int j,
+                                             int n_tiles, int n_full, int N, int tid,
+                                             float scale_log2) {
+  if (j < n_full)
+    fwd_tile<D, CAUSAL, PAR, false>(w, vstage, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
+  else
+    fwd_tile<D, CAUSAL, PAR, true>(w, vstage, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
@@ -121,10 +190,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     int BH, int N, float scale_log2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::VTILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  TrTile<D, C::BC>::zero_pad(v_lds[0], tid, C::THREADS);
+  TrTile<D, C::BC>::zero_pad(v_lds[1], tid, C::THREADS);
 
   // Linear workgroup id -> (row block, batch*head).  Consecutive ids take
   // different heads, so with the round-robin dispatch over the 8 XCDs all row
@@ -147,6 +218,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   w.q_lane = w.q_wave + w.lr;
   w.m_run = -INFINITY;
   w.l_run = 0.f;
+  w.off.init(w.lane);
 #pragma unroll
   for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -158,9 +230,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   // tiles [0, n_full) hold only keys that every row of the block may see
   const int n_full = min(n_tiles, (CAUSAL ? min(q_first + 1, N) : N) / C::BC);
 
+  // Tile 0 into LDS (K directly, V transposed through registers).
+  TrStage<D, FwdCfg<D>::BC> vstage;
   load_tile_async<D, C::BC, C::THREADS>(k_lds[0], Kh, 0, N, tid);
-  load_tile_async<D, C::BC, C::THREADS>(v_lds[0], Vh, 0, N, tid);
-
+  vstage.load(Vh, 0, N, tid);
   // Q fragments stay in registers for the whole pass (B operand of S^T = K Q^T).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
@@ -168,20 +241,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     if (w.q_lane < N) z = ld_global16(Q + head_off + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
     w.qf[s] = as_bf16x8(z);
   }
+  vstage.store(v_lds[0], tid);
 
-  for (int j = 0; j < n_tiles; ++j) {
-    wait_vmem();
-    __syncthreads();   // tile j is in LDS; every wave is done with tile j-1's buffer
-    if (j + 1 < n_tiles) {
-      load_tile_async<D, C::BC, C::THREADS>(k_lds[(j + 1) & 1], Kh, (j + 1) * C::BC, N, tid);
-      load_tile_async<D, C::BC, C::THREADS>(v_lds[(j + 1) & 1], Vh, (j + 1) * C::BC, N, tid);
-    }
-    const int key0 = j * C::BC;
-    if (j < n_full) {
-      w.template tile<false>(k_lds[j & 1], v_lds[j & 1], key0, N, scale_log2);
-    } else if (!CAUSAL || key0 <= w.q_wave + 31) {   // a wave whose rows all precede key0 skips
-      w.template tile<true>(k_lds[j & 1], v_lds[j & 1], key0, N, scale_log2);
-    }
+  // Tile j uses buffer j % 2; unrolled by two so the buffer is an immediate.
+  for (int j = 0; j < n_tiles; j += 2) {
+    fwd_tile_any<D, CAUSAL, 0>(w, vstage, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, N, tid, scale_log2);
+    if (j + 1 < n_tiles)
+      fwd_tile_any<D, CAUSAL, 1>(w, vstage, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, N, tid,
+                                 scale_log2);
   }
 
   // Epilogue: one division by the row sum, then O (bf16) and L (fp32, natural log).

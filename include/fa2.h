@@ -77,7 +77,7 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Rows per (batch, head) of the padded fp32 row arrays used by the backward
- * phases: N rounded up to a multiple of 128.  Returns 0 for N < 1. */
+ * phases: N rounded up to a multiple of 256.  Returns 0 for N < 1. */
 int fa2_bwd_rows_padded(int N);
 
 /* Bytes of device workspace fa2_bwd needs: delta then L*log2(e), each fp32

@@ -89,7 +89,7 @@ def bwd(lib, ws_bytes=None, B=1, H=2, N=128, d=64, scale=0.125, causal=0, **ptrs
 @host_only
 def test_bwd_rejects(lib):
     need = lib.fa2_bwd_workspace_bytes(1, 2, 128, 64)
-    assert need == 2 * (2 * 128 * 4)
+    assert need == 2 * (2 * 256 * 4)
     assert bwd(lib, ws_bytes=need - 1) == WORKSPACE
     assert bwd(lib, ws_bytes=0) == WORKSPACE
     assert bwd(lib, d=72) == UNSUPPORTED
@@ -122,14 +122,14 @@ def test_phase_entry_points_reject(lib):
 
 
 def test_workspace_size_query(lib):
-    assert lib.fa2_bwd_rows_padded(1) == 128
-    assert lib.fa2_bwd_rows_padded(128) == 128
-    assert lib.fa2_bwd_rows_padded(129) == 256
+    assert lib.fa2_bwd_rows_padded(1) == 256
+    assert lib.fa2_bwd_rows_padded(256) == 256
+    assert lib.fa2_bwd_rows_padded(257) == 512
     assert lib.fa2_bwd_rows_padded(0) == 0
     assert lib.fa2_bwd_workspace_bytes(1, 1, 1, 96) == 0
     assert lib.fa2_bwd_workspace_bytes(0, 1, 1, 64) == 0
     # delta and L*log2(e), fp32 [B, H, padded rows], each rounded up to 256 bytes
-    assert lib.fa2_bwd_workspace_bytes(1, 1, 3, 80) == 2 * 512
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 3, 80) == 2 * 1024
     assert lib.fa2_bwd_workspace_bytes(1, 16, 16384, 128) == 2 * 16 * 16384 * 4
     assert lib.fa2_bwd_workspace_bytes(3, 1, 200, 64) == 2 * 3 * 256 * 4
 
