@@ -96,60 +96,104 @@ struct DkdvWave {
   int lane, lr, lh, key_w, key_lane;
   LaneOffsets<D> off;
 
-  // qt, dot: row-major Q and dO tiles; qtt, dott: their transposes.
+  // One 64-query step.  qt, dot: row-major Q and dO tiles; qtt, dott: their
+  // transposes; l2s, dls: the step's L log2 e and delta.
+  //
+  // The step is a fixed sequence of MFMA stages, two MFMAs each:
+  //   stage t <  NS:  S and dP of query half qb = t / DK, feature chunk s = t % DK
+  //   stage NS + u:   dV and dK of 16-query chunk c = u / NDB, feature block mb = u % NDB
+  // Each stage's two LDS operands are read PF stages ahead of it.  The softmax
+  // of query half 0 runs under the S/dP MFMAs of half 1, and that of half 1
+  // under the first dV/dK MFMAs (which only need half 0): with one wavefront
+  // per SIMD this is the only way the matrix cores and the vector ALU overlap.
   template <bool MASK>
   __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const uint16_t* qtt,
                                        const uint16_t* dott, const float* l2s, const float* dls,
                                        int q0, int N, float scale_log2) {
+    static_assert(C::NQB == 2, "two 32-query halves per step");
+    constexpr int NS = C::NQB * C::DK;
+    constexpr int NT = (C::BQ / 16) * C::NDB;
+    constexpr int NALL = NS + NT;
+    constexpr int PF = 3;
+    bf16x8 ra[NALL], rb[NALL];
+    auto fetch = [&](int t) {
+      if (t < NS) {
+        const int o = off.row[t % C::DK] + 2 * (t / C::DK) * LaneOffsets<D>::ROW16;
+        ra[t] = lds_read16(qt + o);
+        rb[t] = lds_read16(dot + o);
+      } else {
+        const int u = t - NS;
+        const int o = off.tr + 16 * (u / C::NDB) + (u % C::NDB) * LaneOffsets<D>::TR32;
+        ra[t] = lds_read16(dott + o);
+        rb[t] = lds_read16(qtt + o);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < PF; ++t) fetch(t);
+
+    // Row statistics of group (qb, g): lane (lr, lh) needs queries
+    // qb*32 + 8g + 4lh + r; read one stage before the group's softmax.
+    f32x4 lv[C::NQB][4], dv[C::NQB][4];
+    auto load_stats = [&](int qb, int g) {
+      lv[qb][g] = *reinterpret_cast<const f32x4*>(l2s + qb * 32 + 8 * g + 4 * lh);
+      dv[qb][g] = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * g + 4 * lh);
+    };
+
     f32x16 sacc[C::NQB], pacc[C::NQB];
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
+    for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         sacc[qb][t] = 0.f;
         pacc[qb][t] = 0.f;
       }
-#pragma unroll
-      for (int s = 0; s < C::DK; ++s) {
-        const int o = off.row[s] + 2 * qb * LaneOffsets<D>::ROW16;
-        sacc[qb] = mfma32x32x16(lds_read16(qt + o), kf[s], sacc[qb]);
-        pacc[qb] = mfma32x32x16(lds_read16(dot + o), vf[s], pacc[qb]);
-      }
-    }
     uint32_t pw[C::NQB][8], dsw[C::NQB][8];
+    // P = 2^(c S - L log2 e) and dS = P (dP - delta) for 4 of a half's 16
+    // registers (queries qb*32 + 8g + 4lh + r), packed to bf16.
+    auto softmax_group = [&](int qb, int g) {
+      float p[4], ds[4];
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * g + r;
+        float x = exp2_fast(__builtin_fmaf(sacc[qb][t], scale_log2, -lv[qb][g][r]));
+        if (MASK && (key_lane >= N || (CAUSAL && key_lane > q0 + qb * 32 + 8 * g + 4 * lh + r))) x = 0.f;
+        p[r] = x;
+        ds[r] = x * (pacc[qb][t] - dv[qb][g][r]);
+      }
+      pw[qb][2 * g] = pack_bf16x2(p[0], p[1]);
+      pw[qb][2 * g + 1] = pack_bf16x2(p[2], p[3]);
+      dsw[qb][2 * g] = pack_bf16x2(ds[0], ds[1]);
+      dsw[qb][2 * g + 1] = pack_bf16x2(ds[2], ds[3]);
+    };
+
+    // S = Q K^T, dP = dO V^T; softmax of half 0 from stage DK + 1 on.
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int qb = t / C::DK, s = t % C::DK;
+      sacc[qb] = mfma32x32x16(ra[t], kf[s], sacc[qb]);
+      pacc[qb] = mfma32x32x16(rb[t], vf[s], pacc[qb]);
+      if (t + PF < NALL) fetch(t + PF);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int ql = qb * 32 + 8 * g + 4 * lh;   // 4 consecutive queries of this lane
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(l2s + ql);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(dls + ql);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * g + r;
-          float p = exp2_fast(__builtin_fmaf(sacc[qb][t], scale_log2, -lv[r]));
-          if (MASK && (key_lane >= N || (CAUSAL && key_lane > q0 + ql + r))) p = 0.f;
-          sacc[qb][t] = p;
-          pacc[qb][t] = p * (pacc[qb][t] - dv[r]);
-        }
+        if (t == C::DK + g * (C::DK - 1) / 4) load_stats(0, g);
+        if (t == C::DK + 1 + g * (C::DK - 1) / 4) softmax_group(0, g);
       }
-#pragma unroll
-      for (int t = 0; t < 16; t += 2) {
-        pw[qb][t >> 1] = pack_bf16x2(sacc[qb][t], sacc[qb][t + 1]);
-        dsw[qb][t >> 1] = pack_bf16x2(pacc[qb][t], pacc[qb][t + 1]);
-      }
+      sched_fence();
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA.
+    // dV^T += dO^T P, dK^T += Q^T dS (16 queries per MFMA); softmax of half 1
+    // under chunks 0 and 1.
 #pragma unroll
-    for (int c = 0; c < C::BQ / 16; ++c) {
-      const bf16x8 bp = acc_chunk(pw[c >> 1], c & 1);
-      const bf16x8 bs = acc_chunk(dsw[c >> 1], c & 1);
+    for (int u = 0; u < NT; ++u) {
+      const int t = NS + u, c = u / C::NDB, mb = u % C::NDB;
+      dvacc[mb] = mfma32x32x16(ra[t], acc_chunk(pw[c >> 1], c & 1), dvacc[mb]);
+      dkacc[mb] = mfma32x32x16(rb[t], acc_chunk(dsw[c >> 1], c & 1), dkacc[mb]);
+      if (t + PF < NALL) fetch(t + PF);
 #pragma unroll
-      for (int mb = 0; mb < C::NDB; ++mb) {
-        const int o = off.tr + 16 * c + mb * LaneOffsets<D>::TR32;
-        dvacc[mb] = mfma32x32x16(lds_read16(dott + o), bp, dvacc[mb]);
-        dkacc[mb] = mfma32x32x16(lds_read16(qtt + o), bs, dkacc[mb]);
+      for (int g = 0; g < 4; ++g) {
+        if (u == g * (2 * C::NDB - 1) / 4) load_stats(1, g);
+        if (u == 1 + g * (2 * C::NDB - 1) / 4) softmax_group(1, g);
       }
+      sched_fence();
     }
   }
 };
@@ -171,8 +215,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   for (int b = 0; b < 2; ++b) {
-    TrTile<D>::zero_pad(qt_lds[b], tid, C::THREADS);
-    TrTile<D>::zero_pad(dot_lds[b], tid, C::THREADS);
+    tr_zero_pad<D>(qt_lds[b], tid, C::THREADS);
+    tr_zero_pad<D>(dot_lds[b], tid, C::THREADS);
   }
 
   // Linear id -> (key block, batch*head); consecutive ids take different heads
@@ -191,24 +235,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int i_begin = CAUSAL ? key_wg / C::BQ : 0;
 
   // L log2 e and delta of one query block: 2 x 64 floats, 16 bytes per lane.
+  // (lanes 16..31 land 256 bytes after lanes 0..15, i.e. at the delta half)
   auto load_ld = [&](float* dst, int q0) {
     if (wave == 0) {
       const int lane = tid & 63;
-      const float* src = lane < C::BQ / 4 ? L2h + q0 + 4 * lane : Dh + q0 + 4 * (lane - C::BQ / 4);
-      if (lane < C::BQ / 2) global_load_lds16(src, dst);
+      if (lane < C::BQ / 4)
+        global_load_lds16(L2h + q0, 16u * lane, dst);
+      else if (lane < C::BQ / 2)
+        global_load_lds16(Dh + q0, 16u * (lane - C::BQ / 4), dst);
     }
   };
+  // Q and dO go through registers once and are written twice per step:
+  // row-major and transposed.
   TrStage<D> qstage, dostage;
+  qstage.init(tid);
+  dostage.init(tid);
   auto load_step = [&](int i, int buf) {
-    load_tile_async<D, C::BQ, C::THREADS>(q_lds[buf], Qh, i * C::BQ, N, tid);
-    load_tile_async<D, C::BQ, C::THREADS>(do_lds[buf], dOh, i * C::BQ, N, tid);
     load_ld(ld_lds[buf], i * C::BQ);
-    qstage.load(Qh, i * C::BQ, N, tid);
-    dostage.load(dOh, i * C::BQ, N, tid);
+    qstage.load(Qh, i * C::BQ, N);
+    dostage.load(dOh, i * C::BQ, N);
   };
   auto store_step = [&](int buf) {
-    qstage.store(qt_lds[buf], tid);
-    dostage.store(dot_lds[buf], tid);
+    qstage.store(qt_lds[buf]);
+    qstage.store_rows(q_lds[buf]);
+    dostage.store(dot_lds[buf]);
+    dostage.store_rows(do_lds[buf]);
   };
   load_step(i_begin, 0);
   store_step(0);
@@ -329,6 +380,7 @@ struct DqWave {
         pacc[kb] = mfma32x32x16(lds_read16(vt + o), dof[s], pacc[kb]);
       }
     }
+    mfma_pipeline_hint<1, 4 * C::DK, 4 * C::DK, 6>();
     uint32_t dsw[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -353,6 +405,7 @@ struct DqWave {
         dqacc[mb] = mfma32x32x16(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D>::TR32), b,
                                  dqacc[mb]);
     }
+    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
   }
 };
 
@@ -369,8 +422,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  TrTile<D>::zero_pad(kt_lds[0], tid, C::THREADS);
-  TrTile<D>::zero_pad(kt_lds[1], tid, C::THREADS);
+  tr_zero_pad<D>(kt_lds[0], tid, C::THREADS);
+  tr_zero_pad<D>(kt_lds[1], tid, C::THREADS);
   const int nrb = (N + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;
@@ -393,10 +446,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   if (CAUSAL) n_tiles = min(n_tiles, (q_first + C::BR - 1) / C::BC + 1);
   const int n_full = min(n_tiles, (CAUSAL ? min(q_first + 1, N) : N) / C::BC);
 
+  // K goes through registers (written row-major and transposed), V is copied
+  // to LDS directly.
   TrStage<D> kstage;
-  load_tile_async<D, C::BC, C::THREADS>(k_lds[0], Kh, 0, N, tid);
-  load_tile_async<D, C::BC, C::THREADS>(v_lds[0], Vh, 0, N, tid);
-  kstage.load(Kh, 0, N, tid);
+  TileDma<D, C::BC, C::THREADS> vdma;
+  kstage.init(tid);
+  vdma.init(tid);
+  vdma.issue(v_lds[0], Vh, 0, N);
+  kstage.load(Kh, 0, N);
 
   // Q and dO fragments stay in registers (B operands of K Q^T and V dO^T);
   // rows past N read as zero and have L = +inf in the padded L array.
@@ -423,9 +480,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     __syncthreads();
     const bool more = j + 1 < n_tiles;
     if (more) {
-      load_tile_async<D, C::BC, C::THREADS>(k_lds[BUF ^ 1], Kh, (j + 1) * C::BC, N, tid);
-      load_tile_async<D, C::BC, C::THREADS>(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, N, tid);
-      kstage.load(Kh, (j + 1) * C::BC, N, tid);
+      vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, N);
+      kstage.load(Kh, (j + 1) * C::BC, N);
     }
     const int key0 = j * C::BC;
     if (j < n_full) {
@@ -433,9 +489,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     } else if (!CAUSAL || key0 <= w.q_wave + 31) {
       w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
     }
-    if (more) kstage.store(kt_lds[BUF ^ 1], tid);
+    if (more) {
+      kstage.store(kt_lds[BUF ^ 1]);
+      kstage.store_rows(k_lds[BUF ^ 1]);
+    }
   };
-  kstage.store(kt_lds[0], tid);
+  kstage.store(kt_lds[0]);
+  kstage.store_rows(k_lds[0]);
   for (int j = 0; j < n_tiles; j += 2) {
     iteration(std::integral_constant<int, 0>{}, j);
     if (j + 1 < n_tiles) iteration(std::integral_constant<int, 1>{}, j + 1);

@@ -76,6 +76,7 @@ struct FwdWave {
         sacc[kb] = mfma32x32x16(lds_read16(kt + off.row[s] + 2 * kb * LaneOffsets<D, FwdCfg<D>::BC>::ROW16), qf[s],
                                 sacc[kb]);
     }
+    mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, 6>();
   }
 
   // Online-softmax step on the scores of the tile starting at key0: P packed to
@@ -138,6 +139,7 @@ struct FwdWave {
         oacc[mb] = mfma32x32x16(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D>::BC>::TR32), b,
                                 oacc[mb]);
     }
+    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
   }
 };
 
@@ -146,6 +148,7 @@ struct FwdWave {
 // rare rescale and O += V(j) P(j), then the transposed store of V(j+1).
 template <int D, bool CAUSAL, int PAR, bool MASK>
 __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+                                         const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
                                          uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                          uint16_t (*v_lds)[FwdCfg<D>::VTILE], const uint16_t* Kh,
                                          const uint16_t* Vh, int j, int n_tiles, int N, int tid,
@@ -155,8 +158,8 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCf
   __syncthreads();   // tile j is in LDS; every wave is done with the other buffer
   const bool more = j + 1 < n_tiles;
   if (more) {
-    load_tile_async<D, C::BC, C::THREADS>(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, N, tid);
-    vstage.load(Vh, (j + 1) * C::BC, N, tid);
+    kdma.issue(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, N);
+    vstage.load(Vh, (j + 1) * C::BC, N);
   }
   // a wavefront whose rows all precede the tile's first key has nothing to do
   if (!MASK || !CAUSAL || j * C::BC <= w.q_wave + 31) {
@@ -167,20 +170,21 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCf
     if (any) w.rescale(alpha);
     w.pv(v_lds[PAR], pw);
   }
-  if (more) vstage.store(v_lds[PAR ^ 1], tid);
+  if (more) vstage.store(v_lds[PAR ^ 1]);
 }
 
 template <int D, bool CAUSAL, int PAR>
 __device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+                                             const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
                                              uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                              uint16_t (*v_lds)[FwdCfg<D>::VTILE],
                                              const uint16_t* Kh, const uint16_t* Vh, int j,
                                              int n_tiles, int n_full, int N, int tid,
                                              float scale_log2) {
   if (j < n_full)
-    fwd_tile<D, CAUSAL, PAR, false>(w, vstage, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
+    fwd_tile<D, CAUSAL, PAR, false>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
   else
-    fwd_tile<D, CAUSAL, PAR, true>(w, vstage, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
+    fwd_tile<D, CAUSAL, PAR, true>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
 }
 
 template <int D, bool CAUSAL>
@@ -194,8 +198,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  TrTile<D, C::BC>::zero_pad(v_lds[0], tid, C::THREADS);
-  TrTile<D, C::BC>::zero_pad(v_lds[1], tid, C::THREADS);
+  tr_zero_pad<D, C::BC>(v_lds[0], tid, C::THREADS);
+  tr_zero_pad<D, C::BC>(v_lds[1], tid, C::THREADS);
 
   // Linear workgroup id -> (row block, batch*head).  Consecutive ids take
   // different heads, so with the round-robin dispatch over the 8 XCDs all row
@@ -231,9 +235,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const int n_full = min(n_tiles, (CAUSAL ? min(q_first + 1, N) : N) / C::BC);
 
   // Tile 0 into LDS (K directly, V transposed through registers).
-  TrStage<D, FwdCfg<D>::BC> vstage;
-  load_tile_async<D, C::BC, C::THREADS>(k_lds[0], Kh, 0, N, tid);
-  vstage.load(Vh, 0, N, tid);
+  TrStage<D, C::BC> vstage;
+  TileDma<D, C::BC, C::THREADS> kdma;
+  vstage.init(tid);
+  kdma.init(tid);
+  kdma.issue(k_lds[0], Kh, 0, N);
+  vstage.load(Vh, 0, N);
   // Q fragments stay in registers for the whole pass (B operand of S^T = K Q^T).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
@@ -241,13 +248,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     if (w.q_lane < N) z = ld_global16(Q + head_off + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
     w.qf[s] = as_bf16x8(z);
   }
-  vstage.store(v_lds[0], tid);
+  vstage.store(v_lds[0]);
 
   // Tile j uses buffer j % 2; unrolled by two so the buffer is an immediate.
   for (int j = 0; j < n_tiles; j += 2) {
-    fwd_tile_any<D, CAUSAL, 0>(w, vstage, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, N, tid, scale_log2);
+    fwd_tile_any<D, CAUSAL, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, N, tid, scale_log2);
     if (j + 1 < n_tiles)
-      fwd_tile_any<D, CAUSAL, 1>(w, vstage, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, N, tid,
+      fwd_tile_any<D, CAUSAL, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, N, tid,
                                  scale_log2);
   }
 

@@ -1,0 +1,197 @@
+// Index arithmetic of the attention kernels: LDS tile layouts, and which
+// global bytes each lane moves into which LDS slot.
+//
+// Everything here is plain integer arithmetic, compiled both into the kernels
+// (through fa2_device.h) and into a host program that enumerates every lane,
+// pass, tile and sequence length of small cases and checks that every global
+// address stays inside its tensor and every LDS slot receives the chunk the
+// layout assigns to it.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define FA2_HD __host__ __device__ __forceinline__
+#else
+#define FA2_HD inline
+#endif
+
+namespace fa2 {
+
+// ---------------------------------------------------------------------------
+// Row-major tiles in LDS.
+//
+// A tile holds ROWS token rows of D bf16 features, in 16-byte chunks.  The
+// chunk order inside a row is permuted per row so that 16-byte reads of one
+// chunk by 32 consecutive rows (the MFMA operands whose reduction index is
+// the feature: Q K^T, dO V^T, K Q^T, V dO^T) spread over the LDS banks.
+// D = 128 (16 chunks) and D = 64 (8 chunks) use an XOR of the chunk index;
+// D = 80 (10 chunks) pads every row to 11 chunk slots instead.
+// ---------------------------------------------------------------------------
+template <int D>
+struct RowTile {
+  static constexpr int CH = D / 8;
+  static constexpr bool PADDED = (CH & (CH - 1)) != 0;
+  static constexpr int SLOTS = PADDED ? CH + 1 : CH;
+  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16), "unsupported head dim");
+
+  // XOR key of a row (an involution on the chunk index); depends on row % 16.
+  static FA2_HD int swz(int row) {
+    if constexpr (PADDED) {
+      return 0;
+    } else if constexpr (CH == 16) {
+      return (4 * (row & 3)) | ((row >> 2) & 3);
+    } else {
+      const int g = (row >> 1) & 7;
+      return (4 * (g & 1)) | (g >> 1);
+    }
+  }
+  // 16-byte slot index of (row, chunk) inside the tile.
+  static FA2_HD int slot(int row, int chunk) {
+    return row * SLOTS + (PADDED ? chunk : (chunk ^ swz(row)));
+  }
+  // bf16 element offset of (row, col); col % 4 == 0.
+  static FA2_HD int elem(int row, int col) { return slot(row, col >> 3) * 8 + (col & 7); }
+  // Logical chunk stored in slot s (the pad slot of D = 80 holds chunk 0).
+  static FA2_HD int chunk_of_slot(int s) {
+    const int row = s / SLOTS;
+    const int c = s % SLOTS;
+    if constexpr (PADDED) return c >= CH ? 0 : c;
+    return c ^ swz(row);
+  }
+  // bf16 elements to reserve for a tile.
+  static constexpr int elems(int rows) { return rows * SLOTS * 8; }
+};
+
+// ---------------------------------------------------------------------------
+// Transposed tiles in LDS.
+//
+// Operands whose reduction index is the token (V^T, K^T, Q^T, dO^T) need 8
+// consecutive tokens per lane, i.e. a column of the row-major tile.  These
+// tiles are transposed once, while being staged: each thread loads a
+// 4-token x 8-feature block into registers, permutes it with v_perm into 8
+// feature rows of 4 tokens and writes those (8 bytes each).  Feature rows hold
+// TOK tokens (+ 8 elements of padding: rows 144 bytes apart for TOK = 64, so
+// 16 consecutive rows cover all 64 banks).  Inside each group of 16 tokens the
+// middle two groups of four are swapped: an MFMA accumulator holds, in lane
+// half h, the tokens {4h..4h+3, 8+4h..8+4h+3}, which then lie side by side, so
+// the operand is one 16-byte read and P or dS feeds the other operand
+// directly.  Feature rows at or past D (the 80 -> 96 padding) stay zero.
+// ---------------------------------------------------------------------------
+template <int D, int TOK = 64>
+struct TrTile {
+  static_assert(TOK == 32 || TOK == 64, "tokens per transposed tile");
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int ROW = TOK + 8;                // bf16 per feature row
+  static constexpr int ELEMS = DP * ROW;
+  static FA2_HD int pos(int tok) {   // swap groups 1 and 2 of each 16
+    const int g = (tok >> 2) & 3;
+    return (tok & ~15) | ((g == 1 ? 2 : g == 2 ? 1 : g) << 2) | (tok & 3);
+  }
+  static FA2_HD int elem(int row, int tok) { return row * ROW + pos(tok); }
+};
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copy of a RowTile of ROWS rows by THREADS threads.
+//
+// Pass t moves slots [t*THREADS, (t+1)*THREADS); wavefront w's 64 lanes move
+// the 64 consecutive slots starting at w*64 + t*THREADS (a global_load_lds
+// writes lane l's 16 bytes at its wavefront base + 16 l).  The chunk swizzle
+// repeats every 16 rows, so when a pass spans a multiple of 16 rows
+// (PERIODIC) a lane's source offset relative to the first row of its pass is
+// the same in every pass and one register holds it.
+// ---------------------------------------------------------------------------
+template <int D, int ROWS, int THREADS>
+struct DmaPlan {
+  using L = RowTile<D>;
+  static constexpr int TOTAL = ROWS * L::SLOTS;   // 16-byte slots per tile
+  static constexpr int ITER = (TOTAL + THREADS - 1) / THREADS;
+  static constexpr int RPP = THREADS / L::SLOTS;  // rows per pass (PERIODIC only)
+  static constexpr bool PERIODIC = !L::PADDED && THREADS % L::SLOTS == 0 && RPP % 16 == 0;
+  static constexpr int NOFF = PERIODIC ? 1 : ITER;
+  static_assert(TOTAL % 64 == 0 && THREADS % 64 == 0, "whole wavefronts per pass");
+
+  // First slot of pass t for wavefront `wave` (uniform); the pass exists for
+  // that wavefront iff the result is < TOTAL.
+  static FA2_HD int pass_slot(int wave, int t) { return wave * 64 + t * THREADS; }
+
+  // Byte offset, from the first row of the tile, of the source chunk of lane
+  // `lane` in pass t (stored once per lane: t < NOFF).
+  static FA2_HD uint32_t lane_offset(int wave, int lane, int t) {
+    const int s = pass_slot(wave, t) + lane;
+    return (uint32_t)((s / L::SLOTS) * D + L::chunk_of_slot(s) * 8) * 2u;
+  }
+
+  // Source of pass t given the stored offset `off` (= lane_offset(wave, lane,
+  // PERIODIC ? 0 : t)): the load reads the 16 bytes at
+  //   head + base_row * D elements + byte_off bytes.
+  // Rows at or past n_rows are clamped to n_rows - 1.  Requires
+  // 0 <= row0 < n_rows; then base_row <= row0 (it never points past the
+  // tensor) and byte_off is a non-negative offset into the tensor.
+  static FA2_HD void source(uint32_t off, int t, int row0, int n_rows, int* base_row,
+                            uint32_t* byte_off) {
+    const uint32_t in_tile = PERIODIC ? off + (uint32_t)(t * RPP * 2 * D) : off;
+    if (row0 + ROWS <= n_rows) {
+      // full tile: for PERIODIC the pass moves the scalar base instead
+      *base_row = PERIODIC ? row0 + t * RPP : row0;
+      *byte_off = off;
+      return;
+    }
+    uint32_t o = in_tile;
+    const int over = row0 + (int)(o / (2u * D)) - (n_rows - 1);
+    if (over > 0) o -= (uint32_t)over * 2u * D;
+    *base_row = row0;
+    *byte_off = o;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Register staging of a tile of TOK tokens by the first G*CH threads
+// (G = TOK/4 token groups x CH = D/8 feature chunks): thread i handles tokens
+// 4(i%G)..+3 and features 8(i/G)..+7.
+// ---------------------------------------------------------------------------
+template <int D, int TOK = 64>
+struct StagePlan {
+  static constexpr int CH = D / 8;
+  static constexpr int G = TOK / 4;
+  static constexpr int THREADS_USED = G * CH;
+  static FA2_HD bool active(int tid) { return tid < THREADS_USED; }
+  // byte offset of (token 4g, feature 8ch) from the tile's first row
+  static FA2_HD uint32_t lane_offset(int tid) {
+    return (uint32_t)(4 * (tid % G) * D + 8 * (tid / G)) * 2u;
+  }
+  static FA2_HD int grp(uint32_t off) { return (int)(off / (8u * D)); }          // 16 ch < 8 D
+  static FA2_HD int chunk(uint32_t off) { return (int)(off % (8u * D)) / 16; }
+  // Byte offset, from the tile's first row tok0 (< n_rows), of the k-th token
+  // of the lane's group, clamped to the last row n_rows - 1.
+  static FA2_HD int64_t source(uint32_t off, int k, int tok0, int n_rows) {
+    if (tok0 + TOK <= n_rows) return (int64_t)off + k * 2 * D;
+    const int g4 = 4 * grp(off);
+    int row = g4 + k;
+    if (row > n_rows - 1 - tok0) row = n_rows - 1 - tok0;
+    return (int64_t)off + (int64_t)(row - g4) * 2 * D;
+  }
+};
+
+// Per-lane LDS element offsets of the two operand reads, computed once per
+// kernel.  The chunk permutation of a RowTile depends only on row % 16, so
+// moving by whole 16-row groups (32-row operand blocks, 16-token chunks) adds
+// a compile-time constant: every read in the hot loops is one precomputed
+// register plus an immediate offset.
+template <int D, int TOK = 64>
+struct LaneOffsets {
+  static constexpr int DK = D / 16;
+  static constexpr int NDB = (D + 31) / 32;
+  static constexpr int ROW16 = 16 * RowTile<D>::SLOTS * 8;   // elements per 16 rows
+  static constexpr int TR32 = 32 * TrTile<D, TOK>::ROW;     // elements per 32 feature rows
+  int row[DK];   // row-major tile: features 16 s + 8 h .. +7 of row lane % 32
+  int tr;        // transposed tile: tokens {4h..4h+3, 8+4h..8+4h+3} of feature row lane % 32
+  FA2_HD void init(int lane) {
+    const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < DK; ++s) row[s] = RowTile<D>::elem(lr, s * 16 + 8 * lh);
+    tr = lr * TrTile<D, TOK>::ROW + 8 * lh;   // + 16 c (token chunk) + TR32 mb (feature block)
+  }
+};
+
+}  // namespace fa2

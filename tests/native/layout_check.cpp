@@ -1,0 +1,180 @@
+// Host check of the kernels' index arithmetic (fa2_layout.h), compiled with
+// the system C++ compiler: for every lane, pass, tile and sequence length of
+// small cases, every global address a tile copy or register stage computes
+// must lie inside its tensor and fetch the chunk the LDS layout assigns to
+// the slot it lands in; every slot of a tile must be written exactly once;
+// every MFMA operand read must stay inside its LDS tile.  Prints "ok" and
+// exits 0, or prints the first violation and exits 1.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "fa2_layout.h"
+
+using namespace fa2;
+
+static int failures = 0;
+#define CHECK(cond, ...)                                   \
+  do {                                                     \
+    if (!(cond)) {                                         \
+      if (failures++ < 10) {                               \
+        std::printf("FAIL %s:%d: %s | ", __FILE__, __LINE__, #cond); \
+        std::printf(__VA_ARGS__);                          \
+        std::printf("\n");                                 \
+      }                                                    \
+    }                                                      \
+  } while (0)
+
+template <int D, int ROWS, int THREADS>
+void check_dma(int max_n) {
+  using P = DmaPlan<D, ROWS, THREADS>;
+  using L = RowTile<D>;
+  const long row_bytes = 2L * D;
+  for (int n = 1; n <= max_n; ++n) {
+    for (int row0 = 0; row0 < n; row0 += ROWS) {
+      std::vector<int> written(P::TOTAL, 0);
+      for (int wave = 0; wave < THREADS / 64; ++wave) {
+        for (int t = 0; t < P::ITER; ++t) {
+          const int first = P::pass_slot(wave, t);
+          if (first >= P::TOTAL) continue;
+          for (int lane = 0; lane < 64; ++lane) {
+            const int slot = first + lane;
+            CHECK(slot < P::TOTAL, "D=%d slot %d", D, slot);
+            if (slot >= P::TOTAL) continue;
+            written[slot]++;
+            const uint32_t off = P::lane_offset(wave, lane, P::PERIODIC ? 0 : t);
+            int base_row;
+            uint32_t o;
+            P::source(off, t, row0, n, &base_row, &o);
+            CHECK(base_row >= 0 && base_row <= n - 1, "D=%d n=%d row0=%d base_row=%d", D, n, row0, base_row);
+            CHECK(o < (1u << 31), "D=%d n=%d row0=%d t=%d offset wraps: %u", D, n, row0, t, o);
+            const long addr = base_row * row_bytes + (long)o;
+            CHECK(addr >= 0 && addr + 16 <= n * row_bytes && addr % 16 == 0,
+                  "D=%d THREADS=%d n=%d row0=%d t=%d wave=%d lane=%d addr=%ld of %ld", D, THREADS, n, row0,
+                  t, wave, lane, addr, n * row_bytes);
+            const long row = addr / row_bytes;
+            const int chunk = (int)((addr % row_bytes) / 16);
+            int want_row = row0 + slot / L::SLOTS;
+            if (want_row > n - 1) want_row = n - 1;
+            CHECK(row == want_row && chunk == L::chunk_of_slot(slot),
+                  "D=%d n=%d row0=%d slot=%d: row %ld chunk %d, want %d %d", D, n, row0, slot, row, chunk,
+                  want_row, L::chunk_of_slot(slot));
+          }
+        }
+      }
+      for (int s = 0; s < P::TOTAL; ++s)
+        CHECK(written[s] == 1, "D=%d THREADS=%d slot %d written %d times", D, THREADS, s, written[s]);
+    }
+  }
+}
+
+template <int D, int TOK, int THREADS>
+void check_stage(int max_n) {
+  using P = StagePlan<D, TOK>;
+  using T = TrTile<D, TOK>;
+  using L = RowTile<D>;
+  static_assert(P::THREADS_USED <= THREADS, "stage needs more threads than the workgroup has");
+  const long row_bytes = 2L * D;
+  for (int n = 1; n <= max_n; ++n) {
+    for (int tok0 = 0; tok0 < n; tok0 += TOK) {
+      std::vector<int> cover(TOK * P::CH, 0);
+      std::vector<int> tr_written(T::ELEMS, 0), row_written(L::elems(TOK), 0);
+      for (int tid = 0; tid < THREADS; ++tid) {
+        if (!P::active(tid)) continue;
+        const uint32_t off = P::lane_offset(tid);
+        const int g = tid % P::G, ch = tid / P::G;
+        CHECK(P::grp(off) == g && P::chunk(off) == ch, "D=%d tid=%d grp/chunk", D, tid);
+        for (int k = 0; k < 4; ++k) {
+          const long addr = (long)tok0 * row_bytes + P::source(off, k, tok0, n);
+          CHECK(addr >= 0 && addr + 16 <= n * row_bytes && addr % 16 == 0, "D=%d n=%d tok0=%d tid=%d k=%d addr=%ld",
+                D, n, tok0, tid, k, addr);
+          int want = tok0 + 4 * g + k;
+          if (want > n - 1) want = n - 1;
+          CHECK(addr / row_bytes == want && (addr % row_bytes) / 16 == ch, "D=%d n=%d tid=%d k=%d row %ld want %d",
+                D, n, tid, k, addr / row_bytes, want);
+          cover[(4 * g + k) * P::CH + ch]++;
+          // store_rows: 16 bytes at RowTile elem(4g + k, 8ch)
+          const int re = L::elem(4 * g + k, 8 * ch);
+          CHECK(re >= 0 && re + 8 <= L::elems(TOK), "D=%d row store out of tile", D);
+          for (int e = 0; e < 8 && re >= 0 && re + 8 <= L::elems(TOK); ++e) row_written[re + e]++;
+        }
+        // store: feature rows 8ch + e, tokens 4g..4g+3 (8 bytes each)
+        for (int e = 0; e < 8; ++e) {
+          const int te = T::elem(8 * ch + e, 4 * g);
+          CHECK(te >= 0 && te + 4 <= T::ELEMS, "D=%d transposed store out of tile", D);
+          for (int j = 0; j < 4 && te >= 0 && te + 4 <= T::ELEMS; ++j) {
+            CHECK(T::elem(8 * ch + e, 4 * g + j) == te + j, "D=%d token group not contiguous", D);
+            tr_written[te + j]++;
+          }
+        }
+      }
+      for (int i = 0; i < TOK * P::CH; ++i) CHECK(cover[i] == 1, "D=%d (token, chunk) %d covered %d times", D, i, cover[i]);
+      for (int f = 0; f < D; ++f)
+        for (int tok = 0; tok < TOK; ++tok)
+          CHECK(tr_written[T::elem(f, tok)] == 1, "D=%d transposed (%d, %d) written %d times", D, f, tok,
+                tr_written[T::elem(f, tok)]);
+      for (int r = 0; r < TOK; ++r)
+        for (int c = 0; c < D; ++c)
+          CHECK(row_written[L::elem(r, c)] == 1, "D=%d row tile (%d, %d) written %d times", D, r, c,
+                row_written[L::elem(r, c)]);
+    }
+  }
+}
+
+// Operand reads: row-major tiles of 64 rows are read at row[s] + 2*b*ROW16
+// (b = 32-row block 0..1, s = 16-feature chunk), 8 elements; transposed
+// tiles at tr + 16c + mb*TR32 (c = 16-token chunk 0..3, mb = 32-feature
+// block), 8 elements.  Each read must stay inside its tile and fetch the
+// features / tokens the MFMA lane layout expects.
+template <int D>
+void check_reads() {
+  using O = LaneOffsets<D, 64>;
+  using L = RowTile<D>;
+  using T = TrTile<D, 64>;
+  for (int lane = 0; lane < 64; ++lane) {
+    O o;
+    o.init(lane);
+    const int lr = lane & 31, lh = lane >> 5;
+    for (int b = 0; b < 2; ++b)
+      for (int s = 0; s < O::DK; ++s) {
+        const int e = o.row[s] + 2 * b * O::ROW16;
+        CHECK(e >= 0 && e + 8 <= L::elems(64), "D=%d row read out of tile", D);
+        CHECK(e == L::elem(32 * b + lr, 16 * s + 8 * lh), "D=%d row read of lane %d b=%d s=%d", D, lane, b, s);
+      }
+    for (int c = 0; c < 4; ++c)
+      for (int mb = 0; mb < O::NDB; ++mb) {
+        const int e = o.tr + 16 * c + mb * O::TR32;
+        CHECK(e >= 0 && e + 8 <= T::ELEMS, "D=%d transposed read out of tile", D);
+        // 8 consecutive elements: tokens 16c + {4lh..4lh+3, 8+4lh..8+4lh+3} of feature 32mb + lr
+        for (int j = 0; j < 8; ++j) {
+          const int tok = 16 * c + (j < 4 ? 4 * lh + j : 8 + 4 * lh + j - 4);
+          CHECK(T::elem(32 * mb + lr, tok) == e + j, "D=%d tr read lane %d c=%d mb=%d j=%d", D, lane, c, mb, j);
+        }
+      }
+  }
+}
+
+int main() {
+  const int max_n = 3 * 64 + 9;
+  check_dma<64, 64, 256>(max_n);
+  check_dma<80, 64, 256>(max_n);
+  check_dma<128, 64, 256>(max_n);
+  check_dma<64, 64, 512>(max_n);
+  check_dma<80, 64, 512>(max_n);
+  check_dma<128, 64, 512>(max_n);
+  check_stage<64, 64, 256>(max_n);
+  check_stage<80, 64, 256>(max_n);
+  check_stage<128, 64, 256>(max_n);
+  check_stage<64, 64, 512>(max_n);
+  check_stage<80, 64, 512>(max_n);
+  check_stage<128, 64, 512>(max_n);
+  check_reads<64>();
+  check_reads<80>();
+  check_reads<128>();
+  if (failures) {
+    std::printf("%d violations\n", failures);
+    return 1;
+  }
+  std::printf("ok\n");
+  return 0;
+}
