@@ -250,8 +250,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   TrStage<D> qstage, dostage;
   qstage.init(tid);
   dostage.init(tid);
-  auto load_step = [&](int i, int buf) {
-    load_ld(ld_lds[buf], i * C::BQ);
+  auto load_stage = [&](int i) {
     qstage.load(Qh, i * C::BQ, N);
     dostage.load(dOh, i * C::BQ, N);
   };
@@ -261,7 +260,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dostage.store(dot_lds[buf]);
     dostage.store_rows(do_lds[buf]);
   };
-  load_step(i_begin, 0);
+  load_ld(ld_lds[0], i_begin * C::BQ);
+  load_stage(i_begin);
   store_step(0);
 
   DkdvWave<D, CAUSAL> w;
@@ -297,7 +297,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     wait_vmem();
     __syncthreads();   // step i is in LDS; every wave is done with the other buffer
     const bool more = i + 1 < n_qblk;
-    if (more) load_step(i + 1, BUF ^ 1);
+    if (more) load_ld(ld_lds[BUF ^ 1], (i + 1) * C::BQ);
+    // The stages are loaded and stored on every step (the last one re-stages
+    // itself into the idle buffers), so their registers never live across steps.
+    load_stage(more ? i + 1 : i);
     const int q0 = i * C::BQ;
     const bool need_mask = (CAUSAL && w.key_w + 31 > q0) || (w.key_w + 32 > N);
     const bool active = !CAUSAL || w.key_w <= q0 + C::BQ - 1;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       w.template step<true>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
                             ld_lds[BUF] + C::BQ, q0, N, scale_log2);
     }
-    if (more) store_step(BUF ^ 1);
+    store_step(BUF ^ 1);
   };
   for (int i = i_begin; i < n_qblk; i += 2) {
     iteration(std::integral_constant<int, 0>{}, i);
@@ -479,20 +482,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     wait_vmem();
     __syncthreads();
     const bool more = j + 1 < n_tiles;
-    if (more) {
-      vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, N);
-      kstage.load(Kh, (j + 1) * C::BC, N);
-    }
+    if (more) vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, N);
+    // The K stage is loaded and stored on every tile (the last one re-stages
+    // itself into the idle buffers), so its registers never live across tiles.
+    kstage.load(Kh, (more ? j + 1 : j) * C::BC, N);
     const int key0 = j * C::BC;
     if (j < n_full) {
       w.template tile<false>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
     } else if (!CAUSAL || key0 <= w.q_wave + 31) {
       w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
     }
-    if (more) {
-      kstage.store(kt_lds[BUF ^ 1]);
-      kstage.store_rows(k_lds[BUF ^ 1]);
-    }
+    kstage.store(kt_lds[BUF ^ 1]);
+    kstage.store_rows(k_lds[BUF ^ 1]);
   };
   kstage.store(kt_lds[0]);
   kstage.store_rows(k_lds[0]);

@@ -157,10 +157,10 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCf
   wait_vmem();
   __syncthreads();   // tile j is in LDS; every wave is done with the other buffer
   const bool more = j + 1 < n_tiles;
-  if (more) {
-    kdma.issue(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, N);
-    vstage.load(Vh, (j + 1) * C::BC, N);
-  }
+  if (more) kdma.issue(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, N);
+  // The V stage is loaded and stored on every tile (the last one re-stages
+  // itself into the idle buffer), so its registers never live across tiles.
+  vstage.load(Vh, (more ? j + 1 : j) * C::BC, N);
   // a wavefront whose rows all precede the tile's first key has nothing to do
   if (!MASK || !CAUSAL || j * C::BC <= w.q_wave + 31) {
     w.scores(k_lds[PAR], w.sc[0]);
@@ -170,7 +170,7 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCf
     if (any) w.rescale(alpha);
     w.pv(v_lds[PAR], pw);
   }
-  if (more) vstage.store(v_lds[PAR ^ 1]);
+  vstage.store(v_lds[PAR ^ 1]);
 }
 
 template <int D, bool CAUSAL, int PAR>
