@@ -43,7 +43,53 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 5 plain device copies of MIB MiB (read + write "
+                         "of known size: the reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) divided by what the same counters read for a
+# plain copy of known size (bench.py --calibrate-copy).  Valid only for the
+# kernel sources it was measured on: keyed by their hash, else reported null.
+MEASURED_TRAFFIC = {
+    # (kernel source hash, workload, kernel): HBM bytes read + written per launch
+    ("23722d68b6c4ef72", "c2", "bwd_dkdv"): 1359222321,
+    ("23722d68b6c4ef72", "c2", "bwd_dq"): 779791454,
+    ("23722d68b6c4ef72", "c2", "bwd_preprocess"): 138455074,
+    ("23722d68b6c4ef72", "c2", "fwd"): 1161657061,
+    ("23722d68b6c4ef72", "c4", "bwd_dkdv"): 870516751,
+    ("23722d68b6c4ef72", "c4", "bwd_dq"): 790724197,
+    ("23722d68b6c4ef72", "c4", "bwd_preprocess"): 138456802,
+    ("23722d68b6c4ef72", "c4", "fwd"): 832824760,
+}
+
+
+def kernel_source_hash():
+    import hashlib
+    d = os.path.join(ROOT, "exact_tiled_attention_34_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def calibrate_copy(mib):
+    """Five copies of a mib-MiB buffer (read mib, write mib each), for counter calibration."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_mib": mib, "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}),
+          flush=True)
 
 
 def cpu_baseline(w, arrs, budget_s):
@@ -76,6 +122,9 @@ def cpu_baseline(w, arrs, budget_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard "
               "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
@@ -150,9 +199,11 @@ def main():
     algo_flops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.6 * f_bwd}
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kern_ms[n])
     achieved = algo_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    src = kernel_source_hash()
+    traffic = MEASURED_TRAFFIC.get((src, w.key, dom))
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+                "traffic": traffic, "kernel_source": src}
 
     props = torch.cuda.get_device_properties(dev)
     line = {
