@@ -97,7 +97,9 @@ struct DkdvWave {
   LaneOffsets<D> off;
 
   // One 64-query step.  qt, dot: row-major Q and dO tiles; qtt, dott: their
-  // transposes; l2s, dls: the step's L log2 e and delta.
+  // transposes; l2s, dls: the step's L log2 e and delta.  issue(t) runs at
+  // the end of stage t (the caller's global loads for the next step, spread
+  // out so that they never arrive in one burst).
   //
   // The step is a fixed sequence of MFMA stages, two MFMAs each:
   //   stage t <  NS:  S and dP of query half qb = t / DK, feature chunk s = t % DK
@@ -106,10 +108,10 @@ struct DkdvWave {
   // of query half 0 runs under the S/dP MFMAs of half 1, and that of half 1
   // under the first dV/dK MFMAs (which only need half 0): with one wavefront
   // per SIMD this is the only way the matrix cores and the vector ALU overlap.
-  template <bool MASK>
+  template <bool MASK, class Issue>
   __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const uint16_t* qtt,
                                        const uint16_t* dott, const float* l2s, const float* dls,
-                                       int q0, int N, float scale_log2) {
+                                       int q0, int N, float scale_log2, Issue&& issue) {
     static_assert(C::NQB == 2, "two 32-query halves per step");
     constexpr int NS = C::NQB * C::DK;
     constexpr int NT = (C::BQ / 16) * C::NDB;
@@ -178,6 +180,7 @@ struct DkdvWave {
         if (t == C::DK + g * (C::DK - 1) / 4) load_stats(0, g);
         if (t == C::DK + 1 + g * (C::DK - 1) / 4) softmax_group(0, g);
       }
+      issue(t);
       sched_fence();
     }
     // dV^T += dO^T P, dK^T += Q^T dS (16 queries per MFMA); softmax of half 1
@@ -193,6 +196,7 @@ struct DkdvWave {
         if (u == g * (2 * C::NDB - 1) / 4) load_stats(1, g);
         if (u == 1 + g * (2 * C::NDB - 1) / 4) softmax_group(1, g);
       }
+      issue(t);
       sched_fence();
     }
   }
@@ -254,6 +258,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     qstage.load(Qh, i * C::BQ, N);
     dostage.load(dOh, i * C::BQ, N);
   };
+  // Inside a step the next step's staging loads go out one per MFMA stage
+  // (stages 0..3: Q tokens k = 0..3, stages 4..7: dO; every step has at least
+  // 16 stages): issued as one burst before the step, they held the wavefront
+  // up for longer than the matrix work of its first stages.
+  auto issue = [&](int t) {
+    if (t < 4) qstage.load_k(t);
+    else if (t < 8) dostage.load_k(t - 4);
+  };
   auto store_step = [&](int buf) {
     qstage.store(qt_lds[buf]);
     qstage.store_rows(q_lds[buf]);
@@ -300,16 +312,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     if (more) load_ld(ld_lds[BUF ^ 1], (i + 1) * C::BQ);
     // The stages are loaded and stored on every step (the last one re-stages
     // itself into the idle buffers), so their registers never live across steps.
-    load_stage(more ? i + 1 : i);
+    const int inext = more ? i + 1 : i;
+    qstage.begin(Qh, inext * C::BQ, N);
+    dostage.begin(dOh, inext * C::BQ, N);
     const int q0 = i * C::BQ;
     const bool need_mask = (CAUSAL && w.key_w + 31 > q0) || (w.key_w + 32 > N);
     const bool active = !CAUSAL || w.key_w <= q0 + C::BQ - 1;
     if (!need_mask) {
       w.template step<false>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
-                             ld_lds[BUF] + C::BQ, q0, N, scale_log2);
+                             ld_lds[BUF] + C::BQ, q0, N, scale_log2, issue);
     } else if (active) {
       w.template step<true>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
-                            ld_lds[BUF] + C::BQ, q0, N, scale_log2);
+                            ld_lds[BUF] + C::BQ, q0, N, scale_log2, issue);
+    } else {
+      load_stage(inext);
     }
     store_step(BUF ^ 1);
   };

@@ -164,31 +164,36 @@ struct TileDma {
   }
 };
 
-// Stager of one tile of TOK tokens through registers (StagePlan): load()
-// issues the global loads, store() (once the values are needed, typically
-// after the current tile's compute) writes the transposed tile, store_rows()
-// the same tokens as a RowTile.  Rows past n_rows are clamped to the last row.
+// Stager of one tile of TOK tokens through registers (StagePlan): begin()
+// and the four load_k() issue the global loads (all at once with load(), or
+// spread over the compute that hides them), store() (once the values are
+// needed, typically after the current tile's compute) writes the transposed
+// tile, store_rows() the same tokens as a RowTile.  Rows past n_rows are
+// clamped to the last row.
 template <int D, int TOK = 64>
 struct TrStage {
   using P = StagePlan<D, TOK>;
   u32x4 r[4];
   uint32_t off;
   bool act;
+  const char* src;
+  int lastk;
   __device__ __forceinline__ void init(int tid) {
     act = P::active(tid);
     off = P::lane_offset(tid);
   }
   // requires 0 <= tok0 < n_rows
+  __device__ __forceinline__ void begin(const uint16_t* head, int tok0, int n_rows) {
+    src = reinterpret_cast<const char*>(head + (size_t)tok0 * D);
+    lastk = P::last_k(off, tok0, n_rows);
+  }
+  __device__ __forceinline__ void load_k(int k) {
+    if (act) r[k] = ld_global16(src + (uint32_t)P::source_k(off, k, lastk));
+  }
   __device__ __forceinline__ void load(const uint16_t* head, int tok0, int n_rows) {
-    if (!act) return;
-    const char* base = reinterpret_cast<const char*>(head + (size_t)tok0 * D);
-    if (tok0 + TOK <= n_rows) {
+    begin(head, tok0, n_rows);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) r[k] = ld_global16(base + off + k * 2 * D);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) r[k] = ld_global16(base + P::source(off, k, tok0, n_rows));
-    }
+    for (int k = 0; k < 4; ++k) load_k(k);
   }
   __device__ __forceinline__ void store(uint16_t* tile) const {
     if (!act) return;

@@ -162,14 +162,20 @@ struct StagePlan {
   }
   static FA2_HD int grp(uint32_t off) { return (int)(off / (8u * D)); }          // 16 ch < 8 D
   static FA2_HD int chunk(uint32_t off) { return (int)(off % (8u * D)) / 16; }
-  // Byte offset, from the tile's first row tok0 (< n_rows), of the k-th token
-  // of the lane's group, clamped to the last row n_rows - 1.
+  // Last token k (0..3) of the lane's group that lies before row n_rows, for
+  // a tile starting at row tok0 < n_rows; 3 for every lane of a full tile,
+  // negative for a group entirely past the end.
+  static FA2_HD int last_k(uint32_t off, int tok0, int n_rows) {
+    const int m = n_rows - 1 - tok0 - 4 * grp(off);
+    return m < 3 ? m : 3;
+  }
+  // Byte offset, from the tile's first row, of the k-th token of the lane's
+  // group, clamped to the last row (lastk = last_k(...)); never negative.
+  static FA2_HD int64_t source_k(uint32_t off, int k, int lastk) {
+    return (int64_t)off + (int64_t)(k < lastk ? k : lastk) * 2 * D;
+  }
   static FA2_HD int64_t source(uint32_t off, int k, int tok0, int n_rows) {
-    if (tok0 + TOK <= n_rows) return (int64_t)off + k * 2 * D;
-    const int g4 = 4 * grp(off);
-    int row = g4 + k;
-    if (row > n_rows - 1 - tok0) row = n_rows - 1 - tok0;
-    return (int64_t)off + (int64_t)(row - g4) * 2 * D;
+    return source_k(off, k, last_k(off, tok0, n_rows));
   }
 };
 
