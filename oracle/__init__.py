@@ -20,6 +20,7 @@ Pins: every function here is checked against facts fixed by the mathematics
 
 from .bf16 import bf16_bits_to_float64
 from .attention import (
+    causal_offset,
     scores,
     softmax_rows,
     forward,
@@ -35,6 +36,7 @@ from .tiled import tiled_forward_head, tiled_backward_head
 
 __all__ = [
     "bf16_bits_to_float64",
+    "causal_offset",
     "scores",
     "softmax_rows",
     "forward",

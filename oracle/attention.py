@@ -9,12 +9,22 @@ materialising every token-by-token score.  So the oracle *is* standard
 attention, written out from its definition, with the full score matrix of one
 (batch, head) materialised at a time:
 
-    S = scale * Q K^T                       (N x N scores)
-    S_ij = -inf for j > i  when causal      (top-left aligned, square)
+    S = scale * Q K^T                       (Nq x Nk scores)
+    S_ij = -inf for j > i + (Nk - Nq)       when causal
     L_i  = log sum_j exp(S_ij)              (natural-log logsumexp of the
                                              scaled, masked scores)
     P    = exp(S - L)                       (row-stochastic)
     O    = P V
+
+Query and key lengths may differ.  The pages show the causal mask only for
+one sequence attending to itself (Nq = Nk: key j is kept for query i iff
+j <= i).  For Nq != Nk the reading taken here places the queries at the END
+of the key sequence (query i sits at key position i + Nk - Nq, the
+"bottom-right" alignment of a query block appended to a key/value cache),
+which reduces to the square rule for Nq = Nk.  With Nq > Nk the first
+Nq - Nk queries see no key: their softmax is over the empty set, so their L
+is -inf (the logsumexp of nothing), their row of P is zero, their output O is
+zero, and they contribute nothing to any gradient.
 
 The pages print no formulas for the logsumexp output L or for the gradient;
 they are the textbook definition of the row logsumexp and the analytic
@@ -27,8 +37,9 @@ derivative of the scalar f = sum(dO * O):
     dQ = scale * dS K
     dK = scale * dS^T Q
 
-All arrays are float64 ``[B, H, N, d]`` (or one head ``[N, d]``); L and D are
-``[B, H, N]``.  The "Sampled" helpers below evaluate the same definitions for
+All arrays are float64 ``[B, H, N, d]`` (or one head ``[N, d]``), with
+N = Nq for Q, O, dO, dQ and N = Nk for K, V, dK, dV; L and D are
+``[B, H, Nq]``.  The "Sampled" helpers below evaluate the same definitions for
 chosen query rows / key columns only, so that the definition can be checked at
 sequence lengths whose N x N matrix would not fit comfortably in host memory;
 they evaluate rows one chunk at a time and nothing else.
@@ -41,24 +52,33 @@ import numpy as np
 # building blocks (one head)
 # ---------------------------------------------------------------------------
 
-def scores(q, k, scale, causal, rows=None):
+def causal_offset(n_q, n_k):
+    """Key position of query 0 under the bottom-right reading: Nk - Nq."""
+    return int(n_k) - int(n_q)
+
+
+def scores(q, k, scale, causal, rows=None, n_q=None):
     """Scaled, masked scores S = scale * q k^T for one head.
 
-    q: [N, d] (or the selected rows), k: [N, d].  ``rows`` gives the absolute
-    query index of each row of ``q`` (needed for the causal mask when q is a
-    subset).  Causal masking keeps key j for query i iff j <= i (the mask
-    described for causal attention on the "FlashAttention-2: Faster Attention
-    with Better Parallelism and Work Partitioning" page, closing sentence on
-    the causal speed-up).
+    q: [Nq, d] (or the selected rows), k: [Nk, d].  ``rows`` gives the
+    absolute query index of each row of ``q`` (needed for the causal mask when
+    q is a subset) and ``n_q`` the total number of query rows (default: the
+    rows of q when ``rows`` is None, else Nk, i.e. a square problem).  Causal
+    masking keeps key j for query i iff j <= i + Nk - Nq; for Nq = Nk that is
+    j <= i, the mask described for causal attention on the "FlashAttention-2:
+    Faster Attention with Better Parallelism and Work Partitioning" page
+    (closing sentence on the causal speed-up).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     s = float(scale) * (q @ k.T)
     if causal:
-        n_q = q.shape[0]
-        qi = np.arange(n_q) if rows is None else np.asarray(rows)
-        kj = np.arange(k.shape[0])
-        s = np.where(kj[None, :] > qi[:, None], -np.inf, s)
+        n_k = k.shape[0]
+        if n_q is None:
+            n_q = q.shape[0] if rows is None else n_k
+        qi = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+        kj = np.arange(n_k)
+        s = np.where(kj[None, :] > qi[:, None] + causal_offset(n_q, n_k), -np.inf, s)
     return s
 
 
@@ -67,12 +87,16 @@ def softmax_rows(s):
 
     Returns (P, L) with L_i = log sum_j exp(S_ij) computed stably as
     m_i + log sum_j exp(S_ij - m_i), m_i = max_j S_ij, and P = exp(S - L).
-    Every row must hold at least one finite score (true for causal top-left
-    masking, where the diagonal is always kept).
+    A row with no finite score (a query that sees no key) has L_i = -inf and
+    a zero row of P.
     """
     m = np.max(s, axis=1)
-    lse = m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
-    p = np.exp(s - lse[:, None])
+    empty = np.isneginf(m)
+    m0 = np.where(empty, 0.0, m)
+    z = np.sum(np.exp(s - m0[:, None]), axis=1)
+    lse = np.where(empty, -np.inf, m0 + np.log(np.where(empty, 1.0, z)))
+    lse0 = np.where(empty, 0.0, lse)
+    p = np.where(empty[:, None], 0.0, np.exp(s - lse0[:, None]))
     return p, lse
 
 
@@ -106,7 +130,7 @@ def backward_head(q, k, v, do, scale, causal):
 
 
 def forward(q, k, v, scale, causal):
-    """O [B,H,N,d] and L [B,H,N] for every (batch, head), one head at a time."""
+    """O [B,H,Nq,d] and L [B,H,Nq] for every (batch, head), one head at a time."""
     q = np.asarray(q, dtype=np.float64)
     B, H, N, d = q.shape
     o = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
@@ -118,12 +142,13 @@ def forward(q, k, v, scale, causal):
 
 
 def backward(q, k, v, do, scale, causal):
-    """dQ, dK, dV [B,H,N,d] for every (batch, head), one head at a time."""
+    """dQ [B,H,Nq,d], dK and dV [B,H,Nk,d] for every (batch, head), one head at a time."""
     q = np.asarray(q, dtype=np.float64)
     B, H, N, d = q.shape
+    n_k = np.shape(k)[2]
     dq = np.empty_like(q)
-    dk = np.empty((B, H, N, d), dtype=np.float64)
-    dv = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
+    dk = np.empty((B, H, n_k, d), dtype=np.float64)
+    dv = np.empty((B, H, n_k, v.shape[-1]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = backward_head(
@@ -138,7 +163,8 @@ def backward(q, k, v, do, scale, causal):
 def forward_rows(q, k, v, scale, causal, rows):
     """O and L of the selected query rows of one head (same definition)."""
     rows = np.asarray(rows)
-    s = scores(np.asarray(q, dtype=np.float64)[rows], k, scale, causal, rows=rows)
+    q = np.asarray(q, dtype=np.float64)
+    s = scores(q[rows], k, scale, causal, rows=rows, n_q=q.shape[0])
     p, lse = softmax_rows(s)
     return p @ np.asarray(v, dtype=np.float64), lse
 
@@ -157,7 +183,7 @@ def row_stats(q, k, v, do, scale, causal, chunk=512):
     d_row = np.empty(n)
     for r0 in range(0, n, chunk):
         rows = np.arange(r0, min(n, r0 + chunk))
-        s = scores(q[rows], k, scale, causal, rows=rows)
+        s = scores(q[rows], k, scale, causal, rows=rows, n_q=n)
         p, lse[rows] = softmax_rows(s)
         dp = do[rows] @ v.T
         d_row[rows] = np.sum(p * dp, axis=1)
@@ -171,7 +197,7 @@ def backward_rows(q, k, v, do, scale, causal, rows):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    s = scores(q[rows], k, scale, causal, rows=rows)
+    s = scores(q[rows], k, scale, causal, rows=rows, n_q=q.shape[0])
     p, _ = softmax_rows(s)
     dp = do[rows] @ v.T
     d_row = np.sum(p * dp, axis=1)
@@ -194,10 +220,12 @@ def backward_cols(q, k, v, do, scale, causal, cols, stats=None):
         stats = row_stats(q, k, v, do, scale, causal)
     lse, d_row = stats
     n = q.shape[0]
-    s = float(scale) * (q @ k[cols].T)                       # [N, c]
+    s = float(scale) * (q @ k[cols].T)                       # [Nq, c]
     if causal:
-        s = np.where(cols[None, :] > np.arange(n)[:, None], -np.inf, s)
-    p = np.exp(s - lse[:, None])
+        off = causal_offset(n, k.shape[0])
+        s = np.where(cols[None, :] > np.arange(n)[:, None] + off, -np.inf, s)
+    # rows that see no key (L = -inf) have every score masked: P = 0 there
+    p = np.where(np.isneginf(s), 0.0, np.exp(s - np.where(np.isneginf(lse), 0.0, lse)[:, None]))
     dp = do @ v[cols].T
     ds = p * (dp - d_row[:, None])
     dv = p.T @ do

@@ -389,3 +389,131 @@ def test_closed_forms_catch_planted_forward_mistakes():
                      0.5 * rand((n, d), 122) @ k.T)
     p_bad, _ = A.softmax_rows(s_bad)
     assert not np.allclose((p_bad @ v)[0], v[0])
+
+
+# ---------------------------------------------------------------------------
+# query and key lengths that differ (causal mask aligned bottom-right)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nq,nk", [(4, 7), (6, 3), (1, 5)])
+def test_brute_force_tiny_rectangular(nq, nk):
+    """Pure-Python loops: query i sees key j iff j <= i + nk - nq (causal); empty rows give O = 0, L = -inf."""
+    d, scale = 3, 0.7
+    q, k, v = rand((nq, d), 200), rand((nk, d), 201), rand((nk, d), 202)
+    for causal in (False, True):
+        o, lse = A.forward_head(q, k, v, scale, causal)
+        assert o.shape == (nq, d) and lse.shape == (nq,)
+        for i in range(nq):
+            visible = [j for j in range(nk) if not (causal and j > i + nk - nq)]
+            if not visible:
+                assert lse[i] == -math.inf and np.all(o[i] == 0)
+                continue
+            sij = {j: scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in visible}
+            z = math.fsum(math.exp(x) for x in sij.values())
+            assert lse[i] == pytest.approx(math.log(z), abs=1e-13)
+            for t in range(d):
+                want = math.fsum(math.exp(sij[j]) / z * v[j][t] for j in visible)
+                assert o[i, t] == pytest.approx(want, abs=1e-13)
+
+
+def test_single_query_sees_every_key():
+    """Decoding one query against a key/value cache: causal equals non-causal."""
+    nk, d, scale = 19, 8, 0.35
+    q, do = rand((1, d), 210), rand((1, d), 211)
+    k, v = rand((nk, d), 212), rand((nk, d), 213)
+    o_c, l_c = A.forward_head(q, k, v, scale, True)
+    o_n, l_n = A.forward_head(q, k, v, scale, False)
+    np.testing.assert_array_equal(o_c, o_n)
+    np.testing.assert_array_equal(l_c, l_n)
+    for gc, gn in zip(A.backward_head(q, k, v, do, scale, True), A.backward_head(q, k, v, do, scale, False)):
+        np.testing.assert_array_equal(gc, gn)
+
+
+def test_bottom_right_rows_are_the_tail_of_the_square_problem():
+    """Nq < Nk: the queries are the last Nq positions of an Nk-token causal problem."""
+    nk, nq, d, scale = 23, 9, 6, 0.5
+    qf, k, v, dof = (rand((nk, d), 220 + i) for i in range(4))
+    q, do = qf[nk - nq:], dof[nk - nq:]
+    o_sq, l_sq = A.forward_head(qf, k, v, scale, True)
+    o, lse = A.forward_head(q, k, v, scale, True)
+    np.testing.assert_allclose(o, o_sq[nk - nq:], atol=1e-14)
+    np.testing.assert_allclose(lse, l_sq[nk - nq:], atol=1e-14)
+    # gradient of sum(dO * O) over the last nq rows only = square problem with dO = 0 on the first rows
+    do_sq = np.zeros_like(dof)
+    do_sq[nk - nq:] = do
+    dq_sq, dk_sq, dv_sq = A.backward_head(qf, k, v, do_sq, scale, True)
+    dq, dk, dv = A.backward_head(q, k, v, do, scale, True)
+    np.testing.assert_allclose(dq, dq_sq[nk - nq:], atol=1e-13)
+    np.testing.assert_allclose(dk, dk_sq, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_sq, atol=1e-13)
+
+
+def test_more_queries_than_keys():
+    """Nq > Nk: the first Nq - Nk queries see nothing; the rest form a square causal problem."""
+    nq, nk, d, scale = 15, 6, 5, 0.6
+    q, do = rand((nq, d), 230), rand((nq, d), 231)
+    k, v = rand((nk, d), 232), rand((nk, d), 233)
+    e = nq - nk
+    o, lse = A.forward_head(q, k, v, scale, True)
+    assert np.all(o[:e] == 0) and np.all(np.isneginf(lse[:e]))
+    o_sq, l_sq = A.forward_head(q[e:], k, v, scale, True)
+    np.testing.assert_allclose(o[e:], o_sq, atol=1e-14)
+    np.testing.assert_allclose(lse[e:], l_sq, atol=1e-14)
+    dq, dk, dv = A.backward_head(q, k, v, do, scale, True)
+    dq_sq, dk_sq, dv_sq = A.backward_head(q[e:], k, v, do[e:], scale, True)
+    assert np.all(dq[:e] == 0)
+    np.testing.assert_allclose(dq[e:], dq_sq, atol=1e-13)
+    np.testing.assert_allclose(dk, dk_sq, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_sq, atol=1e-13)
+    # the sampled helpers agree, empty rows included
+    rows = np.array([0, e - 1, e, nq - 1])
+    o_r, l_r = A.forward_rows(q, k, v, scale, True, rows)
+    np.testing.assert_allclose(o_r, o[rows], atol=1e-14)
+    np.testing.assert_array_equal(np.isneginf(l_r), np.isneginf(lse[rows]))
+    np.testing.assert_allclose(A.backward_rows(q, k, v, do, scale, True, rows), dq[rows], atol=1e-13)
+    cols = np.array([0, 3, nk - 1])
+    dk_c, dv_c = A.backward_cols(q, k, v, do, scale, True, cols)
+    np.testing.assert_allclose(dk_c, dk[cols], atol=1e-13)
+    np.testing.assert_allclose(dv_c, dv[cols], atol=1e-13)
+
+
+@pytest.mark.parametrize("nq,nk,causal", [(5, 7, False), (5, 7, True), (7, 4, True)])
+def test_rectangular_gradients_match_finite_differences(nq, nk, causal):
+    d, scale, h = 3, 0.8, 1e-6
+    q, do = rand((nq, d), 240), rand((nq, d), 241)
+    k, v = rand((nk, d), 242), rand((nk, d), 243)
+    grads = A.backward_head(q, k, v, do, scale, causal)
+
+    def f(qq, kk, vv):
+        return float(np.sum(do * A.forward_head(qq, kk, vv, scale, causal)[0]))
+
+    for idx, (arr, grad) in enumerate(zip((q, k, v), grads)):
+        fd = np.zeros_like(arr)
+        for pos in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[pos] += h
+            am[pos] -= h
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[idx], args_m[idx] = ap, am
+            fd[pos] = (f(*args_p) - f(*args_m)) / (2 * h)
+        assert np.linalg.norm(grad - fd) <= 1e-6 * max(np.linalg.norm(fd), 1e-12)
+
+
+@pytest.mark.parametrize("nq,nk", [(9, 21), (16, 16), (1, 8)])
+def test_matches_torch_lower_right_causal_bias(nq, nk):
+    """Library special case: PyTorch's float64 SDPA with its lower-right causal bias, plus autograd."""
+    torch = pytest.importorskip("torch")
+    bias = pytest.importorskip("torch.nn.attention.bias")
+    B, H, d, scale = 2, 2, 8, 0.3
+    q, do = rand((B, H, nq, d), 250), rand((B, H, nq, d), 251)
+    k, v = rand((B, H, nk, d), 252), rand((B, H, nk, d), 253)
+    o, _ = A.forward(q, k, v, scale, True)
+    dq, dk, dv = A.backward(q, k, v, do, scale, True)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=bias.causal_lower_right(nq, nk), scale=scale)
+    to.backward(torch.tensor(do, dtype=torch.float64))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
