@@ -41,6 +41,12 @@ int check_sizes(int B, int H, int N, int d) {
   return FA2_OK;
 }
 
+// Query and key lengths: both must pass the checks above.
+int check_sizes2(int B, int H, int Nq, int Nk, int d) {
+  const int st = check_sizes(B, H, Nq, d);
+  return st != FA2_OK ? st : check_sizes(B, H, Nk, d);
+}
+
 int check_scale_causal(float scale, int causal) {
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA2_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
@@ -66,18 +72,25 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-            int d, float scale, int causal, void* stream) {
-  int st = check_sizes(B, H, N, d);
+int fa2_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  int st = check_sizes2(B, H, Nq, Nk, d);
   if (st != FA2_OK) return st;
   if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse))
     return FA2_ERR_INVALID_ARG;
-  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
-  const Span ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
-  const Span outs[2] = {span(o, tb), span(lse, lb)};
+  const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+  const size_t lb = (size_t)B * H * Nq * 4;
+  const Span ins[3] = {span(q, qb), span(k, kb), span(v, kb)};
+  const Span outs[2] = {span(o, qb), span(lse, lb)};
   if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
-  return hip_status(fa2::launch_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, as_stream(stream)));
+  return hip_status(
+      fa2::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, as_stream(stream)));
+}
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+            int d, float scale, int causal, void* stream) {
+  return fa2_fwd_qk(q, k, v, o, lse, B, H, N, N, d, scale, causal, stream);
 }
 
 int fa2_bwd_rows_padded(int N) { return N < 1 ? 0 : fa2::bwd_rows_padded(N); }
@@ -103,75 +116,101 @@ int fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, float*
                                                as_stream(stream)));
 }
 
-// Shared checks of the two tile phases: 4 bf16 inputs, the two padded row
-// arrays, and `n_out` bf16 outputs.
+// Shared checks of the two tile phases: 4 bf16 inputs (q, dout: Nq rows; k,
+// v: Nk rows), the two padded row arrays (Nq rows), and one or two bf16
+// outputs of out_rows rows.
 static int check_tile_phase(const void* q, const void* k, const void* v, const void* dout,
                             const float* lse_log2, const float* delta, const void* out0,
-                            const void* out1, int B, int H, int N, int d, float scale,
-                            int causal) {
-  int st = check_sizes(B, H, N, d);
+                            const void* out1, int out_rows, int B, int H, int Nq, int Nk, int d,
+                            float scale, int causal) {
+  int st = check_sizes2(B, H, Nq, Nk, d);
   if (st != FA2_OK) return st;
   if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(dout) || !ptr_ok(lse_log2) ||
       !ptr_ok(delta) || !ptr_ok(out0) || (out1 != nullptr && !ptr_ok(out1)))
     return FA2_ERR_INVALID_ARG;
-  const size_t tb = (size_t)B * H * N * d * 2;
-  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(N);
-  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(dout, tb),
+  const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+  const size_t ob = (size_t)B * H * out_rows * d * 2;
+  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(Nq);
+  const Span ins[6] = {span(q, qb), span(k, kb), span(v, kb), span(dout, qb),
                        span(lse_log2, prow * 4), span(delta, prow * 4)};
-  const Span outs[2] = {span(out0, tb), span(out1, out1 ? tb : 0)};
+  const Span outs[2] = {span(out0, ob), span(out1, out1 ? ob : 0)};
   if (!disjoint(outs, out1 ? 2 : 1, ins, 6)) return FA2_ERR_INVALID_ARG;
   return FA2_OK;
+}
+
+int fa2_bwd_dkdv_qk(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse_log2, const float* delta, void* dk, void* dv, int B, int H,
+                    int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  if (dv == nullptr) return FA2_ERR_INVALID_ARG;
+  const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dk, dv, Nk, B, H, Nq, Nk, d,
+                                  scale, causal);
+  if (st != FA2_OK) return st;
+  return hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, Nq, Nk, d,
+                                         scale, causal, as_stream(stream)));
 }
 
 int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                  const float* lse_log2, const float* delta, void* dk, void* dv, int B, int H,
                  int N, int d, float scale, int causal, void* stream) {
-  if (dv == nullptr) return FA2_ERR_INVALID_ARG;
-  const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d, scale, causal);
+  return fa2_bwd_dkdv_qk(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, N, d, scale, causal,
+                         stream);
+}
+
+int fa2_bwd_dq_qk(const void* q, const void* k, const void* v, const void* dout,
+                  const float* lse_log2, const float* delta, void* dq, int B, int H, int Nq,
+                  int Nk, int d, float scale, int causal, void* stream) {
+  const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dq, nullptr, Nq, B, H, Nq, Nk,
+                                  d, scale, causal);
   if (st != FA2_OK) return st;
-  return hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d, scale,
-                                         causal, as_stream(stream)));
+  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, Nq, Nk, d, scale,
+                                       causal, as_stream(stream)));
 }
 
 int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                const float* lse_log2, const float* delta, void* dq, int B, int H, int N, int d,
                float scale, int causal, void* stream) {
-  const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dq, nullptr, B, H, N, d, scale,
-                                  causal);
-  if (st != FA2_OK) return st;
-  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, N, d, scale,
-                                       causal, as_stream(stream)));
+  return fa2_bwd_dq_qk(q, k, v, dout, lse_log2, delta, dq, B, H, N, N, d, scale, causal, stream);
 }
 
-int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-            float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_sizes(B, H, N, d);
+int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+               int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int st = check_sizes2(B, H, Nq, Nk, d);
   if (st != FA2_OK) return st;
   if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dout) ||
       !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv) || !ptr_ok(workspace))
     return FA2_ERR_INVALID_ARG;
-  const size_t need = fa2_bwd_workspace_bytes(B, H, N, d);
+  const size_t need = fa2_bwd_workspace_bytes(B, H, Nq, d);
   if (workspace_bytes < need) return FA2_ERR_WORKSPACE;
-  const size_t tb = (size_t)B * H * N * d * 2, rows = (size_t)B * H * N;
-  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb),
-                       span(o, tb), span(lse, rows * 4), span(dout, tb)};
-  const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
+  const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+  const size_t rows = (size_t)B * H * Nq;
+  const Span ins[6] = {span(q, qb), span(k, kb), span(v, kb),
+                       span(o, qb), span(lse, rows * 4), span(dout, qb)};
+  const Span outs[4] = {span(dq, qb), span(dk, kb), span(dv, kb), span(workspace, need)};
   if (!disjoint(outs, 4, ins, 6)) return FA2_ERR_INVALID_ARG;
 
-  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(N);
+  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(Nq);
   float* delta = static_cast<float*>(workspace);
   float* lse_log2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(prow * 4));
   hipStream_t s = as_stream(stream);
-  if ((st = hip_status(fa2::launch_bwd_preprocess(o, dout, lse, delta, lse_log2, B, H, N, d, s))) != FA2_OK)
+  if ((st = hip_status(fa2::launch_bwd_preprocess(o, dout, lse, delta, lse_log2, B, H, Nq, d, s))) !=
+      FA2_OK)
     return st;
-  if ((st = hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d,
-                                            scale, causal, s))) != FA2_OK)
+  if ((st = hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, Nq, Nk,
+                                            d, scale, causal, s))) != FA2_OK)
     return st;
-  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, N, d, scale,
+  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, Nq, Nk, d, scale,
                                        causal, s));
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+            float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa2_bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, N, d, scale, causal, workspace,
+                    workspace_bytes, stream);
 }
 
 const char* fa2_strerror(int status) {

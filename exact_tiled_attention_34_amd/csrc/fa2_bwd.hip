@@ -1,9 +1,10 @@
 // Backward pass of exact tiled attention on gfx950.
 //
 // Three kernels, enqueued in order by fa2_bwd:
-//   preprocess  for every row: delta_i = sum_k dO_ik O_ik and L_i log2(e), written
-//               to row-padded fp32 arrays (rows past N: delta 0, L +inf, which makes
-//               every P of such a row exactly 0); HBM-bound, 16 lanes per row.
+//   preprocess  for every query row: delta_i = sum_k dO_ik O_ik and L_i log2(e),
+//               written to row-padded fp32 arrays (rows past Nq, and rows that saw
+//               no key (L = -inf): delta 0 or its value, L +inf, which makes every
+//               P of such a row exactly 0); HBM-bound, 16 lanes per row.
 //   dkdv        one workgroup per (128-key column block, batch*head); each of its 4
 //               wavefronts owns 32 keys and keeps K and V (as MFMA operands) and its
 //               dK, dV accumulators in registers while walking the 64-query row
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (prow < rows_pad && sub == 0) {
     Delta[prow] = valid ? acc : 0.f;
-    L2[prow] = valid ? LSE[row] * kLog2e : INFINITY;
+    const float l = valid ? LSE[row] : -INFINITY;
+    L2[prow] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -97,7 +99,8 @@ struct DkdvWave {
   LaneOffsets<D> off;
 
   // One 64-query step.  qt, dot: row-major Q and dO tiles; qtt, dott: their
-  // transposes; l2s, dls: the step's L log2 e and delta.  issue(t) runs at
+  // transposes; l2s, dls: the step's L log2 e and delta; kq0: the last key
+  // the step's first query may see (causal); Nk: keys.  issue(t) runs at
   // the end of stage t (the caller's global loads for the next step, spread
   // out so that they never arrive in one burst).
   //
@@ -111,7 +114,7 @@ struct DkdvWave {
   template <bool MASK, class Issue>
   __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const uint16_t* qtt,
                                        const uint16_t* dott, const float* l2s, const float* dls,
-                                       int q0, int N, float scale_log2, Issue&& issue) {
+                                       int kq0, int Nk, float scale_log2, Issue&& issue) {
     static_assert(C::NQB == 2, "two 32-query halves per step");
     constexpr int NS = C::NQB * C::DK;
     constexpr int NT = (C::BQ / 16) * C::NDB;
@@ -158,7 +161,7 @@ struct DkdvWave {
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * g + r;
         float x = exp2_fast(__builtin_fmaf(sacc[qb][t], scale_log2, -lv[qb][g][r]));
-        if (MASK && (key_lane >= N || (CAUSAL && key_lane > q0 + qb * 32 + 8 * g + 4 * lh + r))) x = 0.f;
+        if (MASK && (key_lane >= Nk || (CAUSAL && key_lane > kq0 + qb * 32 + 8 * g + 4 * lh + r))) x = 0.f;
         p[r] = x;
         ds[r] = x * (pacc[qb][t] - dv[qb][g][r]);
       }
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    int BH, int N, int Npad, float scale, float scale_log2) {
+    int BH, int Nq, int Nk, int Npad, float scale, float scale_log2) {
   using C = DkdvCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::TILE];
@@ -228,15 +231,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // most query blocks under a causal mask, so it is dispatched first.
   const int bh = blockIdx.x % BH;
   const int kblk = blockIdx.x / BH;
-  const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + head_off;
-  const uint16_t* dOh = dO + head_off;
+  const size_t q_head = (size_t)bh * Nq * D;   // Q, dO
+  const size_t k_head = (size_t)bh * Nk * D;   // K, V, dK, dV
+  const uint16_t* Qh = Q + q_head;
+  const uint16_t* dOh = dO + q_head;
   const float* L2h = L2 + (size_t)bh * Npad;
   const float* Dh = Delta + (size_t)bh * Npad;
+  // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
+  const int koff = Nk - Nq;
 
   const int key_wg = kblk * C::BKC;
-  const int n_qblk = (N + C::BQ - 1) / C::BQ;
-  const int i_begin = CAUSAL ? key_wg / C::BQ : 0;
+  const int n_qblk = (Nq + C::BQ - 1) / C::BQ;
+  // causal: the first query block holding a query that sees key key_wg (the
+  // last query sees every key, so i_begin < n_qblk)
+  const int i_begin = CAUSAL ? max(0, key_wg - koff) / C::BQ : 0;
 
   // L log2 e and delta of one query block: 2 x 64 floats, 16 bytes per lane.
   // (lanes 16..31 land 256 bytes after lanes 0..15, i.e. at the delta half)
@@ -255,8 +263,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   qstage.init(tid);
   dostage.init(tid);
   auto load_stage = [&](int i) {
-    qstage.load(Qh, i * C::BQ, N);
-    dostage.load(dOh, i * C::BQ, N);
+    qstage.load(Qh, i * C::BQ, Nq);
+    dostage.load(dOh, i * C::BQ, Nq);
   };
   // Inside a step the next step's staging loads go out one per MFMA stage
   // (stages 0..3: Q tokens k = 0..3, stages 4..7: dO; every step has at least
@@ -272,9 +280,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dostage.store(dot_lds[buf]);
     dostage.store_rows(do_lds[buf]);
   };
-  load_ld(ld_lds[0], i_begin * C::BQ);
-  load_stage(i_begin);
-  store_step(0);
+  if (i_begin < n_qblk) {
+    load_ld(ld_lds[0], i_begin * C::BQ);
+    load_stage(i_begin);
+    store_step(0);
+  }
 
   DkdvWave<D, CAUSAL> w;
   w.lane = tid & 63;
@@ -287,9 +297,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
     u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-    if (w.key_lane < N) {
-      zk = ld_global16(K + head_off + (size_t)w.key_lane * D + s * 16 + 8 * w.lh);
-      zv = ld_global16(V + head_off + (size_t)w.key_lane * D + s * 16 + 8 * w.lh);
+    if (w.key_lane < Nk) {
+      zk = ld_global16(K + k_head + (size_t)w.key_lane * D + s * 16 + 8 * w.lh);
+      zv = ld_global16(V + k_head + (size_t)w.key_lane * D + s * 16 + 8 * w.lh);
     }
     w.kf[s] = as_bf16x8(zk);
     w.vf[s] = as_bf16x8(zv);
@@ -313,17 +323,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // The stages are loaded and stored on every step (the last one re-stages
     // itself into the idle buffers), so their registers never live across steps.
     const int inext = more ? i + 1 : i;
-    qstage.begin(Qh, inext * C::BQ, N);
-    dostage.begin(dOh, inext * C::BQ, N);
-    const int q0 = i * C::BQ;
-    const bool need_mask = (CAUSAL && w.key_w + 31 > q0) || (w.key_w + 32 > N);
-    const bool active = !CAUSAL || w.key_w <= q0 + C::BQ - 1;
+    qstage.begin(Qh, inext * C::BQ, Nq);
+    dostage.begin(dOh, inext * C::BQ, Nq);
+    // kq0: the key position of the step's first query (its last visible key)
+    const int kq0 = i * C::BQ + koff;
+    const bool need_mask = (CAUSAL && w.key_w + 31 > kq0) || (w.key_w + 32 > Nk);
+    const bool active = !CAUSAL || w.key_w <= kq0 + C::BQ - 1;
     if (!need_mask) {
       w.template step<false>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
-                             ld_lds[BUF] + C::BQ, q0, N, scale_log2, issue);
+                             ld_lds[BUF] + C::BQ, kq0, Nk, scale_log2, issue);
     } else if (active) {
       w.template step<true>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
-                            ld_lds[BUF] + C::BQ, q0, N, scale_log2, issue);
+                            ld_lds[BUF] + C::BQ, kq0, Nk, scale_log2, issue);
     } else {
       load_stage(inext);
     }
@@ -335,9 +346,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 
   // Epilogue: dK = scale * dS^T Q, dV = P^T dO (bf16).
-  if (w.key_lane < N) {
-    uint16_t* dkrow = dK + head_off + (size_t)w.key_lane * D;
-    uint16_t* dvrow = dV + head_off + (size_t)w.key_lane * D;
+  if (w.key_lane < Nk) {
+    uint16_t* dkrow = dK + k_head + (size_t)w.key_lane * D;
+    uint16_t* dvrow = dV + k_head + (size_t)w.key_lane * D;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -378,12 +389,13 @@ struct DqWave {
   f32x16 dqacc[C::NDB];
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
+  int key_last;   // causal: last key this lane's query may see (q_lane + Nk - Nq)
   LaneOffsets<D> off;
 
   // kt, vt: row-major K and V tiles; ktt: transposed K tile.
   template <bool MASK>
   __device__ __forceinline__ void tile(const uint16_t* kt, const uint16_t* vt, const uint16_t* ktt,
-                                       int key0, int N, float scale_log2) {
+                                       int key0, int Nk, float scale_log2) {
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -408,7 +420,7 @@ struct DqWave {
         float p = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -l2));
         if (MASK) {
           const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= N || (CAUSAL && key > q_lane)) p = 0.f;
+          if (key >= Nk || (CAUSAL && key > key_last)) p = 0.f;
         }
         pacc[kb][i] = p * (pacc[kb][i] - dl);
       }
@@ -433,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
-    int BH, int N, int Npad, float scale, float scale_log2) {
+    int BH, int Nq, int Nk, int Npad, float scale, float scale_log2) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE];
@@ -443,14 +455,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int wave = tid >> 6;
   tr_zero_pad<D>(kt_lds[0], tid, C::THREADS);
   tr_zero_pad<D>(kt_lds[1], tid, C::THREADS);
-  const int nrb = (N + C::BR - 1) / C::BR;
+  const int nrb = (Nq + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;
   if (CAUSAL) rb = nrb - 1 - rb;
 
-  const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Kh = K + head_off;
-  const uint16_t* Vh = V + head_off;
+  const size_t q_head = (size_t)bh * Nq * D;   // Q, dO, dQ
+  const size_t k_head = (size_t)bh * Nk * D;   // K, V
+  const uint16_t* Kh = K + k_head;
+  const uint16_t* Vh = V + k_head;
+  // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
+  const int koff = Nk - Nq;
 
   DqWave<D, CAUSAL> w;
   w.lane = tid & 63;
@@ -458,12 +473,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   w.lh = w.lane >> 5;
   w.q_wave = rb * C::BR + wave * 32;
   w.q_lane = w.q_wave + w.lr;
+  w.key_last = w.q_lane + koff;
   w.off.init(w.lane);
 
   const int q_first = rb * C::BR;
-  int n_tiles = (N + C::BC - 1) / C::BC;
-  if (CAUSAL) n_tiles = min(n_tiles, (q_first + C::BR - 1) / C::BC + 1);
-  const int n_full = min(n_tiles, (CAUSAL ? min(q_first + 1, N) : N) / C::BC);
+  int n_tiles = (Nk + C::BC - 1) / C::BC;
+  if (CAUSAL) {
+    const int last_key = q_first + C::BR - 1 + koff;   // last key any row of the block sees
+    n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::BC + 1);
+  }
+  const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
   // K goes through registers (written row-major and transposed), V is copied
   // to LDS directly.
@@ -471,17 +490,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   TileDma<D, C::BC, C::THREADS> vdma;
   kstage.init(tid);
   vdma.init(tid);
-  vdma.issue(v_lds[0], Vh, 0, N);
-  kstage.load(Kh, 0, N);
+  if (n_tiles > 0) {
+    vdma.issue(v_lds[0], Vh, 0, Nk);
+    kstage.load(Kh, 0, Nk);
+  }
 
   // Q and dO fragments stay in registers (B operands of K Q^T and V dO^T);
-  // rows past N read as zero and have L = +inf in the padded L array.
+  // rows past Nq read as zero and have L = +inf in the padded L array.
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
     u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
-    if (w.q_lane < N) {
-      zq = ld_global16(Q + head_off + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
-      zd = ld_global16(dO + head_off + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
+    if (w.q_lane < Nq) {
+      zq = ld_global16(Q + q_head + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
+      zd = ld_global16(dO + q_head + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
     }
     w.qf[s] = as_bf16x8(zq);
     w.dof[s] = as_bf16x8(zd);
@@ -498,29 +519,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     wait_vmem();
     __syncthreads();
     const bool more = j + 1 < n_tiles;
-    if (more) vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, N);
+    if (more) vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, Nk);
     // The K stage is loaded and stored on every tile (the last one re-stages
     // itself into the idle buffers), so its registers never live across tiles.
-    kstage.load(Kh, (more ? j + 1 : j) * C::BC, N);
+    kstage.load(Kh, (more ? j + 1 : j) * C::BC, Nk);
     const int key0 = j * C::BC;
     if (j < n_full) {
-      w.template tile<false>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
-    } else if (!CAUSAL || key0 <= w.q_wave + 31) {
-      w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, N, scale_log2);
+      w.template tile<false>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
+    } else if (!CAUSAL || key0 <= w.q_wave + 31 + koff) {
+      w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
     }
     kstage.store(kt_lds[BUF ^ 1]);
     kstage.store_rows(k_lds[BUF ^ 1]);
   };
-  kstage.store(kt_lds[0]);
-  kstage.store_rows(k_lds[0]);
+  if (n_tiles > 0) {
+    kstage.store(kt_lds[0]);
+    kstage.store_rows(k_lds[0]);
+  }
   for (int j = 0; j < n_tiles; j += 2) {
     iteration(std::integral_constant<int, 0>{}, j);
     if (j + 1 < n_tiles) iteration(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // Epilogue: dQ = scale * dS K (bf16).
-  if (w.q_lane < N) {
-    uint16_t* row = dQ + head_off + (size_t)w.q_lane * D;
+  if (w.q_lane < Nq) {
+    uint16_t* row = dQ + q_head + (size_t)w.q_lane * D;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -548,28 +571,28 @@ hipError_t launch_pre_t(const void* o, const void* dout, const float* lse, float
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout,
-                         const float* l2, const float* delta, void* dk, void* dv, int BH, int N,
-                         float scale, hipStream_t stream) {
+                         const float* l2, const float* delta, void* dk, void* dv, int BH, int Nq,
+                         int Nk, float scale, hipStream_t stream) {
   using C = DkdvCfg<D>;
-  const int nkb = (N + C::BKC - 1) / C::BKC;
+  const int nkb = (Nk + C::BKC - 1) / C::BKC;
   bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(nkb * BH)), C::THREADS, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), l2, delta,
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, N, bwd_rows_padded(N), scale,
-      scale * kLog2e);
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, Nq, Nk, bwd_rows_padded(Nq),
+      scale, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout,
-                       const float* l2, const float* delta, void* dq, int BH, int N, float scale,
-                       hipStream_t stream) {
+                       const float* l2, const float* delta, void* dq, int BH, int Nq, int Nk,
+                       float scale, hipStream_t stream) {
   using C = DqCfg<D>;
-  const int nrb = (N + C::BR - 1) / C::BR;
+  const int nrb = (Nq + C::BR - 1) / C::BR;
   bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), l2, delta,
-      static_cast<uint16_t*>(dq), BH, N, bwd_rows_padded(N), scale, scale * kLog2e);
+      static_cast<uint16_t*>(dq), BH, Nq, Nk, bwd_rows_padded(Nq), scale, scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -595,14 +618,14 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                            const float* l2, const float* delta, void* dk, void* dv, int B, int H,
-                           int N, int d, float scale, int causal, hipStream_t stream) {
-  FA2_DISPATCH(launch_dkdv_t, q, k, v, dout, l2, delta, dk, dv, B * H, N, scale, stream)
+                           int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  FA2_DISPATCH(launch_dkdv_t, q, k, v, dout, l2, delta, dk, dv, B * H, Nq, Nk, scale, stream)
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                         const float* l2, const float* delta, void* dq, int B, int H, int N,
-                         int d, float scale, int causal, hipStream_t stream) {
-  FA2_DISPATCH(launch_dq_t, q, k, v, dout, l2, delta, dq, B * H, N, scale, stream)
+                         const float* l2, const float* delta, void* dq, int B, int H, int Nq,
+                         int Nk, int d, float scale, int causal, hipStream_t stream) {
+  FA2_DISPATCH(launch_dq_t, q, k, v, dout, l2, delta, dq, B * H, Nq, Nk, scale, stream)
 }
 
 #undef FA2_DISPATCH

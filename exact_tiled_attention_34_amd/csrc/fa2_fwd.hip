@@ -63,6 +63,8 @@ struct FwdWave {
   f32x16 sc[1][C::KB];  // scores of the current tile
   float m_run, l_run;
   int lane, lr, lh, q_wave, q_lane;
+  int key_last;        // causal: last key this lane's query may see (q_lane + Nk - Nq)
+  int key_last_wave;   // the same for the wavefront's last query row
   LaneOffsets<D, FwdCfg<D>::BC> off;
 
   // S^T (64 keys x this wave's 32 queries) of the K tile at kt.
@@ -86,14 +88,14 @@ struct FwdWave {
   // the end of the sequence or above the diagonal for some of this wave's rows.
   template <bool MASK>
   __device__ __forceinline__ float softmax(f32x16 (&sacc)[C::KB], uint32_t (&pw)[C::KB][8], bool& any,
-                                           int key0, int N, float scale_log2) {
+                                           int key0, int Nk, float scale_log2) {
     if (MASK) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= N || (CAUSAL && key > q_lane)) sacc[kb][i] = -INFINITY;
+          if (key >= Nk || (CAUSAL && key > key_last)) sacc[kb][i] = -INFINITY;
         }
     }
     float mx = fmaxf(sacc[0][0], sacc[0][1]);
@@ -102,10 +104,14 @@ struct FwdWave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = fmaxf(mx, swap_halves(mx));
-    const bool grow = mx > m_run;          // the first tile always grows (from -inf)
+    const bool grow = mx > m_run;
+    // A masked tile can hide every key from a row (a query that precedes all
+    // visible keys when Nq > Nk): its maximum stays -inf, and 0 stands in
+    // for it so that P = 0 and alpha = 0 instead of NaN.
     const float m_new = grow ? mx : m_run;
-    const float alpha = exp2_fast((m_run - m_new) * scale_log2);
-    const float mc = m_new * scale_log2;
+    const float m_use = (MASK && m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2_fast((m_run - m_use) * scale_log2);
+    const float mc = m_use * scale_log2;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -151,22 +157,22 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCf
                                          const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
                                          uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                          uint16_t (*v_lds)[FwdCfg<D>::VTILE], const uint16_t* Kh,
-                                         const uint16_t* Vh, int j, int n_tiles, int N, int tid,
+                                         const uint16_t* Vh, int j, int n_tiles, int Nk, int tid,
                                          float scale_log2) {
   using C = FwdCfg<D>;
   wait_vmem();
   __syncthreads();   // tile j is in LDS; every wave is done with the other buffer
   const bool more = j + 1 < n_tiles;
-  if (more) kdma.issue(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, N);
+  if (more) kdma.issue(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, Nk);
   // The V stage is loaded and stored on every tile (the last one re-stages
   // itself into the idle buffer), so its registers never live across tiles.
-  vstage.load(Vh, (more ? j + 1 : j) * C::BC, N);
+  vstage.load(Vh, (more ? j + 1 : j) * C::BC, Nk);
   // a wavefront whose rows all precede the tile's first key has nothing to do
-  if (!MASK || !CAUSAL || j * C::BC <= w.q_wave + 31) {
+  if (!MASK || !CAUSAL || j * C::BC <= w.key_last_wave) {
     w.scores(k_lds[PAR], w.sc[0]);
     uint32_t pw[C::KB][8];
     bool any;
-    const float alpha = w.template softmax<MASK>(w.sc[0], pw, any, j * C::BC, N, scale_log2);
+    const float alpha = w.template softmax<MASK>(w.sc[0], pw, any, j * C::BC, Nk, scale_log2);
     if (any) w.rescale(alpha);
     w.pv(v_lds[PAR], pw);
   }
@@ -179,19 +185,19 @@ __device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL>& w, TrStage<D, F
                                              uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                              uint16_t (*v_lds)[FwdCfg<D>::VTILE],
                                              const uint16_t* Kh, const uint16_t* Vh, int j,
-                                             int n_tiles, int n_full, int N, int tid,
+                                             int n_tiles, int n_full, int Nk, int tid,
                                              float scale_log2) {
   if (j < n_full)
-    fwd_tile<D, CAUSAL, PAR, false>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
+    fwd_tile<D, CAUSAL, PAR, false>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
   else
-    fwd_tile<D, CAUSAL, PAR, true>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, N, tid, scale_log2);
+    fwd_tile<D, CAUSAL, PAR, true>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int BH, int N, float scale_log2) {
+    int BH, int Nq, int Nk, float scale_log2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::VTILE];
@@ -205,14 +211,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   // different heads, so with the round-robin dispatch over the 8 XCDs all row
   // blocks of one head land on the same XCD (and its L2).  Causal: the longest
   // row blocks (most tiles) are dispatched first.
-  const int nrb = (N + C::BR - 1) / C::BR;
+  const int nrb = (Nq + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;
   if (CAUSAL) rb = nrb - 1 - rb;
 
-  const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* Kh = K + head_off;
-  const uint16_t* Vh = V + head_off;
+  const size_t q_head = (size_t)bh * Nq * D;   // Q, O
+  const size_t k_head = (size_t)bh * Nk * D;   // K, V
+  const uint16_t* Kh = K + k_head;
+  const uint16_t* Vh = V + k_head;
+  // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
+  const int koff = Nk - Nq;
 
   FwdWave<D, CAUSAL> w;
   w.lane = tid & 63;
@@ -220,6 +229,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   w.lh = w.lane >> 5;
   w.q_wave = rb * C::BR + wave * 32;
   w.q_lane = w.q_wave + w.lr;
+  w.key_last = w.q_lane + koff;
+  w.key_last_wave = w.q_wave + 31 + koff;
   w.m_run = -INFINITY;
   w.l_run = 0.f;
   w.off.init(w.lane);
@@ -229,40 +240,46 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
     for (int i = 0; i < 16; ++i) w.oacc[mb][i] = 0.f;
 
   const int q_first = rb * C::BR;              // first query row of the workgroup
-  int n_tiles = (N + C::BC - 1) / C::BC;
-  if (CAUSAL) n_tiles = min(n_tiles, (q_first + C::BR - 1) / C::BC + 1);
+  int n_tiles = (Nk + C::BC - 1) / C::BC;
+  if (CAUSAL) {
+    const int last_key = q_first + C::BR - 1 + koff;   // last key any row of the block sees
+    n_tiles = last_key < 0 ? 0 : min(n_tiles, last_key / C::BC + 1);
+  }
   // tiles [0, n_full) hold only keys that every row of the block may see
-  const int n_full = min(n_tiles, (CAUSAL ? min(q_first + 1, N) : N) / C::BC);
+  const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
   // Tile 0 into LDS (K directly, V transposed through registers).
   TrStage<D, C::BC> vstage;
   TileDma<D, C::BC, C::THREADS> kdma;
   vstage.init(tid);
   kdma.init(tid);
-  kdma.issue(k_lds[0], Kh, 0, N);
-  vstage.load(Vh, 0, N);
+  if (n_tiles > 0) {
+    kdma.issue(k_lds[0], Kh, 0, Nk);
+    vstage.load(Vh, 0, Nk);
+  }
   // Q fragments stay in registers for the whole pass (B operand of S^T = K Q^T).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
     u32x4 z = {0u, 0u, 0u, 0u};
-    if (w.q_lane < N) z = ld_global16(Q + head_off + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
+    if (w.q_lane < Nq) z = ld_global16(Q + q_head + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
     w.qf[s] = as_bf16x8(z);
   }
-  vstage.store(v_lds[0]);
+  if (n_tiles > 0) vstage.store(v_lds[0]);
 
   // Tile j uses buffer j % 2; unrolled by two so the buffer is an immediate.
   for (int j = 0; j < n_tiles; j += 2) {
-    fwd_tile_any<D, CAUSAL, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, N, tid, scale_log2);
+    fwd_tile_any<D, CAUSAL, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, Nk, tid, scale_log2);
     if (j + 1 < n_tiles)
-      fwd_tile_any<D, CAUSAL, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, N, tid,
+      fwd_tile_any<D, CAUSAL, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, Nk, tid,
                                  scale_log2);
   }
 
-  // Epilogue: one division by the row sum, then O (bf16) and L (fp32, natural log).
+  // Epilogue: one division by the row sum, then O (bf16) and L (fp32, natural
+  // log).  A row that saw no key (l = 0) gets O = 0 and L = -inf.
   const float l_tot = w.l_run + swap_halves(w.l_run);
-  if (w.q_lane < N) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = O + head_off + (size_t)w.q_lane * D;
+  if (w.q_lane < Nq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = O + q_head + (size_t)w.q_lane * D;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -275,33 +292,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
         }
       }
     if (w.lh == 0)
-      LSE[(size_t)bh * N + w.q_lane] = (w.m_run * scale_log2 + log2_fast(l_tot)) * kLn2;
+      LSE[(size_t)bh * Nq + w.q_lane] =
+          l_tot > 0.f ? (w.m_run * scale_log2 + log2_fast(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int N, float scale, hipStream_t stream) {
+                        int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int BH = B * H;
-  const int nrb = (N + C::BR - 1) / C::BR;
+  const int nrb = (Nq + C::BR - 1) / C::BR;
   fwd_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, N, scale * kLog2e);
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Nq, Nk, scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      hipStream_t stream) {
   switch (d) {
-    case 64:  return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                            : launch_fwd_t<64, false>(q, k, v, o, lse, B, H, N, scale, stream);
-    case 80:  return causal ? launch_fwd_t<80, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                            : launch_fwd_t<80, false>(q, k, v, o, lse, B, H, N, scale, stream);
-    case 128: return causal ? launch_fwd_t<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                            : launch_fwd_t<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+    case 64:  return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
+                            : launch_fwd_t<64, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
+    case 80:  return causal ? launch_fwd_t<80, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
+                            : launch_fwd_t<80, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
+    case 128: return causal ? launch_fwd_t<128, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
+                            : launch_fwd_t<128, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
     default:  return hipErrorInvalidValue;
   }
 }

@@ -5,8 +5,10 @@
 
 namespace fa2 {
 
+// Query rows Nq (q, o, lse, dout, dq, row arrays), key rows Nk (k, v, dk, dv).
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      hipStream_t stream);
 
 // Rows per (batch, head) of the padded fp32 arrays the backward kernels read.
 int bwd_rows_padded(int N);
@@ -16,11 +18,12 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                            const float* lse_log2, const float* delta, void* dk, void* dv, int B,
-                           int H, int N, int d, float scale, int causal, hipStream_t stream);
+                           int H, int Nq, int Nk, int d, float scale, int causal,
+                           hipStream_t stream);
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                         const float* lse_log2, const float* delta, void* dq, int B, int H, int N,
-                         int d, float scale, int causal, hipStream_t stream);
+                         const float* lse_log2, const float* delta, void* dq, int B, int H,
+                         int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
 
 void fwd_tiles(int d, int* block_q, int* block_k, int* waves);
 void bwd_tiles(int d, int* block_k, int* block_q, int* waves);

@@ -8,6 +8,9 @@ missing or a call fails, an exception is raised.
 
 Functions mirror the C entry points: ``fwd``, ``bwd``, ``bwd_workspace_bytes``,
 ``bwd_rows_padded``, ``bwd_preprocess``, ``bwd_dkdv``, ``bwd_dq``, ``tile_config``.
+Query and key lengths are taken from the tensors: q, o, do, dq hold Nq rows,
+k, v, dk, dv hold Nk rows; with Nq == Nk the plain entry points are called,
+otherwise their ``_qk`` variants (causal mask aligned bottom-right).
 """
 
 import ctypes
@@ -28,6 +31,10 @@ _c_size = ctypes.c_size_t
 
 _SIGNATURES = {
     "fa2_fwd": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
+    "fa2_fwd_qk": (_c_int, [_c_ptr] * 5 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_qk": (_c_int, [_c_ptr] * 9 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "fa2_bwd_dkdv_qk": (_c_int, [_c_ptr] * 8 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_dq_qk": (_c_int, [_c_ptr] * 7 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
     "fa2_bwd_rows_padded": (_c_int, [_c_int]),
     "fa2_bwd_workspace_bytes": (_c_size, [_c_int] * 4),
     "fa2_bwd": (_c_int, [_c_ptr] * 9 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
@@ -103,13 +110,21 @@ def default_scale(d):
     return 1.0 / math.sqrt(d)
 
 
+def _key_shape(q, k):
+    """[B, H, Nk, d] with Nk taken from k (after checking k itself)."""
+    _check_qkv("k", k)
+    return (q.shape[0], q.shape[1], k.shape[2], q.shape[3])
+
+
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
-    """O, L = attention(q, k, v); q/k/v bf16 [B,H,N,d] on the GPU."""
+    """O, L = attention(q, k, v); q bf16 [B,H,Nq,d], k/v bf16 [B,H,Nk,d] on the GPU."""
     import torch
     _check_qkv("q", q)
     B, H, N, d = q.shape
-    _check_qkv("k", k, q.shape)
-    _check_qkv("v", v, q.shape)
+    kshape = _key_shape(q, k)
+    _check_qkv("k", k, kshape)
+    _check_qkv("v", v, kshape)
+    Nk = kshape[2]
     scale = default_scale(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -117,8 +132,12 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_qkv("out", out, q.shape)
     _check_f32("lse", lse, (B, H, N))
-    st = load().fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if Nk == N:
+        st = load().fa2_fwd(*ptrs, B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    else:
+        st = load().fa2_fwd_qk(*ptrs, B, H, N, Nk, d, scale, int(bool(causal)),
+                               _stream_handle(q.device, stream))
     _check(st, "fa2_fwd")
     return out, lse
 
@@ -129,27 +148,32 @@ def bwd_workspace_bytes(B, H, N, d):
 
 def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None,
         workspace=None, stream=None):
-    """dQ, dK, dV of sum(do * o); all bf16 [B,H,N,d] except lse fp32 [B,H,N]."""
+    """dQ, dK, dV of sum(do * o); q/o/do/dq bf16 [B,H,Nq,d], k/v/dk/dv bf16 [B,H,Nk,d], lse fp32 [B,H,Nq]."""
     import torch
     _check_qkv("q", q)
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
-        _check_qkv(name, t, q.shape)
+    kshape = _key_shape(q, k)
+    Nk = kshape[2]
+    for name, t, shape in (("k", k, kshape), ("v", v, kshape), ("o", o, q.shape), ("do", do, q.shape)):
+        _check_qkv(name, t, shape)
     _check_f32("lse", lse, (B, H, N))
     scale = default_scale(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_qkv(name, t, q.shape)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, kshape), ("dv", dv, kshape)):
+        _check_qkv(name, t, shape)
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = load().fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                        B, H, N, d, scale, int(bool(causal)), workspace.data_ptr(),
-                        workspace.numel() * workspace.element_size(),
-                        _stream_handle(q.device, stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    tail = (scale, int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(q.device, stream))
+    if Nk == N:
+        st = load().fa2_bwd(*ptrs, B, H, N, d, *tail)
+    else:
+        st = load().fa2_bwd_qk(*ptrs, B, H, N, Nk, d, *tail)
     _check(st, "fa2_bwd")
     return dq, dk, dv
 
@@ -175,19 +199,29 @@ def bwd_preprocess(o, do, lse, delta, lse_log2, stream=None):
 
 def bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=False, scale=None, stream=None):
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     scale = default_scale(d) if scale is None else float(scale)
-    st = load().fa2_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                             lse_log2.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                             B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+            lse_log2.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    tail = (scale, int(bool(causal)), _stream_handle(q.device, stream))
+    if Nk == N:
+        st = load().fa2_bwd_dkdv(*ptrs, B, H, N, d, *tail)
+    else:
+        st = load().fa2_bwd_dkdv_qk(*ptrs, B, H, N, Nk, d, *tail)
     _check(st, "fa2_bwd_dkdv")
 
 
 def bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=False, scale=None, stream=None):
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     scale = default_scale(d) if scale is None else float(scale)
-    st = load().fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                           lse_log2.data_ptr(), delta.data_ptr(), dq.data_ptr(),
-                           B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+            lse_log2.data_ptr(), delta.data_ptr(), dq.data_ptr())
+    tail = (scale, int(bool(causal)), _stream_handle(q.device, stream))
+    if Nk == N:
+        st = load().fa2_bwd_dq(*ptrs, B, H, N, d, *tail)
+    else:
+        st = load().fa2_bwd_dq_qk(*ptrs, B, H, N, Nk, d, *tail)
     _check(st, "fa2_bwd_dq")
 
 

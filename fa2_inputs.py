@@ -98,6 +98,16 @@ def make_arrays(B, H, N, d, seed=0, sigma=1.0, spike=False):
     return {"q": q, "k": k, "v": v, "do": do, "spike_rows": rows}
 
 
+def make_arrays_qk(B, H, Nq, Nk, d, seed=0):
+    """Q, dO as uint16 bf16 patterns [B,H,Nq,d] and K, V as [B,H,Nk,d] (N(0,1) draws)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, n in (("q", Nq), ("k", Nk), ("v", Nk), ("do", Nq)):
+        out[name] = round_to_bf16_bits(rng.standard_normal((B, H, n, d), dtype=np.float32))
+    out["spike_rows"] = None
+    return out
+
+
 def make_workload(key, seed=0):
     w = WORKLOADS[key]
     return w, make_arrays(w.B, w.H, w.N, w.d, seed=seed, sigma=w.sigma, spike=w.spike)

@@ -8,9 +8,19 @@
  * that adopting it is only a choice of backend.  Per (batch b, head h):
  *
  *     S    = scale * Q K^T                 (never written to memory)
- *     S_ij = -inf for key j > query i      when causal (top-left aligned)
+ *     S_ij = -inf for key j > query i + Nk - Nq   when causal
  *     L_i  = log sum_j exp(S_ij)           natural-log logsumexp, fp32
  *     O    = softmax(S) V
+ *
+ * The plain entry points take one length N for queries and keys (Nq = Nk = N:
+ * the causal mask keeps key j for query i iff j <= i).  The "_qk" entry points
+ * take Nq query rows (q, o, lse, dout, dq) and Nk key rows (k, v, dk, dv); the
+ * pages show the causal mask only for a sequence attending to itself, and for
+ * Nq != Nk it is aligned bottom-right here: the queries are the last Nq
+ * positions of the key sequence, as for a block of new tokens attending to a
+ * key/value cache.  With Nq > Nk under causal, the first Nq - Nk queries see
+ * no key: their O row is 0, their L is -inf and they add nothing to any
+ * gradient.
  *
  * and, given dO, the gradient of sum(dO * O):  dV = P^T dO, dP = dO V^T,
  * D_i = sum_k dO_ik O_ik, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q,
@@ -64,6 +74,17 @@ typedef enum fa2_status {
 } fa2_status;
 
 /*
+ * Forward pass with separate query and key lengths (see the top of this file
+ * for the causal alignment).
+ *   q       : in,  bf16 [B,H,Nq,d];   k, v : in, bf16 [B,H,Nk,d]
+ *   o       : out, bf16 [B,H,Nq,d]
+ *   lse     : out, fp32 [B,H,Nq] (-inf for a query that sees no key)
+ * Nq, Nk >= 1; every other convention as for fa2_fwd.
+ */
+int fa2_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
+
+/*
  * Forward pass: O and L from Q, K, V.
  * One query row-block per workgroup, its rows split across the workgroup's
  * wavefronts; an online softmax runs over K/V tiles staged in LDS, and the
@@ -82,7 +103,8 @@ int fa2_bwd_rows_padded(int N);
 
 /* Bytes of device workspace fa2_bwd needs: delta then L*log2(e), each fp32
  * [B,H,fa2_bwd_rows_padded(N)] and 256-byte aligned.  Returns 0 for
- * unsupported or invalid sizes. */
+ * unsupported or invalid sizes.  For fa2_bwd_qk pass N = Nq (the row arrays
+ * have one entry per query row). */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
@@ -100,9 +122,19 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             int B, int H, int N, int d, float scale, int causal,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass with separate query and key lengths: as fa2_bwd, with q, o,
+ * dout, dq bf16 [B,H,Nq,d], lse fp32 [B,H,Nq], k, v, dk, dv bf16 [B,H,Nk,d]
+ * and a workspace of >= fa2_bwd_workspace_bytes(B,H,Nq,d) bytes.  Runs
+ * fa2_bwd_preprocess (N = Nq), fa2_bwd_dkdv_qk and fa2_bwd_dq_qk. */
+int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward phase 1 (HBM-bound, elementwise): for every row i of every head,
  * delta_i = sum_k dout_ik * o_ik and lse_log2_i = lse_i * log2(e); rows from N
- * up to fa2_bwd_rows_padded(N) get delta 0 and lse_log2 +inf.
+ * up to fa2_bwd_rows_padded(N) get delta 0 and lse_log2 +inf, and so does the
+ * lse_log2 of a row whose lse is -inf (a query that saw no key).
  *   o, dout : in, bf16 [B,H,N,d];  lse : in, fp32 [B,H,N]
  *   delta, lse_log2 : out, fp32 [B,H,Np], Np = fa2_bwd_rows_padded(N) */
 int fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, float* delta,
@@ -117,6 +149,13 @@ int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                  const float* lse_log2, const float* delta, void* dk, void* dv,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 
+/* Phase 2 with separate lengths: q, dout [B,H,Nq,d]; k, v, dk, dv [B,H,Nk,d];
+ * lse_log2, delta from fa2_bwd_preprocess with N = Nq.  (Under the causal
+ * alignment every key is seen by at least the last query.) */
+int fa2_bwd_dkdv_qk(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse_log2, const float* delta, void* dk, void* dv,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
+
 /* Backward phase 3: dQ.  One query row-block per workgroup, looping over the
  * key tiles it can see, recomputing S and dP; no atomics, no accumulator.
  *   q, k, v, dout   : in, bf16 [B,H,N,d];  lse_log2, delta : in, from phase 1
@@ -124,6 +163,13 @@ int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
 int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                const float* lse_log2, const float* delta, void* dq,
                int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Phase 3 with separate lengths: q, dout, dq [B,H,Nq,d]; k, v [B,H,Nk,d];
+ * lse_log2, delta from fa2_bwd_preprocess with N = Nq.  A query that sees no
+ * key gets dQ = 0. */
+int fa2_bwd_dq_qk(const void* q, const void* k, const void* v, const void* dout,
+                  const float* lse_log2, const float* delta, void* dq,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa2_strerror(int status);

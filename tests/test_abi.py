@@ -121,6 +121,32 @@ def test_phase_entry_points_reject(lib):
     assert lib.fa2_bwd_dq(*P[:6], P[6] + 8, 1, 1, 64, 64, 0.1, 0, None) == INVALID
 
 
+@host_only
+def test_separate_length_entry_points_reject(lib):
+    # fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, stream)
+    assert lib.fa2_fwd_qk(*P[:5], 1, 2, 64, 0, 64, 0.1, 1, None) == INVALID      # no keys
+    assert lib.fa2_fwd_qk(*P[:5], 1, 2, 0, 64, 64, 0.1, 1, None) == INVALID      # no queries
+    assert lib.fa2_fwd_qk(*P[:5], 1, 2, 64, 64, 72, 0.1, 1, None) == UNSUPPORTED
+    assert lib.fa2_fwd_qk(*P[:5], 1, 1 << 16, 1, 1 << 12, 128, 0.1, 0, None) == INVALID  # Nk too long
+    # k spans Nk rows: an output placed inside k's (longer) span is rejected
+    nk_bytes = 2 * 1000 * 64 * 2
+    assert lib.fa2_fwd_qk(P[0], P[1], P[2], P[1] + nk_bytes - 256, P[4], 1, 2, 10, 1000, 64, 0.1, 0,
+                          None) == INVALID
+    # bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, ws, ws_bytes, stream)
+    need = lib.fa2_bwd_workspace_bytes(1, 2, 10, 64)
+    assert lib.fa2_bwd_qk(*P[:9], 1, 2, 10, 0, 64, 0.1, 1, P[9], need, None) == INVALID
+    assert lib.fa2_bwd_qk(*P[:9], 1, 2, 10, 300, 64, 0.1, 1, P[9], need - 1, None) == WORKSPACE
+    assert lib.fa2_bwd_qk(*P[:7], P[1] + 4096, P[8], 1, 2, 10, 300, 64, 0.1, 1, P[9], need,
+                          None) == INVALID                                       # dk inside k
+    # dkdv_qk / dq_qk: dk, dv hold Nk rows, dq holds Nq rows
+    assert lib.fa2_bwd_dkdv_qk(*P[:6], P[6], P[6] + 2 * 10 * 64 * 2, 1, 2, 10, 300, 64, 0.1, 1,
+                               None) == INVALID                                  # dv overlaps dk (Nk rows)
+    assert lib.fa2_bwd_dkdv_qk(*P[:8], 1, 2, 10, 0, 64, 0.1, 1, None) == INVALID
+    assert lib.fa2_bwd_dq_qk(*P[:7], 1, 2, 10, 300, 96, 0.1, 0, None) == UNSUPPORTED
+    assert lib.fa2_bwd_dq_qk(*P[:6], P[1] + 2 * 2 * 299 * 64, 1, 2, 10, 300, 64, 0.1, 0,
+                             None) == INVALID                                    # dq inside k
+
+
 def test_workspace_size_query(lib):
     assert lib.fa2_bwd_rows_padded(1) == 256
     assert lib.fa2_bwd_rows_padded(256) == 256

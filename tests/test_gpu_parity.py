@@ -97,6 +97,35 @@ def test_other_scales(scale):
     assert_full_parity(arrs, True, scale, f"scale={scale}")
 
 
+# Query and key lengths that differ (causal mask aligned bottom-right): decode
+# (one query), a short query block against a long key/value cache, more
+# queries than keys (the first Nq - Nk rows see nothing: O = 0, L = -inf,
+# dQ = 0), ragged tails on both sides, all three head dimensions.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 2, 1, 300, 128), (2, 1, 1, 64, 64), (1, 2, 77, 500, 64),
+                                         (1, 1, 64, 1000, 128), (2, 2, 300, 130, 80),
+                                         (1, 2, 513, 200, 128), (1, 1, 129, 257, 80),
+                                         (1, 3, 200, 333, 128)])
+def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
+    arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=3000 + Nq + Nk + d)
+    label = f"B{B} H{H} Nq{Nq} Nk{Nk} d{d} causal={causal}"
+    out = run_gpu(arrs, causal, 1.0 / math.sqrt(d))
+    x = decode(arrs)
+    o_ref, l_ref = A.forward(x["q"], x["k"], x["v"], 1.0 / math.sqrt(d), causal)
+    g_ref = A.backward(x["q"], x["k"], x["v"], x["do"], 1.0 / math.sqrt(d), causal)
+    o, lse = to_f64(out["o"]), to_f64(out["lse"])
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lse), empty), label   # exactly the rows that see no key
+    assert np.all(o[empty] == 0) and np.all(to_f64(out["dq"])[empty] == 0), label
+    errs = {"O": float(np.max(np.abs(o - o_ref))),
+            "L": float(np.max(np.abs(lse[~empty] - l_ref[~empty]))) if (~empty).any() else 0.0}
+    for n, r in zip(("dq", "dk", "dv"), g_ref):
+        errs[n] = frob_rel(to_f64(out[n]), r)
+    print(label, errs, flush=True)
+    assert errs["O"] <= O_TOL and errs["L"] <= L_TOL, errs
+    assert max(errs["dq"], errs["dk"], errs["dv"]) <= G_TOL, errs
+
+
 def test_workload_c1_every_element():
     w, arrs = gen.make_workload("c1")
     assert_full_parity(arrs, w.causal, w.scale, w.name)
