@@ -603,6 +603,7 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
   switch (d) {
     case 64:  return launch_pre_t<64>(o, dout, lse, delta, l2, B * H, N, stream);
     case 80:  return launch_pre_t<80>(o, dout, lse, delta, l2, B * H, N, stream);
+    case 96:  return launch_pre_t<96>(o, dout, lse, delta, l2, B * H, N, stream);
     case 128: return launch_pre_t<128>(o, dout, lse, delta, l2, B * H, N, stream);
     default:  return hipErrorInvalidValue;
   }
@@ -612,6 +613,7 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
   switch (d) {                                                                  \
     case 64:  return causal ? FN<64, true>(__VA_ARGS__) : FN<64, false>(__VA_ARGS__);   \
     case 80:  return causal ? FN<80, true>(__VA_ARGS__) : FN<80, false>(__VA_ARGS__);   \
+    case 96:  return causal ? FN<96, true>(__VA_ARGS__) : FN<96, false>(__VA_ARGS__);   \
     case 128: return causal ? FN<128, true>(__VA_ARGS__) : FN<128, false>(__VA_ARGS__); \
     default:  return hipErrorInvalidValue;                                      \
   }

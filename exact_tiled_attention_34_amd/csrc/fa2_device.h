@@ -209,7 +209,7 @@ struct TrStage {
       *reinterpret_cast<u32x2*>(dst + e * TrTile<D, TOK>::ROW) = out;
     }
   }
-  // The same tokens as rows 4g..4g+3 of a RowTile (the pad slot of D = 80 is
+  // The same tokens as rows 4g..4g+3 of a RowTile (the pad slot of a padded row is
   // left as it is: no operand read reaches it).
   __device__ __forceinline__ void store_rows(uint16_t* tile) const {
     if (!act) return;

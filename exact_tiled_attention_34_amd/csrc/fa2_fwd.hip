@@ -319,6 +319,8 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                             : launch_fwd_t<64, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
     case 80:  return causal ? launch_fwd_t<80, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
                             : launch_fwd_t<80, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
+    case 96:  return causal ? launch_fwd_t<96, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
+                            : launch_fwd_t<96, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
     case 128: return causal ? launch_fwd_t<128, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
                             : launch_fwd_t<128, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
     default:  return hipErrorInvalidValue;

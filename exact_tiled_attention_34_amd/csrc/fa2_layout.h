@@ -26,7 +26,9 @@ namespace fa2 {
 // chunk by 32 consecutive rows (the MFMA operands whose reduction index is
 // the feature: Q K^T, dO V^T, K Q^T, V dO^T) spread over the LDS banks.
 // D = 128 (16 chunks) and D = 64 (8 chunks) use an XOR of the chunk index;
-// D = 80 (10 chunks) pads every row to 11 chunk slots instead.
+// D = 80 (10 chunks) and D = 96 (12 chunks) pad every row by one chunk slot
+// instead (11 and 13 slots: 176- and 208-byte rows, whose first 16 rows start
+// on 16 distinct 4-bank groups).
 // ---------------------------------------------------------------------------
 template <int D>
 struct RowTile {
@@ -52,7 +54,7 @@ struct RowTile {
   }
   // bf16 element offset of (row, col); col % 4 == 0.
   static FA2_HD int elem(int row, int col) { return slot(row, col >> 3) * 8 + (col & 7); }
-  // Logical chunk stored in slot s (the pad slot of D = 80 holds chunk 0).
+  // Logical chunk stored in slot s (the pad slot of a padded row holds chunk 0).
   static FA2_HD int chunk_of_slot(int s) {
     const int row = s / SLOTS;
     const int c = s % SLOTS;

@@ -20,7 +20,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
 
 FA2_OK = 0
-SUPPORTED_HEAD_DIMS = (64, 80, 128)
+SUPPORTED_HEAD_DIMS = (64, 80, 96, 128)
 
 _lib = None
 

@@ -158,18 +158,23 @@ int main() {
   const int max_n = 3 * 64 + 9;
   check_dma<64, 64, 256>(max_n);
   check_dma<80, 64, 256>(max_n);
+  check_dma<96, 64, 256>(max_n);
   check_dma<128, 64, 256>(max_n);
   check_dma<64, 64, 512>(max_n);
   check_dma<80, 64, 512>(max_n);
+  check_dma<96, 64, 512>(max_n);
   check_dma<128, 64, 512>(max_n);
   check_stage<64, 64, 256>(max_n);
   check_stage<80, 64, 256>(max_n);
+  check_stage<96, 64, 256>(max_n);
   check_stage<128, 64, 256>(max_n);
   check_stage<64, 64, 512>(max_n);
   check_stage<80, 64, 512>(max_n);
+  check_stage<96, 64, 512>(max_n);
   check_stage<128, 64, 512>(max_n);
   check_reads<64>();
   check_reads<80>();
+  check_reads<96>();
   check_reads<128>();
   if (failures) {
     std::printf("%d violations\n", failures);

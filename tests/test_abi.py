@@ -62,7 +62,7 @@ def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=128, d=64, sc
 @host_only
 @pytest.mark.parametrize("kw,want", [
     (dict(N=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(d=112), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
     (dict(causal=2), INVALID), (dict(causal=-1), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=-0.125), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
@@ -106,7 +106,7 @@ def test_bwd_rejects(lib):
 def test_phase_entry_points_reject(lib):
     # preprocess(o, dout, lse, delta, lse_log2, B, H, N, d, stream)
     assert lib.fa2_bwd_preprocess(*P[:5], 1, 1, 0, 64, None) == INVALID
-    assert lib.fa2_bwd_preprocess(*P[:5], 1, 1, 64, 96, None) == UNSUPPORTED
+    assert lib.fa2_bwd_preprocess(*P[:5], 1, 1, 64, 112, None) == UNSUPPORTED
     assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[0], P[4], 1, 1, 64, 64, None) == INVALID
     assert lib.fa2_bwd_preprocess(P[0], P[1], P[2], P[3], P[3] + 256, 1, 1, 64, 64, None) == INVALID
     # dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, N, d, scale, causal, stream)
@@ -142,7 +142,7 @@ def test_separate_length_entry_points_reject(lib):
     assert lib.fa2_bwd_dkdv_qk(*P[:6], P[6], P[6] + 2 * 10 * 64 * 2, 1, 2, 10, 300, 64, 0.1, 1,
                                None) == INVALID                                  # dv overlaps dk (Nk rows)
     assert lib.fa2_bwd_dkdv_qk(*P[:8], 1, 2, 10, 0, 64, 0.1, 1, None) == INVALID
-    assert lib.fa2_bwd_dq_qk(*P[:7], 1, 2, 10, 300, 96, 0.1, 0, None) == UNSUPPORTED
+    assert lib.fa2_bwd_dq_qk(*P[:7], 1, 2, 10, 300, 112, 0.1, 0, None) == UNSUPPORTED
     assert lib.fa2_bwd_dq_qk(*P[:6], P[1] + 2 * 2 * 299 * 64, 1, 2, 10, 300, 64, 0.1, 0,
                              None) == INVALID                                    # dq inside k
 
@@ -152,7 +152,7 @@ def test_workspace_size_query(lib):
     assert lib.fa2_bwd_rows_padded(256) == 256
     assert lib.fa2_bwd_rows_padded(257) == 512
     assert lib.fa2_bwd_rows_padded(0) == 0
-    assert lib.fa2_bwd_workspace_bytes(1, 1, 1, 96) == 0
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 1, 112) == 0
     assert lib.fa2_bwd_workspace_bytes(0, 1, 1, 64) == 0
     # delta and L*log2(e), fp32 [B, H, padded rows], each rounded up to 256 bytes
     assert lib.fa2_bwd_workspace_bytes(1, 1, 3, 80) == 2 * 1024
@@ -165,8 +165,8 @@ def test_strerror_and_tiles(lib):
         assert lib.fa2_strerror(s)
     assert b"unknown" in lib.fa2_strerror(99)
     assert lib.fa2_last_error() == b""
-    for d in (64, 80, 128):
+    for d in (64, 80, 96, 128):
         t = fa2.tile_config(d)
         assert t["fwd_block_q"] % 32 == 0 and t["bwd_block_k"] % 32 == 0
     with pytest.raises(fa2.FA2Error):
-        fa2.tile_config(96)
+        fa2.tile_config(112)

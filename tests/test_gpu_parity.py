@@ -82,7 +82,7 @@ def assert_full_parity(arrs, causal, scale, label=""):
 # small shapes, every element
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", [(1, 1, 1), (1, 1, 12), (1, 2, 64), (2, 1, 127), (1, 1, 128),
                                    (1, 2, 129), (2, 2, 200), (1, 1, 256), (1, 1, 333)])
@@ -105,6 +105,7 @@ def test_other_scales(scale):
 @pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 2, 1, 300, 128), (2, 1, 1, 64, 64), (1, 2, 77, 500, 64),
                                          (1, 1, 64, 1000, 128), (2, 2, 300, 130, 80),
                                          (1, 2, 513, 200, 128), (1, 1, 129, 257, 80),
+                                         (1, 2, 150, 270, 96),
                                          (1, 3, 200, 333, 128)])
 def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=3000 + Nq + Nk + d)
@@ -221,7 +222,7 @@ def test_workload_full_size(key):
 # closed forms on the GPU
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_uniform_scores_give_mean_of_v(d, causal):
     N = 300
@@ -253,7 +254,7 @@ def test_constant_v_gives_ones(causal):
     assert err <= 4e-3, err
 
 
-@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128])
 def test_single_token_and_causal_row0(d):
     arrs = gen.make_arrays(2, 3, 1, d, seed=23)
     out = run_gpu(arrs, True, 1.0 / math.sqrt(d))
@@ -296,7 +297,7 @@ def test_causal_isolation_is_bitwise():
         assert same_o and same_l, i
 
 
-@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128])
 def test_every_output_element_written(d):
     B, H, N = 1, 3, 333
     arrs = gen.make_arrays(B, H, N, d, seed=27)
@@ -326,7 +327,7 @@ def test_run_to_run_determinism():
 
 
 def test_errors_raise():
-    q = torch.zeros((1, 1, 16, 96), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((1, 1, 16, 112), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(fa2.FA2Error) as e:
         fa2.fwd(q, q.clone(), q.clone())
     assert e.value.status == 2
@@ -338,7 +339,7 @@ def test_errors_raise():
         fa2.fwd(q.float(), q, q)
 
 
-@pytest.mark.parametrize("d,causal,N", [(64, True, 200), (80, False, 129), (128, True, 333)])
+@pytest.mark.parametrize("d,causal,N", [(64, True, 200), (80, False, 129), (96, True, 150), (128, True, 333)])
 def test_phases_compose_to_bwd(d, causal, N):
     """fa2_bwd == preprocess + dkdv + dq called one by one (the way bench.py times them)."""
     B, H = 2, 2
