@@ -14,6 +14,8 @@ causal).  ``roofline`` describes the kernel that takes most of the step time;
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+       python bench.py --gpt-block 2k|8k   (the GPT-3-2.7B-shaped attention sublayer:
+                                            model TFLOP/s by the page's end-to-end formula)
 """
 
 import argparse
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
+    ap.add_argument("--gpt-block", choices=sorted(gen.GPT_BLOCKS), default=None,
+                    help="time the GPT-3-2.7B-shaped attention sublayer (synthetic weights) instead")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB (read + write "
                          "of known size: the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -120,6 +124,73 @@ def cpu_baseline(w, arrs, budget_s):
                       f"({dt:.1f} s); conventional flops of those heads / wall time"}
 
 
+def gpt_block_bench(args):
+    """fwd + bwd of one GPT-3-2.7B-shaped attention sublayer (QKV GEMM, the attention
+    kernels, output GEMM; synthetic weights, no data), timed with HIP events; the
+    attention kernels alone are timed on tensors of the same shape for their share."""
+    import numpy as np
+    import torch
+    from exact_tiled_attention_34_amd import fa2
+    from exact_tiled_attention_34_amd.gpt_block import AttentionBlock, model_flops
+
+    cfg = gen.GPT_BLOCKS[args.gpt_block]
+    B, S, hidden, heads = cfg["B"], cfg["S"], cfg["hidden"], cfg["heads"]
+    d = hidden // heads
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    arrs = gen.make_gpt_block(B, S, hidden, seed=args.seed)
+
+    def up(bits, grad=False):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16).requires_grad_(grad)
+
+    x, w_qkv, w_out = up(arrs["x"], True), up(arrs["w_qkv"], True), up(arrs["w_out"], True)
+    dy = up(arrs["dy"])
+    block = AttentionBlock(w_qkv, w_out, heads)
+
+    def step():
+        for t in (x, w_qkv, w_out):
+            t.grad = None
+        block(x, causal=True).backward(dy)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    step_ms = timed(step)
+    qa = gen.make_arrays(B, heads, S, d, seed=args.seed)
+    q, k, v, do = (up(qa[n]) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / np.sqrt(d)
+
+    def attn():
+        o, lse = fa2.fwd(q, k, v, causal=True, scale=scale)
+        fa2.bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+
+    attn_ms = timed(attn)
+    flops = model_flops(B, S, hidden)
+    line = {
+        "metric": "GPT-3-2.7B-shaped attention sublayer fwd+bwd, model TFLOP/s "
+                  "(6*S*params + 12*hidden*S^2 per sequence, causal not halved)",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) x and dy, N(0,0.02^2) weights)",
+        "config": {"workload": f"GPT-3-2.7B attention sublayer, context {args.gpt_block}", "B": B, "S": S,
+                   "hidden": hidden, "heads": heads, "head_dim": d, "causal": True,
+                   "parallelism": "single GPU"},
+        "attention_kernels_ms": round(attn_ms, 4),
+        "attention_share_of_step": round(attn_ms / step_ms, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -129,6 +200,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard "
               "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.gpt_block:
+        gpt_block_bench(args)
+        return
 
     import numpy as np  # noqa: F401
     import torch

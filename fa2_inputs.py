@@ -108,6 +108,27 @@ def make_arrays_qk(B, H, Nq, Nk, d, seed=0):
     return out
 
 
+# Attention sublayer of the GPT-3 2.7B shape in Table 1 of the "FlashAttention-2:
+# Faster Attention with Better Parallelism and Work Partitioning" page (hidden
+# 2560 = 32 heads x 80), at its two context lengths; B x S = 16k tokens each.
+GPT_BLOCKS = {
+    "2k": dict(B=8, S=2048, hidden=2560, heads=32),
+    "8k": dict(B=2, S=8192, hidden=2560, heads=32),
+}
+
+
+def make_gpt_block(B, S, hidden, seed=0, w_std=0.02):
+    """Input x [B,S,hidden], weights W_qkv [hidden,3 hidden] and W_out [hidden,hidden]
+    (N(0, w_std^2), the usual GPT initialisation scale) and the output gradient
+    dy [B,S,hidden], as uint16 bf16 bit patterns; draws in that order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, S, hidden), dtype=np.float32)
+    w_qkv = rng.standard_normal((hidden, 3 * hidden), dtype=np.float32) * np.float32(w_std)
+    w_out = rng.standard_normal((hidden, hidden), dtype=np.float32) * np.float32(w_std)
+    dy = rng.standard_normal((B, S, hidden), dtype=np.float32)
+    return {n: round_to_bf16_bits(a) for n, a in (("x", x), ("w_qkv", w_qkv), ("w_out", w_out), ("dy", dy))}
+
+
 def make_workload(key, seed=0):
     w = WORKLOADS[key]
     return w, make_arrays(w.B, w.H, w.N, w.d, seed=seed, sigma=w.sigma, spike=w.spike)

@@ -1,0 +1,94 @@
+"""GPU: the autograd entry point and the GPT-3-2.7B-shaped attention sublayer against the oracle.
+
+Bar as for the kernels: max |O - O_ref| <= 1e-2 for the attention output and
+relative Frobenius error <= 2e-2 for every gradient; the sublayer (bf16 GEMMs
+around the kernels) is held to relative Frobenius <= 2e-2 on its output and on
+every gradient.  References are float64 on the CPU: the oracle for attention,
+numpy products for the projections, the chain rule written out.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import fa2_inputs as gen
+import oracle
+from oracle import attention as A
+
+torch = pytest.importorskip("torch")
+from exact_tiled_attention_34_amd.autograd import attention  # noqa: E402
+from exact_tiled_attention_34_amd.gpt_block import AttentionBlock  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+O_TOL, G_TOL = 1e-2, 2e-2
+
+
+def to_dev(bits, grad=False):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return t.requires_grad_(grad)
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel(got, ref):
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-3))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(2, 2, 150, 150, 64, True), (1, 3, 97, 230, 128, True),
+                                                 (2, 1, 200, 120, 80, False), (1, 2, 64, 64, 96, True)])
+def test_autograd_attention_matches_oracle(B, H, Nq, Nk, d, causal):
+    arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=4000 + Nq + d)
+    q, k, v = (to_dev(arrs[n], grad=True) for n in ("q", "k", "v"))
+    do = to_dev(arrs["do"])
+    o = attention(q, k, v, causal=causal)
+    o.backward(do)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    x = {n: oracle.bf16_bits_to_float64(arrs[n]) for n in ("q", "k", "v", "do")}
+    o_ref, _ = A.forward(x["q"], x["k"], x["v"], scale, causal)
+    g_ref = A.backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    errs = {"O": float(np.max(np.abs(f64(o) - o_ref)))}
+    for n, t, r in zip(("dq", "dk", "dv"), (q, k, v), g_ref):
+        errs[n] = rel(f64(t.grad), r)
+    print(errs, flush=True)
+    assert errs["O"] <= O_TOL and max(errs["dq"], errs["dk"], errs["dv"]) <= G_TOL, errs
+
+
+def block_reference(x, w_qkv, w_out, dy, heads, causal):
+    """Forward and gradients of y = attn(split(x W_qkv)) W_out in float64 (oracle attention)."""
+    B, S, h = x.shape
+    d = h // heads
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    x2 = x.reshape(B * S, h)
+    qkv = (x2 @ w_qkv).reshape(B, S, 3, heads, d).transpose(2, 0, 3, 1, 4)   # [3, B, H, S, d]
+    o, _ = A.forward(qkv[0], qkv[1], qkv[2], scale, causal)
+    a2 = o.transpose(0, 2, 1, 3).reshape(B * S, h)
+    y = (a2 @ w_out).reshape(B, S, h)
+    dy2 = dy.reshape(B * S, h)
+    dw_out = a2.T @ dy2
+    do = (dy2 @ w_out.T).reshape(B, S, heads, d).transpose(0, 2, 1, 3)
+    dq, dk, dv = A.backward(qkv[0], qkv[1], qkv[2], do, scale, causal)
+    dqkv = np.stack([dq, dk, dv]).transpose(1, 3, 0, 2, 4).reshape(B * S, 3 * h)
+    return y, {"x": (dqkv @ w_qkv.T).reshape(B, S, h), "w_qkv": x2.T @ dqkv, "w_out": dw_out}
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gpt_shaped_block_matches_reference(causal):
+    B, S, hidden, heads = 2, 200, 160, 2          # head dim 80, as in the GPT-3 2.7B shape
+    arrs = gen.make_gpt_block(B, S, hidden, seed=11, w_std=0.1)
+    x = to_dev(arrs["x"], grad=True)
+    w_qkv, w_out = to_dev(arrs["w_qkv"], grad=True), to_dev(arrs["w_out"], grad=True)
+    block = AttentionBlock(w_qkv, w_out, heads)
+    y = block(x, causal=causal)
+    y.backward(to_dev(arrs["dy"]))
+    torch.cuda.synchronize()
+    ref = {n: oracle.bf16_bits_to_float64(arrs[n]) for n in arrs}
+    y_ref, g_ref = block_reference(ref["x"], ref["w_qkv"], ref["w_out"], ref["dy"], heads, causal)
+    errs = {"y": rel(f64(y), y_ref), "dx": rel(f64(x.grad), g_ref["x"]),
+            "dW_qkv": rel(f64(w_qkv.grad), g_ref["w_qkv"]), "dW_out": rel(f64(w_out.grad), g_ref["w_out"])}
+    print(errs, flush=True)
+    assert max(errs.values()) <= G_TOL, errs
