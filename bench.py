@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
     ap.add_argument("--gpt-block", choices=sorted(gen.GPT_BLOCKS), default=None,
                     help="time the GPT-3-2.7B-shaped attention sublayer (synthetic weights) instead")
+    ap.add_argument("--calibrate-gemm", type=int, default=0, metavar="N",
+                    help="instead of the benchmark, time a library bf16 GEMM of N x N x N on random "
+                         "operands (the dense MFMA rate this GPU sustains under realistic data)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB (read + write "
                          "of known size: the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -94,6 +97,30 @@ def calibrate_copy(mib):
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_mib": mib, "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}),
           flush=True)
+
+
+def calibrate_gemm(n, steps=20):
+    """TFLOP/s of torch.mm (hipBLASLt) on random N(0,1) bf16 n x n operands: a practical
+    ceiling for dense bf16 MFMA work, measured with HIP events."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    a = torch.randn(n, n, generator=g).to(dev, torch.bfloat16)
+    b = torch.randn(n, n, generator=g).to(dev, torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"calibrate_gemm_n": n, "ms": round(ms, 4),
+                      "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1),
+                      "peak_bf16_tflops": PEAK_BF16_TFLOPS}), flush=True)
 
 
 def cpu_baseline(w, arrs, budget_s):
@@ -195,6 +222,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.calibrate_gemm:
+        calibrate_gemm(args.calibrate_gemm)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard "

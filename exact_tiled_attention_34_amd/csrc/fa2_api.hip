@@ -66,11 +66,77 @@ bool disjoint(const Span* outs, int n_out, const Span* ins, int n_in) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Contiguous [B, H, N, d] tensors (the plain entry points).
+fa2::Strided dense(const void* p, int H, int N, int d) { return fa2::contiguous(p, H, N, d); }
+
+// A strided bf16 [B, H, N, d] tensor (s == NULL: contiguous).  Checks: 16-byte
+// aligned base; strides >= 0 and multiples of 8 elements (every row starts on
+// 16 bytes); one head's rows within 2^30 elements (the kernels' 32-bit
+// offsets).  For an output, the element map must be one-to-one: ordered by
+// stride, every dimension must step over everything inside it (the last
+// dimension, d elements at stride 1, innermost).  On success *span is the
+// byte range the tensor touches.
+bool strided_view(const void* p, const fa2_strides* s, int B, int H, int N, int d, bool output,
+                  fa2::Strided* t, Span* sp) {
+  if (!ptr_ok(p)) return false;
+  *t = s ? fa2::Strided{p, s->batch, s->head, s->row} : fa2::contiguous(p, H, N, d);
+  const long long st[3] = {t->batch, t->head, t->row};
+  const long long ext[3] = {B, H, N};
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0) return false;
+  if ((long long)(N - 1) * t->row + d > (1LL << 30)) return false;
+  const long long last = (B - 1) * t->batch + (long long)(H - 1) * t->head + (long long)(N - 1) * t->row + d;
+  if (last > (1LL << 40)) return false;
+  if (output) {
+    // insertion-sort the dimensions of extent > 1 by stride, then check nesting
+    long long sst[3], sex[3];
+    int n = 0;
+    for (int i = 0; i < 3; ++i) {
+      if (ext[i] == 1) continue;
+      int j = n++;
+      while (j > 0 && sst[j - 1] > st[i]) {
+        sst[j] = sst[j - 1];
+        sex[j] = sex[j - 1];
+        --j;
+      }
+      sst[j] = st[i];
+      sex[j] = ext[i];
+    }
+    long long inner = d;   // elements spanned by everything inside the current dimension
+    for (int i = 0; i < n; ++i) {
+      if (sst[i] < inner) return false;
+      inner = sst[i] * (sex[i] - 1) + inner;
+    }
+  }
+  *sp = span(p, (size_t)last * 2);
+  return true;
+}
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
 
 extern "C" {
+
+int fa2_fwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
+                    const void* v, const fa2_strides* sv, void* o, const fa2_strides* so,
+                    float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    void* stream) {
+  int st = check_sizes2(B, H, Nq, Nk, d);
+  if (st != FA2_OK) return st;
+  if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  fa2::Strided tq, tk, tv, to;
+  Span ins[3], outs[2];
+  if (!strided_view(q, sq, B, H, Nq, d, false, &tq, &ins[0]) ||
+      !strided_view(k, sk, B, H, Nk, d, false, &tk, &ins[1]) ||
+      !strided_view(v, sv, B, H, Nk, d, false, &tv, &ins[2]) ||
+      !strided_view(o, so, B, H, Nq, d, true, &to, &outs[0]) || !ptr_ok(lse))
+    return FA2_ERR_INVALID_ARG;
+  outs[1] = span(lse, (size_t)B * H * Nq * 4);
+  if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
+  return hip_status(
+      fa2::launch_fwd(tq, tk, tv, to, lse, B, H, Nq, Nk, d, scale, causal, as_stream(stream)));
+}
 
 int fa2_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Nq, int Nk, int d, float scale, int causal, void* stream) {
@@ -84,8 +150,9 @@ int fa2_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
   const Span ins[3] = {span(q, qb), span(k, kb), span(v, kb)};
   const Span outs[2] = {span(o, qb), span(lse, lb)};
   if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
-  return hip_status(
-      fa2::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, as_stream(stream)));
+  return hip_status(fa2::launch_fwd(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d),
+                                    dense(o, H, Nq, d), lse, B, H, Nq, Nk, d, scale, causal,
+                                    as_stream(stream)));
 }
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -112,8 +179,8 @@ int fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, float*
   const Span ins[3] = {span(o, tb), span(dout, tb), span(lse, rows * 4)};
   const Span outs[2] = {span(delta, prow * 4), span(lse_log2, prow * 4)};
   if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
-  return hip_status(fa2::launch_bwd_preprocess(o, dout, lse, delta, lse_log2, B, H, N, d,
-                                               as_stream(stream)));
+  return hip_status(fa2::launch_bwd_preprocess(dense(o, H, N, d), dense(dout, H, N, d), lse, delta,
+                                               lse_log2, B, H, N, d, as_stream(stream)));
 }
 
 // Shared checks of the two tile phases: 4 bf16 inputs (q, dout: Nq rows; k,
@@ -146,8 +213,10 @@ int fa2_bwd_dkdv_qk(const void* q, const void* k, const void* v, const void* dou
   const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dk, dv, Nk, B, H, Nq, Nk, d,
                                   scale, causal);
   if (st != FA2_OK) return st;
-  return hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, Nq, Nk, d,
-                                         scale, causal, as_stream(stream)));
+  return hip_status(fa2::launch_bwd_dkdv(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d),
+                                         dense(dout, H, Nq, d), lse_log2, delta, dense(dk, H, Nk, d),
+                                         dense(dv, H, Nk, d), B, H, Nq, Nk, d, scale, causal,
+                                         as_stream(stream)));
 }
 
 int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
@@ -163,14 +232,36 @@ int fa2_bwd_dq_qk(const void* q, const void* k, const void* v, const void* dout,
   const int st = check_tile_phase(q, k, v, dout, lse_log2, delta, dq, nullptr, Nq, B, H, Nq, Nk,
                                   d, scale, causal);
   if (st != FA2_OK) return st;
-  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, Nq, Nk, d, scale,
-                                       causal, as_stream(stream)));
+  return hip_status(fa2::launch_bwd_dq(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d),
+                                       dense(dout, H, Nq, d), lse_log2, delta, dense(dq, H, Nq, d),
+                                       B, H, Nq, Nk, d, scale, causal, as_stream(stream)));
 }
 
 int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                const float* lse_log2, const float* delta, void* dq, int B, int H, int N, int d,
                float scale, int causal, void* stream) {
   return fa2_bwd_dq_qk(q, k, v, dout, lse_log2, delta, dq, B, H, N, N, d, scale, causal, stream);
+}
+
+// Shared body of fa2_bwd_qk and fa2_bwd_strided: launches the three phases.
+static int bwd_run(const fa2::Strided& tq, const fa2::Strided& tk, const fa2::Strided& tv,
+                   const fa2::Strided& to, const float* lse, const fa2::Strided& tdo,
+                   const fa2::Strided& tdq, const fa2::Strided& tdk, const fa2::Strided& tdv, int B,
+                   int H, int Nq, int Nk, int d, float scale, int causal, void* workspace,
+                   void* stream) {
+  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(Nq);
+  float* delta = static_cast<float*>(workspace);
+  float* lse_log2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(prow * 4));
+  hipStream_t s = as_stream(stream);
+  int st;
+  if ((st = hip_status(fa2::launch_bwd_preprocess(to, tdo, lse, delta, lse_log2, B, H, Nq, d, s))) !=
+      FA2_OK)
+    return st;
+  if ((st = hip_status(fa2::launch_bwd_dkdv(tq, tk, tv, tdo, lse_log2, delta, tdk, tdv, B, H, Nq, Nk,
+                                            d, scale, causal, s))) != FA2_OK)
+    return st;
+  return hip_status(fa2::launch_bwd_dq(tq, tk, tv, tdo, lse_log2, delta, tdq, B, H, Nq, Nk, d, scale,
+                                       causal, s));
 }
 
 int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -191,19 +282,46 @@ int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const
                        span(o, qb), span(lse, rows * 4), span(dout, qb)};
   const Span outs[4] = {span(dq, qb), span(dk, kb), span(dv, kb), span(workspace, need)};
   if (!disjoint(outs, 4, ins, 6)) return FA2_ERR_INVALID_ARG;
+  return bwd_run(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d), dense(o, H, Nq, d), lse,
+                 dense(dout, H, Nq, d), dense(dq, H, Nq, d), dense(dk, H, Nk, d), dense(dv, H, Nk, d),
+                 B, H, Nq, Nk, d, scale, causal, workspace, stream);
+}
 
-  const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(Nq);
-  float* delta = static_cast<float*>(workspace);
-  float* lse_log2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(prow * 4));
-  hipStream_t s = as_stream(stream);
-  if ((st = hip_status(fa2::launch_bwd_preprocess(o, dout, lse, delta, lse_log2, B, H, Nq, d, s))) !=
-      FA2_OK)
-    return st;
-  if ((st = hip_status(fa2::launch_bwd_dkdv(q, k, v, dout, lse_log2, delta, dk, dv, B, H, Nq, Nk,
-                                            d, scale, causal, s))) != FA2_OK)
-    return st;
-  return hip_status(fa2::launch_bwd_dq(q, k, v, dout, lse_log2, delta, dq, B, H, Nq, Nk, d, scale,
-                                       causal, s));
+int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
+                    const void* v, const fa2_strides* sv, const void* o, const fa2_strides* so,
+                    const float* lse, const void* dout, const fa2_strides* sdo, void* dq,
+                    const fa2_strides* sdq, void* dk, const fa2_strides* sdk, void* dv,
+                    const fa2_strides* sdv, int B, int H, int Nq, int Nk, int d, float scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sizes2(B, H, Nq, Nk, d);
+  if (st != FA2_OK) return st;
+  if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  fa2::Strided tq, tk, tv, to, tdo, tdq, tdk, tdv;
+  Span ins[6], outs[4];
+  if (!strided_view(q, sq, B, H, Nq, d, false, &tq, &ins[0]) ||
+      !strided_view(k, sk, B, H, Nk, d, false, &tk, &ins[1]) ||
+      !strided_view(v, sv, B, H, Nk, d, false, &tv, &ins[2]) ||
+      !strided_view(o, so, B, H, Nq, d, false, &to, &ins[3]) ||
+      !strided_view(dout, sdo, B, H, Nq, d, false, &tdo, &ins[4]) ||
+      !strided_view(dq, sdq, B, H, Nq, d, true, &tdq, &outs[0]) ||
+      !strided_view(dk, sdk, B, H, Nk, d, true, &tdk, &outs[1]) ||
+      !strided_view(dv, sdv, B, H, Nk, d, true, &tdv, &outs[2]) || !ptr_ok(lse) ||
+      !ptr_ok(workspace))
+    return FA2_ERR_INVALID_ARG;
+  const size_t need = fa2_bwd_workspace_bytes(B, H, Nq, d);
+  if (workspace_bytes < need) return FA2_ERR_WORKSPACE;
+  ins[5] = span(lse, (size_t)B * H * Nq * 4);
+  outs[3] = span(workspace, need);
+  // each output against every input; the workspace against the three outputs.
+  // The outputs themselves may interleave (for instance three head groups of
+  // one buffer): that they touch disjoint elements is the caller's to ensure.
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], ins[j])) return FA2_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(outs[i], outs[3])) return FA2_ERR_INVALID_ARG;
+  return bwd_run(tq, tk, tv, to, lse, tdo, tdq, tdk, tdv, B, H, Nq, Nk, d, scale, causal, workspace,
+                 stream);
 }
 
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

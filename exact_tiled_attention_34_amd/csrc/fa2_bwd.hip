@@ -43,9 +43,8 @@ namespace {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, float* __restrict__ Delta, float* __restrict__ L2,
-    int N, int Npad, long rows_pad) {
+    CView O, CView dO, const float* __restrict__ LSE, float* __restrict__ Delta,
+    float* __restrict__ L2, int H, int N, int Npad, long rows_pad) {
   constexpr int CH = D / 8;
   const long prow = (long)blockIdx.x * 16 + (threadIdx.x >> 4);   // padded row index
   const int sub = threadIdx.x & 15;
@@ -55,9 +54,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
   const long row = bh * N + q;
   float acc = 0.f;
   if (valid) {
+    const uint16_t* orow = O.head((int)(bh / H), (int)(bh % H)) + (size_t)q * O.sr;
+    const uint16_t* grow = dO.head((int)(bh / H), (int)(bh % H)) + (size_t)q * dO.sr;
     for (int ch = sub; ch < CH; ch += 16) {
-      const u32x4 o = ld_global16(O + row * D + ch * 8);
-      const u32x4 g = ld_global16(dO + row * D + ch * 8);
+      const u32x4 o = ld_global16(orow + ch * 8);
+      const u32x4 g = ld_global16(grow + ch * 8);
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         acc += bf16lo(o[w]) * bf16lo(g[w]) + bf16hi(o[w]) * bf16hi(g[w]);
@@ -207,11 +208,9 @@ struct DkdvWave {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ L2, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    int BH, int Nq, int Nk, int Npad, float scale, float scale_log2) {
+    CView Q, CView K, CView V, CView dO, const float* __restrict__ L2,
+    const float* __restrict__ Delta, View dK, View dV, int BH, int H, int Nq, int Nk, int Npad,
+    float scale, float scale_log2) {
   using C = DkdvCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::TILE];
@@ -231,10 +230,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // most query blocks under a causal mask, so it is dispatched first.
   const int bh = blockIdx.x % BH;
   const int kblk = blockIdx.x / BH;
-  const size_t q_head = (size_t)bh * Nq * D;   // Q, dO
-  const size_t k_head = (size_t)bh * Nk * D;   // K, V, dK, dV
-  const uint16_t* Qh = Q + q_head;
-  const uint16_t* dOh = dO + q_head;
+  const uint16_t* Qh = Q.head(bh / H, bh % H);
+  const uint16_t* dOh = dO.head(bh / H, bh % H);
   const float* L2h = L2 + (size_t)bh * Npad;
   const float* Dh = Delta + (size_t)bh * Npad;
   // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
@@ -260,8 +257,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // Q and dO go through registers once and are written twice per step:
   // row-major and transposed.
   TrStage<D> qstage, dostage;
-  qstage.init(tid);
-  dostage.init(tid);
+  qstage.init(tid, Q.sr);
+  dostage.init(tid, dO.sr);
   auto load_stage = [&](int i) {
     qstage.load(Qh, i * C::BQ, Nq);
     dostage.load(dOh, i * C::BQ, Nq);
@@ -298,8 +295,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   for (int s = 0; s < C::DK; ++s) {
     u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
     if (w.key_lane < Nk) {
-      zk = ld_global16(K + k_head + (size_t)w.key_lane * D + s * 16 + 8 * w.lh);
-      zv = ld_global16(V + k_head + (size_t)w.key_lane * D + s * 16 + 8 * w.lh);
+      zk = ld_global16(K.head(bh / H, bh % H) + (size_t)w.key_lane * K.sr + s * 16 + 8 * w.lh);
+      zv = ld_global16(V.head(bh / H, bh % H) + (size_t)w.key_lane * V.sr + s * 16 + 8 * w.lh);
     }
     w.kf[s] = as_bf16x8(zk);
     w.vf[s] = as_bf16x8(zv);
@@ -347,8 +344,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   // Epilogue: dK = scale * dS^T Q, dV = P^T dO (bf16).
   if (w.key_lane < Nk) {
-    uint16_t* dkrow = dK + k_head + (size_t)w.key_lane * D;
-    uint16_t* dvrow = dV + k_head + (size_t)w.key_lane * D;
+    uint16_t* dkrow = dK.head(bh / H, bh % H) + (size_t)w.key_lane * dK.sr;
+    uint16_t* dvrow = dV.head(bh / H, bh % H) + (size_t)w.key_lane * dV.sr;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -442,10 +439,9 @@ struct DqWave {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
-    int BH, int Nq, int Nk, int Npad, float scale, float scale_log2) {
+    CView Q, CView K, CView V, CView dO, const float* __restrict__ L2,
+    const float* __restrict__ Delta, View dQ, int BH, int H, int Nq, int Nk, int Npad, float scale,
+    float scale_log2) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE];
@@ -460,10 +456,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   int rb = blockIdx.x / BH;
   if (CAUSAL) rb = nrb - 1 - rb;
 
-  const size_t q_head = (size_t)bh * Nq * D;   // Q, dO, dQ
-  const size_t k_head = (size_t)bh * Nk * D;   // K, V
-  const uint16_t* Kh = K + k_head;
-  const uint16_t* Vh = V + k_head;
+  const uint16_t* Kh = K.head(bh / H, bh % H);
+  const uint16_t* Vh = V.head(bh / H, bh % H);
+  const uint16_t* Qh = Q.head(bh / H, bh % H);
+  const uint16_t* dOh = dO.head(bh / H, bh % H);
   // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
   const int koff = Nk - Nq;
 
@@ -488,8 +484,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   // to LDS directly.
   TrStage<D> kstage;
   TileDma<D, C::BC, C::THREADS> vdma;
-  kstage.init(tid);
-  vdma.init(tid);
+  kstage.init(tid, K.sr);
+  vdma.init(tid, V.sr);
   if (n_tiles > 0) {
     vdma.issue(v_lds[0], Vh, 0, Nk);
     kstage.load(Kh, 0, Nk);
@@ -501,8 +497,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   for (int s = 0; s < C::DK; ++s) {
     u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
     if (w.q_lane < Nq) {
-      zq = ld_global16(Q + q_head + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
-      zd = ld_global16(dO + q_head + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
+      zq = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
+      zd = ld_global16(dOh + (size_t)w.q_lane * dO.sr + s * 16 + 8 * w.lh);
     }
     w.qf[s] = as_bf16x8(zq);
     w.dof[s] = as_bf16x8(zd);
@@ -543,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
   // Epilogue: dQ = scale * dS K (bf16).
   if (w.q_lane < Nq) {
-    uint16_t* row = dQ + q_head + (size_t)w.q_lane * D;
+    uint16_t* row = dQ.head(bh / H, bh % H) + (size_t)w.q_lane * dQ.sr;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -559,52 +555,49 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 }
 
 template <int D>
-hipError_t launch_pre_t(const void* o, const void* dout, const float* lse, float* delta, float* l2,
-                        int BH, int N, hipStream_t stream) {
+hipError_t launch_pre_t(const Strided& o, const Strided& dout, const float* lse, float* delta,
+                        float* l2, int B, int H, int N, hipStream_t stream) {
   const int Npad = bwd_rows_padded(N);
-  const long rows_pad = (long)BH * Npad;
+  const long rows_pad = (long)B * H * Npad;
   bwd_preprocess_kernel<D><<<dim3((unsigned)((rows_pad + 15) / 16)), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dout), lse, delta, l2, N, Npad,
-      rows_pad);
+      cview(o), cview(dout), lse, delta, l2, H, N, Npad, rows_pad);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const void* dout,
-                         const float* l2, const float* delta, void* dk, void* dv, int BH, int Nq,
-                         int Nk, float scale, hipStream_t stream) {
+hipError_t launch_dkdv_t(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
+                         const float* l2, const float* delta, const Strided& dk, const Strided& dv,
+                         int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
   using C = DkdvCfg<D>;
   const int nkb = (Nk + C::BKC - 1) / C::BKC;
-  bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(nkb * BH)), C::THREADS, 0, stream>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), l2, delta,
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, Nq, Nk, bwd_rows_padded(Nq),
-      scale, scale * kLog2e);
+  bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(nkb * B * H)), C::THREADS, 0, stream>>>(
+      cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dk), view(dv), B * H, H, Nq, Nk,
+      bwd_rows_padded(Nq), scale, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_dq_t(const void* q, const void* k, const void* v, const void* dout,
-                       const float* l2, const float* delta, void* dq, int BH, int Nq, int Nk,
-                       float scale, hipStream_t stream) {
+hipError_t launch_dq_t(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
+                       const float* l2, const float* delta, const Strided& dq, int B, int H, int Nq,
+                       int Nk, float scale, hipStream_t stream) {
   using C = DqCfg<D>;
   const int nrb = (Nq + C::BR - 1) / C::BR;
-  bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), l2, delta,
-      static_cast<uint16_t*>(dq), BH, Nq, Nk, bwd_rows_padded(Nq), scale, scale * kLog2e);
+  bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * B * H)), C::THREADS, 0, stream>>>(
+      cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dq), B * H, H, Nq, Nk,
+      bwd_rows_padded(Nq), scale, scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, float* delta,
-                                 float* l2, int B, int H, int N, int d, hipStream_t stream) {
+hipError_t launch_bwd_preprocess(const Strided& o, const Strided& dout, const float* lse,
+                                 float* delta, float* l2, int B, int H, int N, int d,
+                                 hipStream_t stream) {
   switch (d) {
-    case 64:  return launch_pre_t<64>(o, dout, lse, delta, l2, B * H, N, stream);
-    case 80:  return launch_pre_t<80>(o, dout, lse, delta, l2, B * H, N, stream);
-    case 96:  return launch_pre_t<96>(o, dout, lse, delta, l2, B * H, N, stream);
-    case 128: return launch_pre_t<128>(o, dout, lse, delta, l2, B * H, N, stream);
+    case 64:  return launch_pre_t<64>(o, dout, lse, delta, l2, B, H, N, stream);
+    case 80:  return launch_pre_t<80>(o, dout, lse, delta, l2, B, H, N, stream);
+    case 96:  return launch_pre_t<96>(o, dout, lse, delta, l2, B, H, N, stream);
+    case 128: return launch_pre_t<128>(o, dout, lse, delta, l2, B, H, N, stream);
     default:  return hipErrorInvalidValue;
   }
 }
@@ -618,16 +611,17 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
     default:  return hipErrorInvalidValue;                                      \
   }
 
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                           const float* l2, const float* delta, void* dk, void* dv, int B, int H,
-                           int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
-  FA2_DISPATCH(launch_dkdv_t, q, k, v, dout, l2, delta, dk, dv, B * H, Nq, Nk, scale, stream)
+hipError_t launch_bwd_dkdv(const Strided& q, const Strided& k, const Strided& v,
+                           const Strided& dout, const float* l2, const float* delta,
+                           const Strided& dk, const Strided& dv, int B, int H, int Nq, int Nk,
+                           int d, float scale, int causal, hipStream_t stream) {
+  FA2_DISPATCH(launch_dkdv_t, q, k, v, dout, l2, delta, dk, dv, B, H, Nq, Nk, scale, stream)
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                         const float* l2, const float* delta, void* dq, int B, int H, int Nq,
-                         int Nk, int d, float scale, int causal, hipStream_t stream) {
-  FA2_DISPATCH(launch_dq_t, q, k, v, dout, l2, delta, dq, B * H, Nq, Nk, scale, stream)
+hipError_t launch_bwd_dq(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
+                         const float* l2, const float* delta, const Strided& dq, int B, int H,
+                         int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  FA2_DISPATCH(launch_dq_t, q, k, v, dout, l2, delta, dq, B, H, Nq, Nk, scale, stream)
 }
 
 #undef FA2_DISPATCH

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa2_launch.h"
 #include "fa2_layout.h"
 
 namespace fa2 {
@@ -130,23 +131,28 @@ __device__ __forceinline__ void global_load_lds16(const void* base, uint32_t byt
 #endif
 }
 
-// Copies ROWS-row tiles of one head (row-major, D features) into a RowTile in
-// LDS with direct global -> LDS loads, following DmaPlan: the per-lane source
-// offsets are computed once (init); a full tile then costs one load per chunk
-// and no vector arithmetic.  Rows past n_rows (the ragged last tile) are
-// clamped to the last row: finite data that the caller masks or weights by
-// zero.  issue() returns immediately; wait_vmem() and a workgroup barrier make
-// the tile visible.
+// Copies ROWS-row tiles of one head (rows R elements apart, D features) into
+// a RowTile in LDS with direct global -> LDS loads, following DmaPlan: the
+// per-lane source offsets are computed once (init); a full tile then costs
+// one load per chunk and no vector arithmetic.  Rows past n_rows (the ragged
+// last tile) are clamped to the last row: finite data that the caller masks
+// or weights by zero.  issue() returns immediately; wait_vmem() and a
+// workgroup barrier make the tile visible.
 template <int D, int ROWS, int THREADS>
 struct TileDma {
   using P = DmaPlan<D, ROWS, THREADS>;
   uint32_t off[P::NOFF];
-  int wave;
+  int lrow[P::NOFF];
+  int wave, R;
 
-  __device__ __forceinline__ void init(int tid) {
+  __device__ __forceinline__ void init(int tid, int row_pitch) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    R = row_pitch;
 #pragma unroll
-    for (int t = 0; t < P::NOFF; ++t) off[t] = P::lane_offset(wave, tid & 63, t);
+    for (int t = 0; t < P::NOFF; ++t) {
+      off[t] = P::lane_offset(wave, tid & 63, t, R);
+      lrow[t] = P::lane_row(wave, tid & 63, t);
+    }
   }
   // requires 0 <= row0 < n_rows
   __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* head, int row0,
@@ -157,38 +163,43 @@ struct TileDma {
       if (first < P::TOTAL) {
         int base_row;
         uint32_t o;
-        P::source(off[P::PERIODIC ? 0 : t], t, row0, n_rows, &base_row, &o);
-        global_load_lds16(head + (size_t)base_row * D, o, tile + first * 8);
+        const int i = P::PERIODIC ? 0 : t;
+        P::source(off[i], lrow[i], t, row0, n_rows, R, &base_row, &o);
+        global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
       }
     }
   }
 };
 
-// Stager of one tile of TOK tokens through registers (StagePlan): begin()
-// and the four load_k() issue the global loads (all at once with load(), or
-// spread over the compute that hides them), store() (once the values are
-// needed, typically after the current tile's compute) writes the transposed
-// tile, store_rows() the same tokens as a RowTile.  Rows past n_rows are
-// clamped to the last row.
+// Stager of one tile of TOK tokens through registers (StagePlan), rows R
+// elements apart: begin() and the four load_k() issue the global loads (all
+// at once with load(), or spread over the compute that hides them), store()
+// (once the values are needed, typically after the current tile's compute)
+// writes the transposed tile, store_rows() the same tokens as a RowTile.
+// Rows past n_rows are clamped to the last row.
 template <int D, int TOK = 64>
 struct TrStage {
   using P = StagePlan<D, TOK>;
   u32x4 r[4];
   uint32_t off;
+  int g, c, R;
   bool act;
   const char* src;
   int lastk;
-  __device__ __forceinline__ void init(int tid) {
+  __device__ __forceinline__ void init(int tid, int row_pitch) {
     act = P::active(tid);
-    off = P::lane_offset(tid);
+    g = P::grp(tid);
+    c = P::chunk(tid);
+    R = row_pitch;
+    off = P::lane_offset(tid, R);
   }
   // requires 0 <= tok0 < n_rows
   __device__ __forceinline__ void begin(const uint16_t* head, int tok0, int n_rows) {
-    src = reinterpret_cast<const char*>(head + (size_t)tok0 * D);
-    lastk = P::last_k(off, tok0, n_rows);
+    src = reinterpret_cast<const char*>(head + (size_t)tok0 * R);
+    lastk = P::last_k(g, tok0, n_rows);
   }
   __device__ __forceinline__ void load_k(int k) {
-    if (act) r[k] = ld_global16(src + (uint32_t)P::source_k(off, k, lastk));
+    if (act) r[k] = ld_global16(src + (uint32_t)P::source_k(off, k, lastk, R));
   }
   __device__ __forceinline__ void load(const uint16_t* head, int tok0, int n_rows) {
     begin(head, tok0, n_rows);
@@ -197,11 +208,11 @@ struct TrStage {
   }
   __device__ __forceinline__ void store(uint16_t* tile) const {
     if (!act) return;
-    uint16_t* dst = tile + TrTile<D, TOK>::elem(8 * P::chunk(off), 4 * P::grp(off));
+    uint16_t* dst = tile + TrTile<D, TOK>::elem(8 * c, 4 * g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;
-      // feature 8 ch + e of tokens 4g..4g+3: low or high halves of word w
+      // feature 8 c + e of tokens 4g..4g+3: low or high halves of word w
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       u32x2 out;
       out[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
@@ -213,10 +224,9 @@ struct TrStage {
   // left as it is: no operand read reaches it).
   __device__ __forceinline__ void store_rows(uint16_t* tile) const {
     if (!act) return;
-    const int g4 = 4 * P::grp(off), c8 = 8 * P::chunk(off);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<u32x4*>(tile + RowTile<D>::elem(g4 + k, c8)) = r[k];
+      *reinterpret_cast<u32x4*>(tile + RowTile<D>::elem(4 * g + k, 8 * c)) = r[k];
   }
 };
 
@@ -227,6 +237,29 @@ __device__ __forceinline__ void tr_zero_pad(uint16_t* t, int tid, int nthreads) 
   using T = TrTile<D, TOK>;
   if constexpr (T::DP != D)
     for (int i = tid; i < (T::DP - D) * T::ROW; i += nthreads) t[D * T::ROW + i] = 0;
+}
+
+// One bf16 [B, H, N, D] tensor addressed through element strides (the last
+// dimension contiguous): element (b, h, n, i) is at p + b sb + h sh + n sr + i.
+// sr is the row pitch R of the tile copies and stages.
+struct CView {
+  const uint16_t* p;
+  long long sb, sh;
+  int sr;
+  __device__ __forceinline__ const uint16_t* head(int b, int h) const { return p + b * sb + h * sh; }
+};
+struct View {
+  uint16_t* p;
+  long long sb, sh;
+  int sr;
+  __device__ __forceinline__ uint16_t* head(int b, int h) const { return p + b * sb + h * sh; }
+};
+
+inline CView cview(const Strided& t) {
+  return CView{static_cast<const uint16_t*>(t.p), t.batch, t.head, (int)t.row};
+}
+inline View view(const Strided& t) {
+  return View{static_cast<uint16_t*>(const_cast<void*>(t.p)), t.batch, t.head, (int)t.row};
 }
 
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {

@@ -194,10 +194,9 @@ __device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL>& w, TrStage<D, F
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int BH, int Nq, int Nk, float scale_log2) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(CView Q, CView K, CView V, View O,
+                                                     float* __restrict__ LSE, int BH, int H, int Nq,
+                                                     int Nk, float scale_log2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::VTILE];
@@ -216,10 +215,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   int rb = blockIdx.x / BH;
   if (CAUSAL) rb = nrb - 1 - rb;
 
-  const size_t q_head = (size_t)bh * Nq * D;   // Q, O
-  const size_t k_head = (size_t)bh * Nk * D;   // K, V
-  const uint16_t* Kh = K + k_head;
-  const uint16_t* Vh = V + k_head;
+  const uint16_t* Qh = Q.head(bh / H, bh % H);
+  const uint16_t* Kh = K.head(bh / H, bh % H);
+  const uint16_t* Vh = V.head(bh / H, bh % H);
+  uint16_t* Oh = O.head(bh / H, bh % H);
   // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
   const int koff = Nk - Nq;
 
@@ -251,8 +250,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   // Tile 0 into LDS (K directly, V transposed through registers).
   TrStage<D, C::BC> vstage;
   TileDma<D, C::BC, C::THREADS> kdma;
-  vstage.init(tid);
-  kdma.init(tid);
+  vstage.init(tid, V.sr);
+  kdma.init(tid, K.sr);
   if (n_tiles > 0) {
     kdma.issue(k_lds[0], Kh, 0, Nk);
     vstage.load(Vh, 0, Nk);
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
     u32x4 z = {0u, 0u, 0u, 0u};
-    if (w.q_lane < Nq) z = ld_global16(Q + q_head + (size_t)w.q_lane * D + s * 16 + 8 * w.lh);
+    if (w.q_lane < Nq) z = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
     w.qf[s] = as_bf16x8(z);
   }
   if (n_tiles > 0) vstage.store(v_lds[0]);
@@ -279,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
   const float l_tot = w.l_run + swap_halves(w.l_run);
   if (w.q_lane < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = O + q_head + (size_t)w.q_lane * D;
+    uint16_t* orow = Oh + (size_t)w.q_lane * O.sr;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -298,21 +297,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
+hipError_t launch_fwd_t(const Strided& q, const Strided& k, const Strided& v, const Strided& o,
+                        float* lse, int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int BH = B * H;
   const int nrb = (Nq + C::BR - 1) / C::BR;
   fwd_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Nq, Nk, scale * kLog2e);
+      cview(q), cview(k), cview(v), view(o), lse, BH, H, Nq, Nk, scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+hipError_t launch_fwd(const Strided& q, const Strided& k, const Strided& v, const Strided& o,
+                      float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
                       hipStream_t stream) {
   switch (d) {
     case 64:  return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)

@@ -98,10 +98,12 @@ struct TrTile {
 //
 // Pass t moves slots [t*THREADS, (t+1)*THREADS); wavefront w's 64 lanes move
 // the 64 consecutive slots starting at w*64 + t*THREADS (a global_load_lds
-// writes lane l's 16 bytes at its wavefront base + 16 l).  The chunk swizzle
-// repeats every 16 rows, so when a pass spans a multiple of 16 rows
-// (PERIODIC) a lane's source offset relative to the first row of its pass is
-// the same in every pass and one register holds it.
+// writes lane l's 16 bytes at its wavefront base + 16 l).  Rows of the source
+// tensor lie R elements apart (R >= D, a multiple of 8: the row pitch, D for a
+// contiguous [.., N, D] tensor).  The chunk swizzle repeats every 16 rows, so
+// when a pass spans a multiple of 16 rows (PERIODIC) a lane's source offset
+// relative to the first row of its pass is the same in every pass and one
+// register holds it.
 // ---------------------------------------------------------------------------
 template <int D, int ROWS, int THREADS>
 struct DmaPlan {
@@ -117,40 +119,41 @@ struct DmaPlan {
   // that wavefront iff the result is < TOTAL.
   static FA2_HD int pass_slot(int wave, int t) { return wave * 64 + t * THREADS; }
 
-  // Byte offset, from the first row of the tile, of the source chunk of lane
-  // `lane` in pass t (stored once per lane: t < NOFF).
-  static FA2_HD uint32_t lane_offset(int wave, int lane, int t) {
+  // Row (from the first row of the tile, or of the pass when PERIODIC) and
+  // byte offset of the source chunk of lane `lane` in pass t, stored once per
+  // lane (t < NOFF).
+  static FA2_HD int lane_row(int wave, int lane, int t) { return (pass_slot(wave, t) + lane) / L::SLOTS; }
+  static FA2_HD uint32_t lane_offset(int wave, int lane, int t, int R) {
     const int s = pass_slot(wave, t) + lane;
-    return (uint32_t)((s / L::SLOTS) * D + L::chunk_of_slot(s) * 8) * 2u;
+    return (uint32_t)((s / L::SLOTS) * R + L::chunk_of_slot(s) * 8) * 2u;
   }
 
-  // Source of pass t given the stored offset `off` (= lane_offset(wave, lane,
-  // PERIODIC ? 0 : t)): the load reads the 16 bytes at
-  //   head + base_row * D elements + byte_off bytes.
+  // Source of pass t given the stored offset `off` and row `lrow` (those of
+  // pass PERIODIC ? 0 : t): the load reads the 16 bytes at
+  //   head + base_row * R elements + byte_off bytes.
   // Rows at or past n_rows are clamped to n_rows - 1.  Requires
   // 0 <= row0 < n_rows; then base_row <= row0 (it never points past the
-  // tensor) and byte_off is a non-negative offset into the tensor.
-  static FA2_HD void source(uint32_t off, int t, int row0, int n_rows, int* base_row,
+  // tensor) and byte_off is a non-negative offset into it.
+  static FA2_HD void source(uint32_t off, int lrow, int t, int row0, int n_rows, int R, int* base_row,
                             uint32_t* byte_off) {
-    const uint32_t in_tile = PERIODIC ? off + (uint32_t)(t * RPP * 2 * D) : off;
     if (row0 + ROWS <= n_rows) {
       // full tile: for PERIODIC the pass moves the scalar base instead
       *base_row = PERIODIC ? row0 + t * RPP : row0;
       *byte_off = off;
       return;
     }
-    uint32_t o = in_tile;
-    const int over = row0 + (int)(o / (2u * D)) - (n_rows - 1);
-    if (over > 0) o -= (uint32_t)over * 2u * D;
+    const int rt = lrow + (PERIODIC ? t * RPP : 0);   // row of the chunk within the tile
+    const int last = n_rows - 1 - row0;
+    const int rc = rt < last ? rt : last;
     *base_row = row0;
-    *byte_off = o;
+    *byte_off = (uint32_t)((int)off + (rc - lrow) * 2 * R);
   }
 };
 
 // ---------------------------------------------------------------------------
 // Register staging of a tile of TOK tokens by the first G*CH threads
 // (G = TOK/4 token groups x CH = D/8 feature chunks): thread i handles tokens
-// 4(i%G)..+3 and features 8(i/G)..+7.
+// 4(i%G)..+3 and features 8(i/G)..+7, reading rows R elements apart.
 // ---------------------------------------------------------------------------
 template <int D, int TOK = 64>
 struct StagePlan {
@@ -158,26 +161,26 @@ struct StagePlan {
   static constexpr int G = TOK / 4;
   static constexpr int THREADS_USED = G * CH;
   static FA2_HD bool active(int tid) { return tid < THREADS_USED; }
+  static FA2_HD int grp(int tid) { return tid % G; }
+  static FA2_HD int chunk(int tid) { return tid / G; }
   // byte offset of (token 4g, feature 8ch) from the tile's first row
-  static FA2_HD uint32_t lane_offset(int tid) {
-    return (uint32_t)(4 * (tid % G) * D + 8 * (tid / G)) * 2u;
+  static FA2_HD uint32_t lane_offset(int tid, int R) {
+    return (uint32_t)(4 * grp(tid) * R + 8 * chunk(tid)) * 2u;
   }
-  static FA2_HD int grp(uint32_t off) { return (int)(off / (8u * D)); }          // 16 ch < 8 D
-  static FA2_HD int chunk(uint32_t off) { return (int)(off % (8u * D)) / 16; }
-  // Last token k (0..3) of the lane's group that lies before row n_rows, for
-  // a tile starting at row tok0 < n_rows; 3 for every lane of a full tile,
+  // Last token k (0..3) of group g that lies before row n_rows, for a tile
+  // starting at row tok0 < n_rows; 3 for every group of a full tile,
   // negative for a group entirely past the end.
-  static FA2_HD int last_k(uint32_t off, int tok0, int n_rows) {
-    const int m = n_rows - 1 - tok0 - 4 * grp(off);
+  static FA2_HD int last_k(int g, int tok0, int n_rows) {
+    const int m = n_rows - 1 - tok0 - 4 * g;
     return m < 3 ? m : 3;
   }
   // Byte offset, from the tile's first row, of the k-th token of the lane's
   // group, clamped to the last row (lastk = last_k(...)); never negative.
-  static FA2_HD int64_t source_k(uint32_t off, int k, int lastk) {
-    return (int64_t)off + (int64_t)(k < lastk ? k : lastk) * 2 * D;
+  static FA2_HD int64_t source_k(uint32_t off, int k, int lastk, int R) {
+    return (int64_t)off + (int64_t)(k < lastk ? k : lastk) * 2 * R;
   }
-  static FA2_HD int64_t source(uint32_t off, int k, int tok0, int n_rows) {
-    return source_k(off, k, last_k(off, tok0, n_rows));
+  static FA2_HD int64_t source(uint32_t off, int g, int k, int tok0, int n_rows, int R) {
+    return source_k(off, k, last_k(g, tok0, n_rows), R);
   }
 };
 

@@ -10,7 +10,11 @@ Functions mirror the C entry points: ``fwd``, ``bwd``, ``bwd_workspace_bytes``,
 ``bwd_rows_padded``, ``bwd_preprocess``, ``bwd_dkdv``, ``bwd_dq``, ``tile_config``.
 Query and key lengths are taken from the tensors: q, o, do, dq hold Nq rows,
 k, v, dk, dv hold Nk rows; with Nq == Nk the plain entry points are called,
-otherwise their ``_qk`` variants (causal mask aligned bottom-right).
+otherwise their ``_qk`` variants (causal mask aligned bottom-right).  Tensors
+need a contiguous last dimension only: when any bf16 tensor of a call is not
+contiguous [B, H, N, d] (a [B, N, H, d] tensor seen through ``transpose(1, 2)``,
+a head group of a fused QKV projection), ``fwd`` and ``bwd`` pass element
+strides to ``fa2_fwd_strided`` / ``fa2_bwd_strided`` instead of copying.
 """
 
 import ctypes
@@ -29,7 +33,17 @@ _c_int = ctypes.c_int
 _c_float = ctypes.c_float
 _c_size = ctypes.c_size_t
 
+class Strides(ctypes.Structure):
+    """fa2_strides: element strides of the batch, head and row dimensions."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
+
+
+_c_strides = ctypes.POINTER(Strides)
+
 _SIGNATURES = {
+    "fa2_fwd_strided": (_c_int, [_c_ptr, _c_strides] * 4 + [_c_ptr] + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_strided": (_c_int, [_c_ptr, _c_strides] * 4 + [_c_ptr] + [_c_ptr, _c_strides] * 4
+                        + [_c_int] * 5 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
     "fa2_fwd": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
     "fa2_fwd_qk": (_c_int, [_c_ptr] * 5 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
     "fa2_bwd_qk": (_c_int, [_c_ptr] * 9 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
@@ -86,18 +100,26 @@ def _stream_handle(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check_qkv(name, t, shape=None):
+def _check_qkv(name, t, shape=None, strided_ok=False):
     import torch
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != torch.bfloat16:
         raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
     if t.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+    if strided_ok:
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} needs a contiguous last dimension")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _strides(t):
+    """fa2_strides of a [B, H, N, d] tensor (element strides), by reference."""
+    return ctypes.byref(Strides(t.stride(0), t.stride(1), t.stride(2)))
 
 
 def _check_f32(name, t, shape):
@@ -112,32 +134,39 @@ def default_scale(d):
 
 def _key_shape(q, k):
     """[B, H, Nk, d] with Nk taken from k (after checking k itself)."""
-    _check_qkv("k", k)
+    _check_qkv("k", k, strided_ok=True)
     return (q.shape[0], q.shape[1], k.shape[2], q.shape[3])
 
 
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
-    """O, L = attention(q, k, v); q bf16 [B,H,Nq,d], k/v bf16 [B,H,Nk,d] on the GPU."""
+    """O, L = attention(q, k, v); q bf16 [B,H,Nq,d], k/v bf16 [B,H,Nk,d] on the GPU.
+
+    Any of q, k, v, out may be a strided view with a contiguous last dimension."""
     import torch
-    _check_qkv("q", q)
+    _check_qkv("q", q, strided_ok=True)
     B, H, N, d = q.shape
     kshape = _key_shape(q, k)
-    _check_qkv("k", k, kshape)
-    _check_qkv("v", v, kshape)
+    _check_qkv("k", k, kshape, strided_ok=True)
+    _check_qkv("v", v, kshape, strided_ok=True)
     Nk = kshape[2]
     scale = default_scale(d) if scale is None else float(scale)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _check_qkv("out", out, q.shape)
+    _check_qkv("out", out, q.shape, strided_ok=True)
     _check_f32("lse", lse, (B, H, N))
-    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
-    if Nk == N:
-        st = load().fa2_fwd(*ptrs, B, H, N, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    tail = (scale, int(bool(causal)), _stream_handle(q.device, stream))
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+        if Nk == N:
+            st = load().fa2_fwd(*ptrs, B, H, N, d, *tail)
+        else:
+            st = load().fa2_fwd_qk(*ptrs, B, H, N, Nk, d, *tail)
     else:
-        st = load().fa2_fwd_qk(*ptrs, B, H, N, Nk, d, scale, int(bool(causal)),
-                               _stream_handle(q.device, stream))
+        st = load().fa2_fwd_strided(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),
+                                    _strides(v), out.data_ptr(), _strides(out), lse.data_ptr(),
+                                    B, H, N, Nk, d, *tail)
     _check(st, "fa2_fwd")
     return out, lse
 
@@ -150,30 +179,40 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None
         workspace=None, stream=None):
     """dQ, dK, dV of sum(do * o); q/o/do/dq bf16 [B,H,Nq,d], k/v/dk/dv bf16 [B,H,Nk,d], lse fp32 [B,H,Nq]."""
     import torch
-    _check_qkv("q", q)
+    _check_qkv("q", q, strided_ok=True)
     B, H, N, d = q.shape
     kshape = _key_shape(q, k)
     Nk = kshape[2]
     for name, t, shape in (("k", k, kshape), ("v", v, kshape), ("o", o, q.shape), ("do", do, q.shape)):
-        _check_qkv(name, t, shape)
+        _check_qkv(name, t, shape, strided_ok=True)
     _check_f32("lse", lse, (B, H, N))
     scale = default_scale(d) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(k) if dv is None else dv
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(kshape, dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(kshape, dtype=q.dtype, device=q.device) if dv is None else dv
     for name, t, shape in (("dq", dq, q.shape), ("dk", dk, kshape), ("dv", dv, kshape)):
-        _check_qkv(name, t, shape)
+        _check_qkv(name, t, shape, strided_ok=True)
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     tail = (scale, int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             _stream_handle(q.device, stream))
-    if Nk == N:
-        st = load().fa2_bwd(*ptrs, B, H, N, d, *tail)
+    tensors = (q, k, v, o, do, dq, dk, dv)
+    if all(t.is_contiguous() for t in tensors):
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+        if Nk == N:
+            st = load().fa2_bwd(*ptrs, B, H, N, d, *tail)
+        else:
+            st = load().fa2_bwd_qk(*ptrs, B, H, N, Nk, d, *tail)
     else:
-        st = load().fa2_bwd_qk(*ptrs, B, H, N, Nk, d, *tail)
+        args = []
+        for t in (q, k, v, o):
+            args += [t.data_ptr(), _strides(t)]
+        args.append(lse.data_ptr())
+        for t in (do, dq, dk, dv):
+            args += [t.data_ptr(), _strides(t)]
+        st = load().fa2_bwd_strided(*args, B, H, N, Nk, d, *tail)
     _check(st, "fa2_bwd")
     return dq, dk, dv
 

@@ -7,13 +7,15 @@ kernels serve, one attention sublayer of the 2.7B shape (hidden 2560, 32 heads
 of 80), with caller-supplied weights and no data and no training:
 
     qkv = x W_qkv                    (plain library GEMM, [B*S, h] x [h, 3h])
-    q, k, v = split(qkv) per head    ([B, H, S, d] each)
-    a = attention(q, k, v, causal)   (the HIP kernels, fa2_fwd / fa2_bwd)
-    y = merge(a) W_out               (plain library GEMM)
+    a = attention(qkv, causal)       (the HIP kernels, fa2_fwd / fa2_bwd, reading
+                                      Q, K, V out of the fused [B, S, 3, H, d]
+                                      tensor and writing a as [B, S, H, d])
+    y = a W_out                      (plain library GEMM)
 
-Backward runs through PyTorch autograd, with ``autograd.FlashAttention2``
-calling fa2_bwd for the attention.  The GEMMs are 2-D matrix products on
-purpose (no batched products of transposed views).
+Backward runs through PyTorch autograd, with
+``autograd.FlashAttention2QKVPacked`` calling fa2_bwd, which writes the fused
+gradient of qkv directly; no tensor is copied to change its layout.  The GEMMs
+are 2-D matrix products on purpose (no batched products of transposed views).
 
 ``model_flops`` applies the page's accounting for end-to-end throughput,
 6 x sequence length x parameters + 12 x layers x hidden x sequence length^2
@@ -24,7 +26,7 @@ parameters are the 4 hidden^2 projection weights.
 
 import torch
 
-from .autograd import attention
+from .autograd import attention_qkvpacked
 
 
 class AttentionBlock:
@@ -42,10 +44,8 @@ class AttentionBlock:
         B, S, h = x.shape
         H, d = self.heads, self.head_dim
         qkv = torch.mm(x.reshape(B * S, h), self.w_qkv)              # [B*S, 3h]
-        qkv = qkv.view(B, S, 3, H, d).permute(2, 0, 3, 1, 4)         # [3, B, H, S, d]
-        a = attention(qkv[0], qkv[1], qkv[2], causal=causal)          # [B, H, S, d]
-        a = a.permute(0, 2, 1, 3).reshape(B * S, h)
-        return torch.mm(a, self.w_out).view(B, S, h)
+        a = attention_qkvpacked(qkv.view(B, S, 3, H, d), causal=causal)  # [B, S, H, d]
+        return torch.mm(a.view(B * S, h), self.w_out).view(B, S, h)
 
 
 def model_flops(B, S, hidden, layers=1):

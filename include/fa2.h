@@ -37,7 +37,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are DEVICE pointers to contiguous row-major [B, H, N, d] arrays
- *    (d fastest).  q, k, v, o, dout, dq, dk, dv hold bfloat16 values stored as
+ *    (d fastest), except in the two "_strided" entry points, which take the
+ *    element strides of each bf16 tensor (fa2_strides).  q, k, v, o, dout, dq, dk, dv hold bfloat16 values stored as
  *    16-bit words.  lse is fp32 [B, H, N]; the backward's delta and lse_log2
  *    are fp32 [B, H, fa2_bwd_rows_padded(N)].
  *  - Supported: B, H, N >= 1 with B*H*N*d < 2^31; d in {64, 80, 96, 128};
@@ -72,6 +73,48 @@ typedef enum fa2_status {
     FA2_ERR_WORKSPACE = 3,   /* workspace too small */
     FA2_ERR_HIP = 4          /* a HIP launch failed; see fa2_last_error() */
 } fa2_status;
+
+/*
+ * Element strides of a bf16 [B, H, N, d] tensor whose last dimension is
+ * contiguous: element (b, h, n, i) lies at base + b*batch + h*head + n*row + i
+ * (in elements, not bytes).  The contiguous [B,H,N,d] layout is
+ * {H*N*d, N*d, d}; a [B, N, H, d] ("batch, sequence, head") tensor is
+ * {N*H*d, d, H*d}; head group j of a fused [B, N, 3, H, d] projection is
+ * base + j*H*d with {N*3*H*d, d, 3*H*d}.
+ * Requirements (else FA2_ERR_INVALID_ARG): the base 16-byte aligned; every
+ * stride >= 0 and a multiple of 8; (N-1)*row + d <= 2^30.  An output tensor
+ * must also map its elements one to one: ordered by stride, every dimension
+ * steps over everything inside it (the d contiguous elements innermost).
+ */
+typedef struct fa2_strides {
+    long long batch, head, row;
+} fa2_strides;
+
+/*
+ * Forward pass on strided tensors: as fa2_fwd_qk, with the layout of q, k, v
+ * and o given by sq, sk, sv, so (NULL: contiguous).  lse stays contiguous fp32
+ * [B,H,Nq].  o and lse must not overlap any input.
+ */
+int fa2_fwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
+                    const void* v, const fa2_strides* sv, void* o, const fa2_strides* so,
+                    float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    void* stream);
+
+/*
+ * Backward pass on strided tensors: as fa2_bwd_qk, with the layout of every
+ * bf16 tensor given by its fa2_strides (NULL: contiguous); lse is contiguous
+ * fp32 [B,H,Nq]; workspace as for fa2_bwd_qk.  No output (dq, dk, dv, the
+ * workspace) may overlap an input, and the workspace no output.  dq, dk and
+ * dv may share one buffer (for instance the three head groups of a fused
+ * [B, N, 3, H, d] gradient) as long as they write disjoint elements, which
+ * the library does not check.
+ */
+int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
+                    const void* v, const fa2_strides* sv, const void* o, const fa2_strides* so,
+                    const float* lse, const void* dout, const fa2_strides* sdo, void* dq,
+                    const fa2_strides* sdq, void* dk, const fa2_strides* sdk, void* dv,
+                    const fa2_strides* sdv, int B, int H, int Nq, int Nk, int d, float scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Forward pass with separate query and key lengths (see the top of this file

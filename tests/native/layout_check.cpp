@@ -25,11 +25,14 @@ static int failures = 0;
     }                                                      \
   } while (0)
 
+// Rows of the source tensor lie R elements apart (R = D: contiguous rows;
+// R > D: a strided view such as one head of a [B, N, H, D] tensor); the
+// tensor's last byte is that of row n - 1's last feature.
 template <int D, int ROWS, int THREADS>
-void check_dma(int max_n) {
+void check_dma(int max_n, int R) {
   using P = DmaPlan<D, ROWS, THREADS>;
   using L = RowTile<D>;
-  const long row_bytes = 2L * D;
+  const long row_bytes = 2L * R;
   for (int n = 1; n <= max_n; ++n) {
     for (int row0 = 0; row0 < n; row0 += ROWS) {
       std::vector<int> written(P::TOTAL, 0);
@@ -42,16 +45,18 @@ void check_dma(int max_n) {
             CHECK(slot < P::TOTAL, "D=%d slot %d", D, slot);
             if (slot >= P::TOTAL) continue;
             written[slot]++;
-            const uint32_t off = P::lane_offset(wave, lane, P::PERIODIC ? 0 : t);
+            const int ti = P::PERIODIC ? 0 : t;
+            const uint32_t off = P::lane_offset(wave, lane, ti, R);
             int base_row;
             uint32_t o;
-            P::source(off, t, row0, n, &base_row, &o);
+            P::source(off, P::lane_row(wave, lane, ti), t, row0, n, R, &base_row, &o);
             CHECK(base_row >= 0 && base_row <= n - 1, "D=%d n=%d row0=%d base_row=%d", D, n, row0, base_row);
             CHECK(o < (1u << 31), "D=%d n=%d row0=%d t=%d offset wraps: %u", D, n, row0, t, o);
             const long addr = base_row * row_bytes + (long)o;
-            CHECK(addr >= 0 && addr + 16 <= n * row_bytes && addr % 16 == 0,
-                  "D=%d THREADS=%d n=%d row0=%d t=%d wave=%d lane=%d addr=%ld of %ld", D, THREADS, n, row0,
-                  t, wave, lane, addr, n * row_bytes);
+            const long end = (n - 1) * row_bytes + 2L * D;
+            CHECK(addr >= 0 && addr + 16 <= end && addr % 16 == 0 && addr % row_bytes + 16 <= 2L * D,
+                  "D=%d R=%d THREADS=%d n=%d row0=%d t=%d wave=%d lane=%d addr=%ld of %ld", D, R, THREADS, n,
+                  row0, t, wave, lane, addr, end);
             const long row = addr / row_bytes;
             const int chunk = (int)((addr % row_bytes) / 16);
             int want_row = row0 + slot / L::SLOTS;
@@ -69,25 +74,26 @@ void check_dma(int max_n) {
 }
 
 template <int D, int TOK, int THREADS>
-void check_stage(int max_n) {
+void check_stage(int max_n, int R) {
   using P = StagePlan<D, TOK>;
   using T = TrTile<D, TOK>;
   using L = RowTile<D>;
   static_assert(P::THREADS_USED <= THREADS, "stage needs more threads than the workgroup has");
-  const long row_bytes = 2L * D;
+  const long row_bytes = 2L * R;
   for (int n = 1; n <= max_n; ++n) {
     for (int tok0 = 0; tok0 < n; tok0 += TOK) {
       std::vector<int> cover(TOK * P::CH, 0);
       std::vector<int> tr_written(T::ELEMS, 0), row_written(L::elems(TOK), 0);
       for (int tid = 0; tid < THREADS; ++tid) {
         if (!P::active(tid)) continue;
-        const uint32_t off = P::lane_offset(tid);
+        const uint32_t off = P::lane_offset(tid, R);
         const int g = tid % P::G, ch = tid / P::G;
-        CHECK(P::grp(off) == g && P::chunk(off) == ch, "D=%d tid=%d grp/chunk", D, tid);
+        CHECK(P::grp(tid) == g && P::chunk(tid) == ch, "D=%d tid=%d grp/chunk", D, tid);
         for (int k = 0; k < 4; ++k) {
-          const long addr = (long)tok0 * row_bytes + P::source(off, k, tok0, n);
-          CHECK(addr >= 0 && addr + 16 <= n * row_bytes && addr % 16 == 0, "D=%d n=%d tok0=%d tid=%d k=%d addr=%ld",
-                D, n, tok0, tid, k, addr);
+          const long addr = (long)tok0 * row_bytes + P::source(off, g, k, tok0, n, R);
+          const long end = (n - 1) * row_bytes + 2L * D;
+          CHECK(addr >= 0 && addr + 16 <= end && addr % 16 == 0 && addr % row_bytes + 16 <= 2L * D,
+                "D=%d R=%d n=%d tok0=%d tid=%d k=%d addr=%ld", D, R, n, tok0, tid, k, addr);
           int want = tok0 + 4 * g + k;
           if (want > n - 1) want = n - 1;
           CHECK(addr / row_bytes == want && (addr % row_bytes) / 16 == ch, "D=%d n=%d tid=%d k=%d row %ld want %d",
@@ -156,22 +162,30 @@ void check_reads() {
 
 int main() {
   const int max_n = 3 * 64 + 9;
-  check_dma<64, 64, 256>(max_n);
-  check_dma<80, 64, 256>(max_n);
-  check_dma<96, 64, 256>(max_n);
-  check_dma<128, 64, 256>(max_n);
-  check_dma<64, 64, 512>(max_n);
-  check_dma<80, 64, 512>(max_n);
-  check_dma<96, 64, 512>(max_n);
-  check_dma<128, 64, 512>(max_n);
-  check_stage<64, 64, 256>(max_n);
-  check_stage<80, 64, 256>(max_n);
-  check_stage<96, 64, 256>(max_n);
-  check_stage<128, 64, 256>(max_n);
-  check_stage<64, 64, 512>(max_n);
-  check_stage<80, 64, 512>(max_n);
-  check_stage<96, 64, 512>(max_n);
-  check_stage<128, 64, 512>(max_n);
+  // row pitches: contiguous rows, a [B, N, H, D] head (R = H D), the q part of a
+  // fused [B, N, 3, H, D] projection (R = 3 H D), and a pitch of D + 8
+  for (int mult : {1, 2, 3}) {
+    check_dma<64, 64, 256>(max_n, 64 * mult);
+    check_dma<80, 64, 256>(max_n, 80 * mult);
+    check_dma<96, 64, 256>(max_n, 96 * mult);
+    check_dma<128, 64, 256>(max_n, 128 * mult);
+    check_dma<64, 64, 512>(max_n, 64 * mult);
+    check_dma<80, 64, 512>(max_n, 80 * mult);
+    check_dma<96, 64, 512>(max_n, 96 * mult);
+    check_dma<128, 64, 512>(max_n, 128 * mult);
+    check_stage<64, 64, 256>(max_n, 64 * mult);
+    check_stage<80, 64, 256>(max_n, 80 * mult);
+    check_stage<96, 64, 256>(max_n, 96 * mult);
+    check_stage<128, 64, 256>(max_n, 128 * mult);
+    check_stage<64, 64, 512>(max_n, 64 * mult);
+    check_stage<80, 64, 512>(max_n, 80 * mult);
+    check_stage<96, 64, 512>(max_n, 96 * mult);
+    check_stage<128, 64, 512>(max_n, 128 * mult);
+  }
+  check_dma<128, 64, 256>(max_n, 136);
+  check_dma<80, 64, 512>(max_n, 88);
+  check_stage<128, 64, 256>(max_n, 136);
+  check_stage<80, 64, 256>(max_n, 88);
   check_reads<64>();
   check_reads<80>();
   check_reads<96>();

@@ -17,7 +17,8 @@ import oracle
 from oracle import attention as A
 
 torch = pytest.importorskip("torch")
-from exact_tiled_attention_34_amd.autograd import attention  # noqa: E402
+from exact_tiled_attention_34_amd import fa2  # noqa: E402
+from exact_tiled_attention_34_amd.autograd import attention, attention_qkvpacked  # noqa: E402
 from exact_tiled_attention_34_amd.gpt_block import AttentionBlock  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -92,3 +93,69 @@ def test_gpt_shaped_block_matches_reference(causal):
             "dW_qkv": rel(f64(w_qkv.grad), g_ref["w_qkv"]), "dW_out": rel(f64(w_out.grad), g_ref["w_out"])}
     print(errs, flush=True)
     assert max(errs.values()) <= G_TOL, errs
+
+
+# ---------------------------------------------------------------------------
+# strided layouts: the kernels read and write views, no copies
+# ---------------------------------------------------------------------------
+
+def bshd(t):
+    """The same values as a [B, N, H, d]-stored tensor, seen as [B, H, N, d]."""
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+def padded_rows(t, pad=8):
+    """The same values in rows of d + pad elements (row stride d + pad)."""
+    B, H, N, d = t.shape
+    buf = torch.zeros((B, H, N, d + pad), dtype=t.dtype, device=t.device)
+    buf[..., :d] = t
+    return buf[..., :d]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(2, 3, 140, 140, 128, True), (1, 2, 77, 260, 80, False),
+                                                 (2, 2, 200, 90, 64, True), (1, 2, 129, 129, 96, False)])
+def test_strided_views_match_oracle(B, H, Nq, Nk, d, causal):
+    arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=5000 + Nq + Nk + d)
+    q, k, v, do = (to_dev(arrs[n]) for n in ("q", "k", "v", "do"))
+    qs, ks, vs, dos = bshd(q), padded_rows(k), bshd(v), padded_rows(do, 16)
+    assert not any(t.is_contiguous() for t in (qs, ks, vs, dos))
+    o_buf = torch.empty((B, Nq, H, d), dtype=torch.bfloat16, device=DEV)
+    o, lse = fa2.fwd(qs, ks, vs, causal=causal, out=o_buf.transpose(1, 2))
+    dq_buf = torch.empty((B, Nq, H, d + 8), dtype=torch.bfloat16, device=DEV)
+    dq = dq_buf[..., :d].transpose(1, 2)
+    dq, dk, dv = fa2.bwd(qs, ks, vs, o, lse, dos, causal=causal, dq=dq)
+    torch.cuda.synchronize()
+    # the same call on contiguous tensors gives bitwise the same results
+    o_c, lse_c = fa2.fwd(q, k, v, causal=causal)
+    g_c = fa2.bwd(q, k, v, o_c, lse_c, do, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), o_c) and torch.equal(lse, lse_c)
+    for a, b in zip((dq, dk, dv), g_c):
+        assert torch.equal(a.contiguous(), b)
+    scale = 1.0 / math.sqrt(d)
+    x = {n: oracle.bf16_bits_to_float64(arrs[n]) for n in ("q", "k", "v", "do")}
+    o_ref, _ = A.forward(x["q"], x["k"], x["v"], scale, causal)
+    g_ref = A.backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    assert float(np.max(np.abs(f64(o) - o_ref))) <= O_TOL
+    for t, r in zip((dq, dk, dv), g_ref):
+        assert rel(f64(t), r) <= G_TOL
+
+
+@pytest.mark.parametrize("B,S,H,d,causal", [(2, 150, 2, 80, True), (1, 257, 3, 128, False), (2, 64, 4, 64, True)])
+def test_qkvpacked_matches_oracle(B, S, H, d, causal):
+    arrs = gen.make_arrays(B, H, S, d, seed=6000 + S + d)
+    qkv_bits = np.stack([arrs[n].transpose(0, 2, 1, 3) for n in ("q", "k", "v")], axis=2)  # [B, S, 3, H, d]
+    qkv = to_dev(qkv_bits, grad=True)
+    do = to_dev(np.ascontiguousarray(arrs["do"].transpose(0, 2, 1, 3)))                    # [B, S, H, d]
+    o = attention_qkvpacked(qkv, causal=causal)
+    assert o.shape == (B, S, H, d) and o.is_contiguous()
+    o.backward(do)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    x = {n: oracle.bf16_bits_to_float64(arrs[n]) for n in ("q", "k", "v", "do")}
+    o_ref, _ = A.forward(x["q"], x["k"], x["v"], scale, causal)
+    g_ref = A.backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    assert float(np.max(np.abs(f64(o).transpose(0, 2, 1, 3) - o_ref))) <= O_TOL
+    g = f64(qkv.grad)
+    for j, r in enumerate(g_ref):
+        assert rel(g[:, :, j].transpose(0, 2, 1, 3), r) <= G_TOL
