@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--calibrate-gemm", type=int, default=0, metavar="N",
                     help="instead of the benchmark, time a library bf16 GEMM of N x N x N on random "
                          "operands (the dense MFMA rate this GPU sustains under realistic data)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="instead of the benchmark, run the register-only MFMA rate probe "
+                         "(zero and random bf16 operands)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB (read + write "
                          "of known size: the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -62,14 +65,14 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("23722d68b6c4ef72", "c2", "bwd_dkdv"): 1359222321,
-    ("23722d68b6c4ef72", "c2", "bwd_dq"): 779791454,
-    ("23722d68b6c4ef72", "c2", "bwd_preprocess"): 138455074,
-    ("23722d68b6c4ef72", "c2", "fwd"): 1161657061,
-    ("23722d68b6c4ef72", "c4", "bwd_dkdv"): 870516751,
-    ("23722d68b6c4ef72", "c4", "bwd_dq"): 790724197,
-    ("23722d68b6c4ef72", "c4", "bwd_preprocess"): 138456802,
-    ("23722d68b6c4ef72", "c4", "fwd"): 832824760,
+    ("0ba954ac8c11beaf", "c2", "bwd_dkdv"): 1359205533,
+    ("0ba954ac8c11beaf", "c2", "bwd_dq"): 770989685,
+    ("0ba954ac8c11beaf", "c2", "bwd_preprocess"): 138465620,
+    ("0ba954ac8c11beaf", "c2", "fwd"): 1166693803,
+    ("0ba954ac8c11beaf", "c4", "bwd_dkdv"): 869917203,
+    ("0ba954ac8c11beaf", "c4", "bwd_dq"): 773862746,
+    ("0ba954ac8c11beaf", "c4", "bwd_preprocess"): 138467476,
+    ("0ba954ac8c11beaf", "c4", "fwd"): 784457191,
 }
 
 
@@ -226,6 +229,14 @@ def main():
     if args.calibrate_gemm:
         calibrate_gemm(args.calibrate_gemm)
         return
+    if args.calibrate_mfma:
+        # a separate program (built by the package's build step); this process
+        # has not touched the GPU, and runs it as a child
+        import subprocess
+        exe = os.path.join(ROOT, "exact_tiled_attention_34_amd", "calib", "mfma_ceiling")
+        if not os.path.exists(exe):
+            sys.exit(f"{exe} is missing: build with `python -m exact_tiled_attention_34_amd.build`")
+        sys.exit(subprocess.run([exe]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard "
               "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
