@@ -78,8 +78,24 @@ def round_to_bf16_bits(x) -> np.ndarray:
     return out
 
 
-def make_arrays(B, H, N, d, seed=0, sigma=1.0, spike=False):
-    """Q, K, V, dO as uint16 bf16 patterns [B,H,N,d] plus the spike rows (or None)."""
+def round_to_fp16_bits(x) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), round-to-nearest-even (numpy's
+    float16 conversion; values past 65504 become infinity)."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _rounder(dtype):
+    if dtype == "bf16":
+        return round_to_bf16_bits
+    if dtype == "fp16":
+        return round_to_fp16_bits
+    raise ValueError(f"unknown 16-bit type {dtype!r}")
+
+
+def make_arrays(B, H, N, d, seed=0, sigma=1.0, spike=False, dtype="bf16"):
+    """Q, K, V, dO as uint16 bit patterns [B,H,N,d] (bf16, or fp16 with dtype="fp16")
+    plus the spike rows (or None)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     shape = (B, H, N, d)
     draws = []
@@ -94,16 +110,16 @@ def make_arrays(B, H, N, d, seed=0, sigma=1.0, spike=False):
         bi, hi = np.meshgrid(np.arange(B), np.arange(H), indexing="ij")
         draws[0][bi, hi, rows] *= np.float32(8.0)
         draws[1][bi, hi, rows] *= np.float32(8.0)
-    q, k, v, do = (round_to_bf16_bits(x) for x in draws)
+    q, k, v, do = (_rounder(dtype)(x) for x in draws)
     return {"q": q, "k": k, "v": v, "do": do, "spike_rows": rows}
 
 
-def make_arrays_qk(B, H, Nq, Nk, d, seed=0):
-    """Q, dO as uint16 bf16 patterns [B,H,Nq,d] and K, V as [B,H,Nk,d] (N(0,1) draws)."""
+def make_arrays_qk(B, H, Nq, Nk, d, seed=0, dtype="bf16"):
+    """Q, dO as uint16 bit patterns [B,H,Nq,d] and K, V as [B,H,Nk,d] (N(0,1) draws)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
     for name, n in (("q", Nq), ("k", Nk), ("v", Nk), ("do", Nq)):
-        out[name] = round_to_bf16_bits(rng.standard_normal((B, H, n, d), dtype=np.float32))
+        out[name] = _rounder(dtype)(rng.standard_normal((B, H, n, d), dtype=np.float32))
     out["spike_rows"] = None
     return out
 

@@ -11,14 +11,14 @@ Contents
                gradient, materialised per (batch, head) in float64.
 ``tiled``      a float64 model of the tile-by-tile online-softmax algorithm,
                used only to show that tiling reaches exactly the plain result.
-``bf16``       decoding of bfloat16 bit patterns to float64 (exact).
+``bf16``       decoding of bfloat16 and float16 bit patterns to float64 (exact).
 
 Pins: every function here is checked against facts fixed by the mathematics
 (closed forms, finite differences, invariants, a library special case) in
 ``tests/test_oracle.py``; nothing is "parity unpinned".
 """
 
-from .bf16 import bf16_bits_to_float64
+from .bf16 import bf16_bits_to_float64, fp16_bits_to_float64, bits_to_float64
 from .attention import (
     causal_offset,
     scores,
@@ -36,6 +36,8 @@ from .tiled import tiled_forward_head, tiled_backward_head
 
 __all__ = [
     "bf16_bits_to_float64",
+    "fp16_bits_to_float64",
+    "bits_to_float64",
     "causal_offset",
     "scores",
     "softmax_rows",

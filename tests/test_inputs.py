@@ -73,3 +73,23 @@ def test_workload_table():
     # conventional flop counts: 4 B H N^2 d forward, x2.5 backward, halved when causal
     assert w["c2"].flops("fwd") == 4 * 8 * 16 * 2048 ** 2 * 128
     assert w["c4"].flops("fwdbwd") == pytest.approx(3.8483e12, rel=1e-4)
+
+
+def test_fp16_rounding_is_nearest_even():
+    one = 1.0
+    x = np.array([one, one + 2.0 ** -11, one + 3 * 2.0 ** -11, -2.5, 65504.0, 65520.0, 2.0 ** -25 * 3],
+                 dtype=np.float32)
+    got = gen.round_to_fp16_bits(x)
+    # 1 + 2^-11 is halfway: to 1.0 (even); 1 + 3*2^-11 halfway: to 1 + 2^-9 (even);
+    # 65520 is halfway to the overflow threshold: to infinity; 1.5 * 2^-24 -> 2^-23 (even)
+    assert got.tolist() == [0x3C00, 0x3C00, 0x3C02, 0xC100, 0x7BFF, 0x7C00, 0x0002]
+
+
+def test_fp16_arrays_match_bf16_draws():
+    a16 = gen.make_arrays(1, 2, 40, 64, seed=9, dtype="fp16")
+    ab = gen.make_arrays(1, 2, 40, 64, seed=9)
+    for n in ("q", "k", "v", "do"):
+        f = a16[n].view(np.float16).astype(np.float64)
+        b = (ab[n].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        # the same draws, rounded to two formats: within one bf16 half-ulp of each other
+        assert np.all(np.abs(f - b) <= np.abs(b) * 2.0 ** -8 + 1e-7)

@@ -38,6 +38,19 @@ def test_bf16_decode_known_patterns():
     assert np.array_equal(oracle.bf16_bits_to_float64(bits.view(np.int16)), got)
 
 
+def test_fp16_decode_known_patterns():
+    bits = np.array([0x0000, 0x8000, 0x3C00, 0xBC00, 0x4000, 0xC200, 0x3800, 0x7C00, 0xFC00,
+                     0x0001, 0x0400, 0x7BFF, 0x3555], dtype=np.uint16)
+    got = oracle.fp16_bits_to_float64(bits)
+    want = [0.0, -0.0, 1.0, -1.0, 2.0, -3.0, 0.5, np.inf, -np.inf,
+            2.0 ** -24, 2.0 ** -14, 65504.0, 1365.0 / 4096.0]   # 0x3555 = 1.0101010101b x 2^-2
+    assert np.array_equal(got, np.array(want))
+    assert np.signbit(got[1])
+    assert np.isnan(oracle.fp16_bits_to_float64(np.array([0x7E00], dtype=np.uint16))[0])
+    assert np.array_equal(oracle.bits_to_float64(bits.view(np.int16), "fp16"), got)
+    assert np.array_equal(oracle.bits_to_float64(bits, "bf16"), oracle.bf16_bits_to_float64(bits))
+
+
 # ---------------------------------------------------------------------------
 # forward closed forms
 # ---------------------------------------------------------------------------
