@@ -121,10 +121,11 @@ extern "C" {
 int fa2_fwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
                     const void* v, const fa2_strides* sv, void* o, const fa2_strides* so,
                     float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                    void* stream) {
+                    int dtype, void* stream) {
   int st = check_sizes2(B, H, Nq, Nk, d);
   if (st != FA2_OK) return st;
   if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_INVALID_ARG;
   fa2::Strided tq, tk, tv, to;
   Span ins[3], outs[2];
   if (!strided_view(q, sq, B, H, Nq, d, false, &tq, &ins[0]) ||
@@ -134,8 +135,8 @@ int fa2_fwd_strided(const void* q, const fa2_strides* sq, const void* k, const f
     return FA2_ERR_INVALID_ARG;
   outs[1] = span(lse, (size_t)B * H * Nq * 4);
   if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
-  return hip_status(
-      fa2::launch_fwd(tq, tk, tv, to, lse, B, H, Nq, Nk, d, scale, causal, as_stream(stream)));
+  return hip_status(fa2::launch_fwd(tq, tk, tv, to, lse, B, H, Nq, Nk, d, scale, causal, dtype,
+                                    as_stream(stream)));
 }
 
 int fa2_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -152,7 +153,7 @@ int fa2_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
   return hip_status(fa2::launch_fwd(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d),
                                     dense(o, H, Nq, d), lse, B, H, Nq, Nk, d, scale, causal,
-                                    as_stream(stream)));
+                                    FA2_BF16, as_stream(stream)));
 }
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -180,7 +181,7 @@ int fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, float*
   const Span outs[2] = {span(delta, prow * 4), span(lse_log2, prow * 4)};
   if (!disjoint(outs, 2, ins, 3)) return FA2_ERR_INVALID_ARG;
   return hip_status(fa2::launch_bwd_preprocess(dense(o, H, N, d), dense(dout, H, N, d), lse, delta,
-                                               lse_log2, B, H, N, d, as_stream(stream)));
+                                               lse_log2, B, H, N, d, FA2_BF16, as_stream(stream)));
 }
 
 // Shared checks of the two tile phases: 4 bf16 inputs (q, dout: Nq rows; k,
@@ -216,7 +217,7 @@ int fa2_bwd_dkdv_qk(const void* q, const void* k, const void* v, const void* dou
   return hip_status(fa2::launch_bwd_dkdv(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d),
                                          dense(dout, H, Nq, d), lse_log2, delta, dense(dk, H, Nk, d),
                                          dense(dv, H, Nk, d), B, H, Nq, Nk, d, scale, causal,
-                                         as_stream(stream)));
+                                         FA2_BF16, as_stream(stream)));
 }
 
 int fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
@@ -234,7 +235,8 @@ int fa2_bwd_dq_qk(const void* q, const void* k, const void* v, const void* dout,
   if (st != FA2_OK) return st;
   return hip_status(fa2::launch_bwd_dq(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d),
                                        dense(dout, H, Nq, d), lse_log2, delta, dense(dq, H, Nq, d),
-                                       B, H, Nq, Nk, d, scale, causal, as_stream(stream)));
+                                       B, H, Nq, Nk, d, scale, causal, FA2_BF16,
+                                       as_stream(stream)));
 }
 
 int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
@@ -247,21 +249,21 @@ int fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
 static int bwd_run(const fa2::Strided& tq, const fa2::Strided& tk, const fa2::Strided& tv,
                    const fa2::Strided& to, const float* lse, const fa2::Strided& tdo,
                    const fa2::Strided& tdq, const fa2::Strided& tdk, const fa2::Strided& tdv, int B,
-                   int H, int Nq, int Nk, int d, float scale, int causal, void* workspace,
-                   void* stream) {
+                   int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                   void* workspace, void* stream) {
   const size_t prow = (size_t)B * H * fa2::bwd_rows_padded(Nq);
   float* delta = static_cast<float*>(workspace);
   float* lse_log2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(prow * 4));
   hipStream_t s = as_stream(stream);
   int st;
-  if ((st = hip_status(fa2::launch_bwd_preprocess(to, tdo, lse, delta, lse_log2, B, H, Nq, d, s))) !=
-      FA2_OK)
+  if ((st = hip_status(fa2::launch_bwd_preprocess(to, tdo, lse, delta, lse_log2, B, H, Nq, d, dtype,
+                                                  s))) != FA2_OK)
     return st;
   if ((st = hip_status(fa2::launch_bwd_dkdv(tq, tk, tv, tdo, lse_log2, delta, tdk, tdv, B, H, Nq, Nk,
-                                            d, scale, causal, s))) != FA2_OK)
+                                            d, scale, causal, dtype, s))) != FA2_OK)
     return st;
   return hip_status(fa2::launch_bwd_dq(tq, tk, tv, tdo, lse_log2, delta, tdq, B, H, Nq, Nk, d, scale,
-                                       causal, s));
+                                       causal, dtype, s));
 }
 
 int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -284,7 +286,7 @@ int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const
   if (!disjoint(outs, 4, ins, 6)) return FA2_ERR_INVALID_ARG;
   return bwd_run(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d), dense(o, H, Nq, d), lse,
                  dense(dout, H, Nq, d), dense(dq, H, Nq, d), dense(dk, H, Nk, d), dense(dv, H, Nk, d),
-                 B, H, Nq, Nk, d, scale, causal, workspace, stream);
+                 B, H, Nq, Nk, d, scale, causal, FA2_BF16, workspace, stream);
 }
 
 int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
@@ -292,10 +294,11 @@ int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const f
                     const float* lse, const void* dout, const fa2_strides* sdo, void* dq,
                     const fa2_strides* sdq, void* dk, const fa2_strides* sdk, void* dv,
                     const fa2_strides* sdv, int B, int H, int Nq, int Nk, int d, float scale,
-                    int causal, void* workspace, size_t workspace_bytes, void* stream) {
+                    int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_sizes2(B, H, Nq, Nk, d);
   if (st != FA2_OK) return st;
   if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  if (dtype != FA2_BF16 && dtype != FA2_FP16) return FA2_ERR_INVALID_ARG;
   fa2::Strided tq, tk, tv, to, tdo, tdq, tdk, tdv;
   Span ins[6], outs[4];
   if (!strided_view(q, sq, B, H, Nq, d, false, &tq, &ins[0]) ||
@@ -320,8 +323,8 @@ int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const f
       if (overlaps(outs[i], ins[j])) return FA2_ERR_INVALID_ARG;
   for (int i = 0; i < 3; ++i)
     if (overlaps(outs[i], outs[3])) return FA2_ERR_INVALID_ARG;
-  return bwd_run(tq, tk, tv, to, lse, tdo, tdq, tdk, tdv, B, H, Nq, Nk, d, scale, causal, workspace,
-                 stream);
+  return bwd_run(tq, tk, tv, to, lse, tdo, tdq, tdk, tdv, B, H, Nq, Nk, d, scale, causal, dtype,
+                 workspace, stream);
 }
 
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

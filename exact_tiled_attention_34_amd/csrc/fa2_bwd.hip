@@ -41,7 +41,7 @@ namespace {
 // ---------------------------------------------------------------------------
 // preprocess
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, class E>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     CView O, CView dO, const float* __restrict__ LSE, float* __restrict__ Delta,
     float* __restrict__ L2, int H, int N, int Npad, long rows_pad) {
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
       const u32x4 g = ld_global16(grow + ch * 8);
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        acc += bf16lo(o[w]) * bf16lo(g[w]) + bf16hi(o[w]) * bf16hi(g[w]);
+        acc += E::lo(o[w]) * E::lo(g[w]) + E::hi(o[w]) * E::hi(g[w]);
     }
   }
 #pragma unroll
@@ -91,10 +91,10 @@ struct DkdvCfg {
   static_assert(BQ == 64, "transposed tiles hold 64 tokens");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 struct DkdvWave {
   using C = DkdvCfg<D>;
-  bf16x8 kf[C::DK], vf[C::DK];
+  u32x4 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
   LaneOffsets<D> off;
@@ -121,7 +121,7 @@ struct DkdvWave {
     constexpr int NT = (C::BQ / 16) * C::NDB;
     constexpr int NALL = NS + NT;
     constexpr int PF = 3;
-    bf16x8 ra[NALL], rb[NALL];
+    u32x4 ra[NALL], rb[NALL];
     auto fetch = [&](int t) {
       if (t < NS) {
         const int o = off.row[t % C::DK] + 2 * (t / C::DK) * LaneOffsets<D>::ROW16;
@@ -166,18 +166,18 @@ struct DkdvWave {
         p[r] = x;
         ds[r] = x * (pacc[qb][t] - dv[qb][g][r]);
       }
-      pw[qb][2 * g] = pack_bf16x2(p[0], p[1]);
-      pw[qb][2 * g + 1] = pack_bf16x2(p[2], p[3]);
-      dsw[qb][2 * g] = pack_bf16x2(ds[0], ds[1]);
-      dsw[qb][2 * g + 1] = pack_bf16x2(ds[2], ds[3]);
+      pw[qb][2 * g] = E::pack2(p[0], p[1]);
+      pw[qb][2 * g + 1] = E::pack2(p[2], p[3]);
+      dsw[qb][2 * g] = E::pack2(ds[0], ds[1]);
+      dsw[qb][2 * g + 1] = E::pack2(ds[2], ds[3]);
     };
 
     // S = Q K^T, dP = dO V^T; softmax of half 0 from stage DK + 1 on.
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       const int qb = t / C::DK, s = t % C::DK;
-      sacc[qb] = mfma32x32x16(ra[t], kf[s], sacc[qb]);
-      pacc[qb] = mfma32x32x16(rb[t], vf[s], pacc[qb]);
+      sacc[qb] = E::mfma(ra[t], kf[s], sacc[qb]);
+      pacc[qb] = E::mfma(rb[t], vf[s], pacc[qb]);
       if (t + PF < NALL) fetch(t + PF);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -192,8 +192,8 @@ struct DkdvWave {
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       const int t = NS + u, c = u / C::NDB, mb = u % C::NDB;
-      dvacc[mb] = mfma32x32x16(ra[t], acc_chunk(pw[c >> 1], c & 1), dvacc[mb]);
-      dkacc[mb] = mfma32x32x16(rb[t], acc_chunk(dsw[c >> 1], c & 1), dkacc[mb]);
+      dvacc[mb] = E::mfma(ra[t], acc_chunk(pw[c >> 1], c & 1), dvacc[mb]);
+      dkacc[mb] = E::mfma(rb[t], acc_chunk(dsw[c >> 1], c & 1), dkacc[mb]);
       if (t + PF < NALL) fetch(t + PF);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -206,7 +206,7 @@ struct DkdvWave {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     CView Q, CView K, CView V, CView dO, const float* __restrict__ L2,
     const float* __restrict__ Delta, View dK, View dV, int BH, int H, int Nq, int Nk, int Npad,
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     store_step(0);
   }
 
-  DkdvWave<D, CAUSAL> w;
+  DkdvWave<D, CAUSAL, E> w;
   w.lane = tid & 63;
   w.lr = w.lane & 31;
   w.lh = w.lane >> 5;
@@ -298,8 +298,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       zk = ld_global16(K.head(bh / H, bh % H) + (size_t)w.key_lane * K.sr + s * 16 + 8 * w.lh);
       zv = ld_global16(V.head(bh / H, bh % H) + (size_t)w.key_lane * V.sr + s * 16 + 8 * w.lh);
     }
-    w.kf[s] = as_bf16x8(zk);
-    w.vf[s] = as_bf16x8(zv);
+    w.kf[s] = zk;
+    w.vf[s] = zv;
   }
 #pragma unroll
   for (int mb = 0; mb < C::NDB; ++mb)
@@ -352,10 +352,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int g = 0; g < 4; ++g) {
         const int d0 = mb * 32 + 8 * g + 4 * w.lh;
         if (d0 < D) {
-          u32x2 wk = {pack_bf16x2(w.dkacc[mb][4 * g] * scale, w.dkacc[mb][4 * g + 1] * scale),
-                      pack_bf16x2(w.dkacc[mb][4 * g + 2] * scale, w.dkacc[mb][4 * g + 3] * scale)};
-          u32x2 wv = {pack_bf16x2(w.dvacc[mb][4 * g], w.dvacc[mb][4 * g + 1]),
-                      pack_bf16x2(w.dvacc[mb][4 * g + 2], w.dvacc[mb][4 * g + 3])};
+          u32x2 wk = {E::pack2(w.dkacc[mb][4 * g] * scale, w.dkacc[mb][4 * g + 1] * scale),
+                      E::pack2(w.dkacc[mb][4 * g + 2] * scale, w.dkacc[mb][4 * g + 3] * scale)};
+          u32x2 wv = {E::pack2(w.dvacc[mb][4 * g], w.dvacc[mb][4 * g + 1]),
+                      E::pack2(w.dvacc[mb][4 * g + 2], w.dvacc[mb][4 * g + 3])};
           *reinterpret_cast<u32x2*>(dkrow + d0) = wk;
           *reinterpret_cast<u32x2*>(dvrow + d0) = wv;
         }
@@ -379,10 +379,10 @@ struct DqCfg {
   static constexpr int TTILE = TrTile<D, 64>::ELEMS;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 struct DqWave {
   using C = DqCfg<D>;
-  bf16x8 qf[C::DK], dof[C::DK];
+  u32x4 qf[C::DK], dof[C::DK];
   f32x16 dqacc[C::NDB];
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
@@ -404,8 +404,8 @@ struct DqWave {
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
         const int o = off.row[s] + 2 * kb * LaneOffsets<D>::ROW16;
-        sacc[kb] = mfma32x32x16(lds_read16(kt + o), qf[s], sacc[kb]);
-        pacc[kb] = mfma32x32x16(lds_read16(vt + o), dof[s], pacc[kb]);
+        sacc[kb] = E::mfma(lds_read16(kt + o), qf[s], sacc[kb]);
+        pacc[kb] = E::mfma(lds_read16(vt + o), dof[s], pacc[kb]);
       }
     }
     mfma_pipeline_hint<1, 4 * C::DK, 4 * C::DK, 6>();
@@ -422,22 +422,22 @@ struct DqWave {
         pacc[kb][i] = p * (pacc[kb][i] - dl);
       }
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) dsw[kb][i >> 1] = pack_bf16x2(pacc[kb][i], pacc[kb][i + 1]);
+      for (int i = 0; i < 16; i += 2) dsw[kb][i >> 1] = E::pack2(pacc[kb][i], pacc[kb][i + 1]);
     }
     // dQ^T (d x query) += K^T (d x 16 keys) dS^T (16 keys x query).
 #pragma unroll
     for (int c = 0; c < C::BC / 16; ++c) {
-      const bf16x8 b = acc_chunk(dsw[c >> 1], c & 1);
+      const u32x4 b = acc_chunk(dsw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        dqacc[mb] = mfma32x32x16(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D>::TR32), b,
+        dqacc[mb] = E::mfma(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D>::TR32), b,
                                  dqacc[mb]);
     }
     mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     CView Q, CView K, CView V, CView dO, const float* __restrict__ L2,
     const float* __restrict__ Delta, View dQ, int BH, int H, int Nq, int Nk, int Npad, float scale,
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
   const int koff = Nk - Nq;
 
-  DqWave<D, CAUSAL> w;
+  DqWave<D, CAUSAL, E> w;
   w.lane = tid & 63;
   w.lr = w.lane & 31;
   w.lh = w.lane >> 5;
@@ -500,8 +500,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       zq = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
       zd = ld_global16(dOh + (size_t)w.q_lane * dO.sr + s * 16 + 8 * w.lh);
     }
-    w.qf[s] = as_bf16x8(zq);
-    w.dof[s] = as_bf16x8(zd);
+    w.qf[s] = zq;
+    w.dof[s] = zd;
   }
   w.l2 = L2[(size_t)bh * Npad + w.q_lane];
   w.dl = Delta[(size_t)bh * Npad + w.q_lane];
@@ -546,43 +546,43 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       for (int g = 0; g < 4; ++g) {
         const int d0 = mb * 32 + 8 * g + 4 * w.lh;
         if (d0 < D) {
-          u32x2 v = {pack_bf16x2(w.dqacc[mb][4 * g] * scale, w.dqacc[mb][4 * g + 1] * scale),
-                     pack_bf16x2(w.dqacc[mb][4 * g + 2] * scale, w.dqacc[mb][4 * g + 3] * scale)};
+          u32x2 v = {E::pack2(w.dqacc[mb][4 * g] * scale, w.dqacc[mb][4 * g + 1] * scale),
+                     E::pack2(w.dqacc[mb][4 * g + 2] * scale, w.dqacc[mb][4 * g + 3] * scale)};
           *reinterpret_cast<u32x2*>(row + d0) = v;
         }
       }
   }
 }
 
-template <int D>
+template <int D, class E>
 hipError_t launch_pre_t(const Strided& o, const Strided& dout, const float* lse, float* delta,
                         float* l2, int B, int H, int N, hipStream_t stream) {
   const int Npad = bwd_rows_padded(N);
   const long rows_pad = (long)B * H * Npad;
-  bwd_preprocess_kernel<D><<<dim3((unsigned)((rows_pad + 15) / 16)), 256, 0, stream>>>(
+  bwd_preprocess_kernel<D, E><<<dim3((unsigned)((rows_pad + 15) / 16)), 256, 0, stream>>>(
       cview(o), cview(dout), lse, delta, l2, H, N, Npad, rows_pad);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 hipError_t launch_dkdv_t(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
                          const float* l2, const float* delta, const Strided& dk, const Strided& dv,
                          int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
   using C = DkdvCfg<D>;
   const int nkb = (Nk + C::BKC - 1) / C::BKC;
-  bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(nkb * B * H)), C::THREADS, 0, stream>>>(
+  bwd_dkdv_kernel<D, CAUSAL, E><<<dim3((unsigned)(nkb * B * H)), C::THREADS, 0, stream>>>(
       cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dk), view(dv), B * H, H, Nq, Nk,
       bwd_rows_padded(Nq), scale, scale * kLog2e);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 hipError_t launch_dq_t(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
                        const float* l2, const float* delta, const Strided& dq, int B, int H, int Nq,
                        int Nk, float scale, hipStream_t stream) {
   using C = DqCfg<D>;
   const int nrb = (Nq + C::BR - 1) / C::BR;
-  bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * B * H)), C::THREADS, 0, stream>>>(
+  bwd_dq_kernel<D, CAUSAL, E><<<dim3((unsigned)(nrb * B * H)), C::THREADS, 0, stream>>>(
       cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dq), B * H, H, Nq, Nk,
       bwd_rows_padded(Nq), scale, scale * kLog2e);
   return hipGetLastError();
@@ -591,40 +591,32 @@ hipError_t launch_dq_t(const Strided& q, const Strided& k, const Strided& v, con
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const Strided& o, const Strided& dout, const float* lse,
-                                 float* delta, float* l2, int B, int H, int N, int d,
+                                 float* delta, float* l2, int B, int H, int N, int d, int dtype,
                                  hipStream_t stream) {
-  switch (d) {
-    case 64:  return launch_pre_t<64>(o, dout, lse, delta, l2, B, H, N, stream);
-    case 80:  return launch_pre_t<80>(o, dout, lse, delta, l2, B, H, N, stream);
-    case 96:  return launch_pre_t<96>(o, dout, lse, delta, l2, B, H, N, stream);
-    case 128: return launch_pre_t<128>(o, dout, lse, delta, l2, B, H, N, stream);
-    default:  return hipErrorInvalidValue;
-  }
+  return dispatch(d, 0, dtype, [&](auto dc, auto, auto ec) {
+    return launch_pre_t<decltype(dc)::value, decltype(ec)>(o, dout, lse, delta, l2, B, H, N, stream);
+  });
 }
-
-#define FA2_DISPATCH(FN, ...)                                                   \
-  switch (d) {                                                                  \
-    case 64:  return causal ? FN<64, true>(__VA_ARGS__) : FN<64, false>(__VA_ARGS__);   \
-    case 80:  return causal ? FN<80, true>(__VA_ARGS__) : FN<80, false>(__VA_ARGS__);   \
-    case 96:  return causal ? FN<96, true>(__VA_ARGS__) : FN<96, false>(__VA_ARGS__);   \
-    case 128: return causal ? FN<128, true>(__VA_ARGS__) : FN<128, false>(__VA_ARGS__); \
-    default:  return hipErrorInvalidValue;                                      \
-  }
 
 hipError_t launch_bwd_dkdv(const Strided& q, const Strided& k, const Strided& v,
                            const Strided& dout, const float* l2, const float* delta,
                            const Strided& dk, const Strided& dv, int B, int H, int Nq, int Nk,
-                           int d, float scale, int causal, hipStream_t stream) {
-  FA2_DISPATCH(launch_dkdv_t, q, k, v, dout, l2, delta, dk, dv, B, H, Nq, Nk, scale, stream)
+                           int d, float scale, int causal, int dtype, hipStream_t stream) {
+  return dispatch(d, causal, dtype, [&](auto dc, auto cc, auto ec) {
+    return launch_dkdv_t<decltype(dc)::value, decltype(cc)::value, decltype(ec)>(
+        q, k, v, dout, l2, delta, dk, dv, B, H, Nq, Nk, scale, stream);
+  });
 }
 
 hipError_t launch_bwd_dq(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
                          const float* l2, const float* delta, const Strided& dq, int B, int H,
-                         int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
-  FA2_DISPATCH(launch_dq_t, q, k, v, dout, l2, delta, dq, B, H, Nq, Nk, scale, stream)
+                         int Nq, int Nk, int d, float scale, int causal, int dtype,
+                         hipStream_t stream) {
+  return dispatch(d, causal, dtype, [&](auto dc, auto cc, auto ec) {
+    return launch_dq_t<decltype(dc)::value, decltype(cc)::value, decltype(ec)>(
+        q, k, v, dout, l2, delta, dq, B, H, Nq, Nk, scale, stream);
+  });
 }
-
-#undef FA2_DISPATCH
 
 void bwd_tiles(int d, int* block_k, int* block_q, int* waves) {
   (void)d;

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa2_launch.h"
 #include "fa2_layout.h"
 
@@ -29,18 +31,44 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Two fp32 -> one word of two bf16 (round to nearest even; v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 x = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-}
+// The 16-bit storage types.  Operands travel as raw 32-bit words (u32x4: 8
+// elements) and are reinterpreted only at the MFMA; P, dS and the outputs are
+// rounded to the storage type to nearest-even.
+struct BF16 {
+  static constexpr int kId = 0;
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> one word of two bf16 (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+};
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+struct F16 {
+  static constexpr int kId = 1;
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -50,7 +78,6 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Exchange with the lane 32 positions away (the other half of the wavefront).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
@@ -255,6 +282,28 @@ struct View {
   __device__ __forceinline__ uint16_t* head(int b, int h) const { return p + b * sb + h * sh; }
 };
 
+// Calls f(head dim, causal, element type) with compile-time values for the
+// run-time (d, causal, dtype) of a launch: the one place that lists every
+// kernel instantiation.
+template <class F>
+inline hipError_t dispatch(int d, int causal, int dtype, F&& f) {
+  auto by_type = [&](auto dc, auto cc) -> hipError_t {
+    if (dtype == 0) return f(dc, cc, BF16{});
+    if (dtype == 1) return f(dc, cc, F16{});
+    return hipErrorInvalidValue;
+  };
+  auto by_causal = [&](auto dc) -> hipError_t {
+    return causal ? by_type(dc, std::true_type{}) : by_type(dc, std::false_type{});
+  };
+  switch (d) {
+    case 64:  return by_causal(std::integral_constant<int, 64>{});
+    case 80:  return by_causal(std::integral_constant<int, 80>{});
+    case 96:  return by_causal(std::integral_constant<int, 96>{});
+    case 128: return by_causal(std::integral_constant<int, 128>{});
+    default:  return hipErrorInvalidValue;
+  }
+}
+
 inline CView cview(const Strided& t) {
   return CView{static_cast<const uint16_t*>(t.p), t.batch, t.head, (int)t.row};
 }
@@ -262,15 +311,15 @@ inline View view(const Strided& t) {
   return View{static_cast<uint16_t*>(const_cast<void*>(t.p)), t.batch, t.head, (int)t.row};
 }
 
-__device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
-// bf16x8 B operand for 16 tokens (chunk c of a 32-row accumulator pair) from
+// MFMA B operand for 16 tokens (chunk c of a 32-row accumulator pair) from
 // packed accumulator words w[0..7] (w[t] = rows 2t, 2t+1 of the accumulator).
-__device__ __forceinline__ bf16x8 acc_chunk(const uint32_t* w, int half) {
+__device__ __forceinline__ u32x4 acc_chunk(const uint32_t* w, int half) {
   const u32x4 v = {w[4 * half + 0], w[4 * half + 1], w[4 * half + 2], w[4 * half + 3]};
-  return as_bf16x8(v);
+  return v;
 }
 
 }  // namespace fa2

@@ -55,10 +55,10 @@ struct FwdCfg {
   static constexpr int VTILE = TrTile<D, BC>::ELEMS;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 struct FwdWave {
   using C = FwdCfg<D>;
-  bf16x8 qf[C::DK];
+  u32x4 qf[C::DK];
   f32x16 oacc[C::NDB];
   f32x16 sc[1][C::KB];  // scores of the current tile
   float m_run, l_run;
@@ -75,7 +75,7 @@ struct FwdWave {
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < C::DK; ++s)
-        sacc[kb] = mfma32x32x16(lds_read16(kt + off.row[s] + 2 * kb * LaneOffsets<D, FwdCfg<D>::BC>::ROW16), qf[s],
+        sacc[kb] = E::mfma(lds_read16(kt + off.row[s] + 2 * kb * LaneOffsets<D, FwdCfg<D>::BC>::ROW16), qf[s],
                                 sacc[kb]);
     }
     mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, 6>();
@@ -120,7 +120,7 @@ struct FwdWave {
         const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -mc));
         const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][i + 1], scale_log2, -mc));
         rs += p0 + p1;
-        pw[kb][i >> 1] = pack_bf16x2(p0, p1);
+        pw[kb][i >> 1] = E::pack2(p0, p1);
       }
     l_run = l_run * alpha + rs;
     m_run = m_new;
@@ -139,10 +139,10 @@ struct FwdWave {
   __device__ __forceinline__ void pv(const uint16_t* vt, const uint32_t (&pw)[C::KB][8]) {
 #pragma unroll
     for (int c = 0; c < C::BC / 16; ++c) {
-      const bf16x8 b = acc_chunk(pw[c >> 1], c & 1);
+      const u32x4 b = acc_chunk(pw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        oacc[mb] = mfma32x32x16(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D>::BC>::TR32), b,
+        oacc[mb] = E::mfma(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D>::BC>::TR32), b,
                                 oacc[mb]);
     }
     mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
@@ -152,8 +152,8 @@ struct FwdWave {
 // Tile j (PAR = j % 2, a compile-time constant so that LDS buffers are
 // immediate offsets): issue the loads of tile j+1, then scores, softmax, the
 // rare rescale and O += V(j) P(j), then the transposed store of V(j+1).
-template <int D, bool CAUSAL, int PAR, bool MASK>
-__device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+template <int D, bool CAUSAL, class E, int PAR, bool MASK>
+__device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
                                          const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
                                          uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                          uint16_t (*v_lds)[FwdCfg<D>::VTILE], const uint16_t* Kh,
@@ -179,8 +179,8 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCf
   vstage.store(v_lds[PAR ^ 1]);
 }
 
-template <int D, bool CAUSAL, int PAR>
-__device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+template <int D, bool CAUSAL, class E, int PAR>
+__device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
                                              const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
                                              uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                              uint16_t (*v_lds)[FwdCfg<D>::VTILE],
@@ -188,12 +188,12 @@ __device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL>& w, TrStage<D, F
                                              int n_tiles, int n_full, int Nk, int tid,
                                              float scale_log2) {
   if (j < n_full)
-    fwd_tile<D, CAUSAL, PAR, false>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
+    fwd_tile<D, CAUSAL, E, PAR, false>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
   else
-    fwd_tile<D, CAUSAL, PAR, true>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
+    fwd_tile<D, CAUSAL, E, PAR, true>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(CView Q, CView K, CView V, View O,
                                                      float* __restrict__ LSE, int BH, int H, int Nq,
                                                      int Nk, float scale_log2) {
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(CView Q, CView K, CView V, 
   // causal: query i sees keys j <= i + koff (queries aligned to the end of the keys)
   const int koff = Nk - Nq;
 
-  FwdWave<D, CAUSAL> w;
+  FwdWave<D, CAUSAL, E> w;
   w.lane = tid & 63;
   w.lr = w.lane & 31;
   w.lh = w.lane >> 5;
@@ -261,15 +261,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(CView Q, CView K, CView V, 
   for (int s = 0; s < C::DK; ++s) {
     u32x4 z = {0u, 0u, 0u, 0u};
     if (w.q_lane < Nq) z = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
-    w.qf[s] = as_bf16x8(z);
+    w.qf[s] = z;
   }
   if (n_tiles > 0) vstage.store(v_lds[0]);
 
   // Tile j uses buffer j % 2; unrolled by two so the buffer is an immediate.
   for (int j = 0; j < n_tiles; j += 2) {
-    fwd_tile_any<D, CAUSAL, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, Nk, tid, scale_log2);
+    fwd_tile_any<D, CAUSAL, E, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, Nk, tid, scale_log2);
     if (j + 1 < n_tiles)
-      fwd_tile_any<D, CAUSAL, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, Nk, tid,
+      fwd_tile_any<D, CAUSAL, E, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, Nk, tid,
                                  scale_log2);
   }
 
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(CView Q, CView K, CView V, 
       for (int g = 0; g < 4; ++g) {
         const int d0 = mb * 32 + 8 * g + 4 * w.lh;
         if (d0 < D) {
-          u32x2 v = {pack_bf16x2(w.oacc[mb][4 * g + 0] * inv, w.oacc[mb][4 * g + 1] * inv),
-                     pack_bf16x2(w.oacc[mb][4 * g + 2] * inv, w.oacc[mb][4 * g + 3] * inv)};
+          u32x2 v = {E::pack2(w.oacc[mb][4 * g + 0] * inv, w.oacc[mb][4 * g + 1] * inv),
+                     E::pack2(w.oacc[mb][4 * g + 2] * inv, w.oacc[mb][4 * g + 3] * inv)};
           *reinterpret_cast<u32x2*>(orow + d0) = v;
         }
       }
@@ -296,13 +296,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(CView Q, CView K, CView V, 
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, class E>
 hipError_t launch_fwd_t(const Strided& q, const Strided& k, const Strided& v, const Strided& o,
                         float* lse, int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int BH = B * H;
   const int nrb = (Nq + C::BR - 1) / C::BR;
-  fwd_kernel<D, CAUSAL><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(
+  fwd_kernel<D, CAUSAL, E><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(
       cview(q), cview(k), cview(v), view(o), lse, BH, H, Nq, Nk, scale * kLog2e);
   return hipGetLastError();
 }
@@ -311,18 +311,11 @@ hipError_t launch_fwd_t(const Strided& q, const Strided& k, const Strided& v, co
 
 hipError_t launch_fwd(const Strided& q, const Strided& k, const Strided& v, const Strided& o,
                       float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                      hipStream_t stream) {
-  switch (d) {
-    case 64:  return causal ? launch_fwd_t<64, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
-                            : launch_fwd_t<64, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
-    case 80:  return causal ? launch_fwd_t<80, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
-                            : launch_fwd_t<80, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
-    case 96:  return causal ? launch_fwd_t<96, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
-                            : launch_fwd_t<96, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
-    case 128: return causal ? launch_fwd_t<128, true>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream)
-                            : launch_fwd_t<128, false>(q, k, v, o, lse, B, H, Nq, Nk, scale, stream);
-    default:  return hipErrorInvalidValue;
-  }
+                      int dtype, hipStream_t stream) {
+  return dispatch(d, causal, dtype, [&](auto dc, auto cc, auto ec) {
+    return launch_fwd_t<decltype(dc)::value, decltype(cc)::value, decltype(ec)>(q, k, v, o, lse, B, H,
+                                                                                 Nq, Nk, scale, stream);
+  });
 }
 
 void fwd_tiles(int d, int* block_q, int* block_k, int* waves) {

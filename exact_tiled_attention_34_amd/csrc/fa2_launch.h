@@ -17,25 +17,27 @@ inline Strided contiguous(const void* p, int H, int N, int d) {
 }
 
 // Query rows Nq (q, o, lse, dout, dq, row arrays), key rows Nk (k, v, dk, dv).
+// dtype: 0 = bfloat16, 1 = float16 (all 16-bit tensors of a call share it).
 hipError_t launch_fwd(const Strided& q, const Strided& k, const Strided& v, const Strided& o,
                       float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                      hipStream_t stream);
+                      int dtype, hipStream_t stream);
 
 // Rows per (batch, head) of the padded fp32 arrays the backward kernels read.
 int bwd_rows_padded(int N);
 
 hipError_t launch_bwd_preprocess(const Strided& o, const Strided& dout, const float* lse,
                                  float* delta, float* lse_log2, int B, int H, int N, int d,
-                                 hipStream_t stream);
+                                 int dtype, hipStream_t stream);
 
 hipError_t launch_bwd_dkdv(const Strided& q, const Strided& k, const Strided& v,
                            const Strided& dout, const float* lse_log2, const float* delta,
                            const Strided& dk, const Strided& dv, int B, int H, int Nq, int Nk,
-                           int d, float scale, int causal, hipStream_t stream);
+                           int d, float scale, int causal, int dtype, hipStream_t stream);
 
 hipError_t launch_bwd_dq(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
                          const float* lse_log2, const float* delta, const Strided& dq, int B, int H,
-                         int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
+                         int Nq, int Nk, int d, float scale, int causal, int dtype,
+                         hipStream_t stream);
 
 void fwd_tiles(int d, int* block_q, int* block_k, int* waves);
 void bwd_tiles(int d, int* block_k, int* block_q, int* waves);

@@ -15,6 +15,8 @@ need a contiguous last dimension only: when any bf16 tensor of a call is not
 contiguous [B, H, N, d] (a [B, N, H, d] tensor seen through ``transpose(1, 2)``,
 a head group of a fused QKV projection), ``fwd`` and ``bwd`` pass element
 strides to ``fa2_fwd_strided`` / ``fa2_bwd_strided`` instead of copying.
+float16 tensors (all 16-bit tensors of a call share one type) go through the
+strided entry points with ``FA2_FP16``.
 """
 
 import ctypes
@@ -24,6 +26,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
 
 FA2_OK = 0
+FA2_BF16, FA2_FP16 = 0, 1
 SUPPORTED_HEAD_DIMS = (64, 80, 96, 128)
 
 _lib = None
@@ -41,9 +44,10 @@ class Strides(ctypes.Structure):
 _c_strides = ctypes.POINTER(Strides)
 
 _SIGNATURES = {
-    "fa2_fwd_strided": (_c_int, [_c_ptr, _c_strides] * 4 + [_c_ptr] + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
+    "fa2_fwd_strided": (_c_int, [_c_ptr, _c_strides] * 4 + [_c_ptr] + [_c_int] * 5
+                        + [_c_float, _c_int, _c_int, _c_ptr]),
     "fa2_bwd_strided": (_c_int, [_c_ptr, _c_strides] * 4 + [_c_ptr] + [_c_ptr, _c_strides] * 4
-                        + [_c_int] * 5 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
+                        + [_c_int] * 5 + [_c_float, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
     "fa2_fwd": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
     "fa2_fwd_qk": (_c_int, [_c_ptr] * 5 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
     "fa2_bwd_qk": (_c_int, [_c_ptr] * 9 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
@@ -104,8 +108,8 @@ def _check_qkv(name, t, shape=None, strided_ok=False):
     import torch
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if t.dtype != torch.bfloat16:
-        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"{name} must be bfloat16 or float16, got {t.dtype}")
     if t.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, H, N, d]")
     if strided_ok:
@@ -115,6 +119,15 @@ def _check_qkv(name, t, shape=None, strided_ok=False):
         raise ValueError(f"{name} must be contiguous [B, H, N, d]")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dtype_code(tensors):
+    """FA2_BF16 / FA2_FP16 for a call whose 16-bit tensors must share one type."""
+    import torch
+    kinds = {t.dtype for t in tensors}
+    if len(kinds) != 1:
+        raise ValueError(f"all 16-bit tensors of a call must share one dtype, got {sorted(map(str, kinds))}")
+    return FA2_FP16 if kinds.pop() == torch.float16 else FA2_BF16
 
 
 def _strides(t):
@@ -156,8 +169,9 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_qkv("out", out, q.shape, strided_ok=True)
     _check_f32("lse", lse, (B, H, N))
+    code = _dtype_code((q, k, v, out))
     tail = (scale, int(bool(causal)), _stream_handle(q.device, stream))
-    if all(t.is_contiguous() for t in (q, k, v, out)):
+    if code == FA2_BF16 and all(t.is_contiguous() for t in (q, k, v, out)):
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
         if Nk == N:
             st = load().fa2_fwd(*ptrs, B, H, N, d, *tail)
@@ -166,7 +180,8 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     else:
         st = load().fa2_fwd_strided(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),
                                     _strides(v), out.data_ptr(), _strides(out), lse.data_ptr(),
-                                    B, H, N, Nk, d, *tail)
+                                    B, H, N, Nk, d, scale, int(bool(causal)), code,
+                                    _stream_handle(q.device, stream))
     _check(st, "fa2_fwd")
     return out, lse
 
@@ -195,10 +210,11 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    tail = (scale, int(bool(causal)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            _stream_handle(q.device, stream))
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(q.device, stream))
+    tail = (scale, int(bool(causal))) + ws
     tensors = (q, k, v, o, do, dq, dk, dv)
-    if all(t.is_contiguous() for t in tensors):
+    code = _dtype_code(tensors)
+    if code == FA2_BF16 and all(t.is_contiguous() for t in tensors):
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                 do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
         if Nk == N:
@@ -212,7 +228,7 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None
         args.append(lse.data_ptr())
         for t in (do, dq, dk, dv):
             args += [t.data_ptr(), _strides(t)]
-        st = load().fa2_bwd_strided(*args, B, H, N, Nk, d, *tail)
+        st = load().fa2_bwd_strided(*args, B, H, N, Nk, d, scale, int(bool(causal)), code, *ws)
     _check(st, "fa2_bwd")
     return dq, dk, dv
 

@@ -90,19 +90,28 @@ typedef struct fa2_strides {
     long long batch, head, row;
 } fa2_strides;
 
+/* Storage type of the 16-bit tensors of a "_strided" call (q, k, v, o, dout,
+ * dq, dk, dv share it; lse and the workspace stay fp32).  The other entry
+ * points take bfloat16.  Both run the same kernels with the matching 16-bit
+ * matrix instruction (v_mfma_f32_32x32x16_bf16 / _f16); P and dS are rounded
+ * to the storage type (nearest even) before their products. */
+typedef enum fa2_dtype { FA2_BF16 = 0, FA2_FP16 = 1 } fa2_dtype;
+
 /*
  * Forward pass on strided tensors: as fa2_fwd_qk, with the layout of q, k, v
- * and o given by sq, sk, sv, so (NULL: contiguous).  lse stays contiguous fp32
- * [B,H,Nq].  o and lse must not overlap any input.
+ * and o given by sq, sk, sv, so (NULL: contiguous) and their 16-bit storage
+ * type by dtype (fa2_dtype; anything else is FA2_ERR_INVALID_ARG).  lse stays
+ * contiguous fp32 [B,H,Nq].  o and lse must not overlap any input.
  */
 int fa2_fwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
                     const void* v, const fa2_strides* sv, void* o, const fa2_strides* so,
                     float* lse, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                    void* stream);
+                    int dtype, void* stream);
 
 /*
  * Backward pass on strided tensors: as fa2_bwd_qk, with the layout of every
- * bf16 tensor given by its fa2_strides (NULL: contiguous); lse is contiguous
+ * 16-bit tensor given by its fa2_strides (NULL: contiguous) and their storage
+ * type by dtype (fa2_dtype); lse is contiguous
  * fp32 [B,H,Nq]; workspace as for fa2_bwd_qk.  No output (dq, dk, dv, the
  * workspace) may overlap an input, and the workspace no output.  dq, dk and
  * dv may share one buffer (for instance the three head groups of a fused
@@ -114,7 +123,7 @@ int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const f
                     const float* lse, const void* dout, const fa2_strides* sdo, void* dq,
                     const fa2_strides* sdq, void* dk, const fa2_strides* sdk, void* dv,
                     const fa2_strides* sdv, int B, int H, int Nq, int Nk, int d, float scale,
-                    int causal, void* workspace, size_t workspace_bytes, void* stream);
+                    int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Forward pass with separate query and key lengths (see the top of this file

@@ -154,9 +154,9 @@ def test_strided_entry_points_reject(lib):
     dense = S(H * N * d, N * d, d)
     bshd = S(N * H * d, d, H * d)
 
-    def fwd_s(sq=dense, so=dense, o=P[3], q=P[0]):
+    def fwd_s(sq=dense, so=dense, o=P[3], q=P[0], dtype=0):
         return lib.fa2_fwd_strided(q, ctypes.byref(sq), P[1], None, P[2], None, o, ctypes.byref(so), P[4],
-                                   B, H, N, N, d, 0.1, 1, None)
+                                   B, H, N, N, d, 0.1, 1, dtype, None)
 
     assert fwd_s(sq=S(H * N * d, N * d, d + 4)) == INVALID        # row stride not a multiple of 8
     assert fwd_s(sq=S(-8, N * d, d)) == INVALID                   # negative stride
@@ -164,16 +164,19 @@ def test_strided_entry_points_reject(lib):
     assert fwd_s(so=S(H * N * d, d, d)) == INVALID                # output heads overlap rows
     assert fwd_s(o=P[0] + 2 * d * 3, so=bshd) == INVALID          # output inside q's span
     assert fwd_s(q=P[0] + 8) == INVALID                           # misaligned base
+    assert fwd_s(sq=S(H * N * d, N * d, d + 4), dtype=1) == INVALID
+    assert fwd_s(dtype=2) == INVALID                              # unknown 16-bit type
     assert fwd_s(sq=S(0, 0, 1 << 24)) == INVALID                  # rows beyond 2^30 elements
     # backward: an output inside an input, the workspace inside an output
     need = lib.fa2_bwd_workspace_bytes(B, H, N, d)
     args = [P[0], None, P[1], None, P[2], None, P[3], None, P[4], P[5], None,
             P[6], None, P[7], None, P[8], None]
-    assert lib.fa2_bwd_strided(*args, B, H, N, N, d, 0.1, 1, P[9], need - 1, None) == WORKSPACE
+    assert lib.fa2_bwd_strided(*args, B, H, N, N, d, 0.1, 1, 0, P[9], need - 1, None) == WORKSPACE
+    assert lib.fa2_bwd_strided(*args, B, H, N, N, d, 0.1, 1, 5, P[9], need, None) == INVALID
     bad = list(args)
     bad[13] = P[1] + 64                                          # dk inside k
-    assert lib.fa2_bwd_strided(*bad, B, H, N, N, d, 0.1, 1, P[9], need, None) == INVALID
-    assert lib.fa2_bwd_strided(*args, B, H, N, N, d, 0.1, 1, P[8] + 256, need, None) == INVALID
+    assert lib.fa2_bwd_strided(*bad, B, H, N, N, d, 0.1, 1, 1, P[9], need, None) == INVALID
+    assert lib.fa2_bwd_strided(*args, B, H, N, N, d, 0.1, 1, 0, P[8] + 256, need, None) == INVALID
 
 
 def test_workspace_size_query(lib):

@@ -26,8 +26,9 @@ DEV = "cuda:0"
 O_TOL, G_TOL = 1e-2, 2e-2
 
 
-def to_dev(bits, grad=False):
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+def to_dev(bits, grad=False, dtype="bf16"):
+    kind = torch.bfloat16 if dtype == "bf16" else torch.float16
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(kind)
     return t.requires_grad_(grad)
 
 
@@ -141,18 +142,19 @@ def test_strided_views_match_oracle(B, H, Nq, Nk, d, causal):
         assert rel(f64(t), r) <= G_TOL
 
 
-@pytest.mark.parametrize("B,S,H,d,causal", [(2, 150, 2, 80, True), (1, 257, 3, 128, False), (2, 64, 4, 64, True)])
-def test_qkvpacked_matches_oracle(B, S, H, d, causal):
-    arrs = gen.make_arrays(B, H, S, d, seed=6000 + S + d)
+@pytest.mark.parametrize("B,S,H,d,causal,dtype", [(2, 150, 2, 80, True, "bf16"), (1, 257, 3, 128, False, "bf16"),
+                                                   (2, 64, 4, 64, True, "bf16"), (2, 150, 2, 80, True, "fp16")])
+def test_qkvpacked_matches_oracle(B, S, H, d, causal, dtype):
+    arrs = gen.make_arrays(B, H, S, d, seed=6000 + S + d, dtype=dtype)
     qkv_bits = np.stack([arrs[n].transpose(0, 2, 1, 3) for n in ("q", "k", "v")], axis=2)  # [B, S, 3, H, d]
-    qkv = to_dev(qkv_bits, grad=True)
-    do = to_dev(np.ascontiguousarray(arrs["do"].transpose(0, 2, 1, 3)))                    # [B, S, H, d]
+    qkv = to_dev(qkv_bits, grad=True, dtype=dtype)
+    do = to_dev(np.ascontiguousarray(arrs["do"].transpose(0, 2, 1, 3)), dtype=dtype)       # [B, S, H, d]
     o = attention_qkvpacked(qkv, causal=causal)
     assert o.shape == (B, S, H, d) and o.is_contiguous()
     o.backward(do)
     torch.cuda.synchronize()
     scale = 1.0 / math.sqrt(d)
-    x = {n: oracle.bf16_bits_to_float64(arrs[n]) for n in ("q", "k", "v", "do")}
+    x = {n: oracle.bits_to_float64(arrs[n], dtype) for n in ("q", "k", "v", "do")}
     o_ref, _ = A.forward(x["q"], x["k"], x["v"], scale, causal)
     g_ref = A.backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
     assert float(np.max(np.abs(f64(o).transpose(0, 2, 1, 3) - o_ref))) <= O_TOL

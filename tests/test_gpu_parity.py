@@ -31,8 +31,9 @@ O_TOL, L_TOL, G_TOL = 1e-2, 1e-3, 2e-2
 DEV = "cuda:0"
 
 
-def to_dev(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+def to_dev(bits, dtype="bf16"):
+    kind = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(kind)
 
 
 def to_f64(t):
@@ -46,21 +47,21 @@ def frob_rel(got, ref):
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-3))
 
 
-def run_gpu(arrs, causal, scale):
-    q, k, v, do = (to_dev(arrs[n]) for n in ("q", "k", "v", "do"))
+def run_gpu(arrs, causal, scale, dtype="bf16"):
+    q, k, v, do = (to_dev(arrs[n], dtype) for n in ("q", "k", "v", "do"))
     o, lse = fa2.fwd(q, k, v, causal=causal, scale=scale)
     dq, dk, dv = fa2.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
     torch.cuda.synchronize()
     return {n: t for n, t in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, dq, dk, dv))}
 
 
-def decode(arrs):
-    return {n: oracle.bf16_bits_to_float64(arrs[n]) for n in ("q", "k", "v", "do")}
+def decode(arrs, dtype="bf16"):
+    return {n: oracle.bits_to_float64(arrs[n], dtype) for n in ("q", "k", "v", "do")}
 
 
-def assert_full_parity(arrs, causal, scale, label=""):
-    out = run_gpu(arrs, causal, scale)
-    x = decode(arrs)
+def assert_full_parity(arrs, causal, scale, label="", dtype="bf16"):
+    out = run_gpu(arrs, causal, scale, dtype)
+    x = decode(arrs, dtype)
     o_ref, l_ref = A.forward(x["q"], x["k"], x["v"], scale, causal)
     dq_ref, dk_ref, dv_ref = A.backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
     o, lse = to_f64(out["o"]), to_f64(out["lse"])
@@ -125,6 +126,47 @@ def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
     print(label, errs, flush=True)
     assert errs["O"] <= O_TOL and errs["L"] <= L_TOL, errs
     assert max(errs["dq"], errs["dk"], errs["dv"]) <= G_TOL, errs
+
+
+# float16 storage: the same kernels with the f16 matrix instruction, through the
+# strided entry points (contiguous, [B, N, H, d] views, Nq != Nk)
+@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(1, 1, 12), (2, 2, 200), (1, 1, 333)])
+def test_fp16_small_shapes(d, causal, B, H, N):
+    arrs = gen.make_arrays(B, H, N, d, seed=7000 + N + d, dtype="fp16")
+    out, _ = assert_full_parity(arrs, causal, 1.0 / math.sqrt(d), f"fp16 B{B} H{H} N{N} d{d} causal={causal}",
+                                dtype="fp16")
+    assert all(t.dtype == torch.float16 for n, t in out.items() if n != "lse")
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(1, 2, 77, 300, 128, True), (2, 2, 250, 100, 80, True),
+                                                 (1, 3, 130, 130, 64, False)])
+def test_fp16_views_and_lengths(B, H, Nq, Nk, d, causal):
+    arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=7100 + Nq + Nk, dtype="fp16")
+    q, k, v, do = (to_dev(arrs[n], "fp16") for n in ("q", "k", "v", "do"))
+    qs, vs = q.transpose(1, 2).contiguous().transpose(1, 2), v.transpose(1, 2).contiguous().transpose(1, 2)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa2.fwd(qs, k, vs, causal=causal, scale=scale)
+    dq, dk, dv = fa2.bwd(qs, k, vs, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    x = decode(arrs, "fp16")
+    o_ref, l_ref = A.forward(x["q"], x["k"], x["v"], scale, causal)
+    g_ref = A.backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    empty = np.isneginf(l_ref)
+    lse64 = to_f64(lse)
+    assert np.array_equal(np.isneginf(lse64), empty)
+    assert float(np.max(np.abs(to_f64(o) - o_ref))) <= O_TOL
+    if (~empty).any():
+        assert float(np.max(np.abs(lse64[~empty] - l_ref[~empty]))) <= L_TOL
+    for t, r in zip((dq, dk, dv), g_ref):
+        assert frob_rel(to_f64(t), r) <= G_TOL
+
+
+def test_mixed_16bit_types_rejected():
+    q = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        fa2.fwd(q, q.half(), q)
 
 
 def test_workload_c1_every_element():
