@@ -371,12 +371,13 @@ struct DqCfg {
   static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per K/V tile
+  static constexpr int BC = 64;                   // keys per K/V tile (32 or 64)
+  static constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
   static constexpr int TILE = RowTile<D>::elems(BC);
-  static constexpr int TTILE = TrTile<D, 64>::ELEMS;
+  static constexpr int TTILE = TrTile<D, BC>::ELEMS;
 };
 
 template <int D, bool CAUSAL, class E>
@@ -387,15 +388,15 @@ struct DqWave {
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
   int key_last;   // causal: last key this lane's query may see (q_lane + Nk - Nq)
-  LaneOffsets<D> off;
+  LaneOffsets<D, DqCfg<D>::BC> off;
 
   // kt, vt: row-major K and V tiles; ktt: transposed K tile.
   template <bool MASK>
   __device__ __forceinline__ void tile(const uint16_t* kt, const uint16_t* vt, const uint16_t* ktt,
                                        int key0, int Nk, float scale_log2) {
-    f32x16 sacc[2], pacc[2];
+    f32x16 sacc[C::KB], pacc[C::KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sacc[kb][i] = 0.f;
@@ -403,15 +404,15 @@ struct DqWave {
       }
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
-        const int o = off.row[s] + 2 * kb * LaneOffsets<D>::ROW16;
+        const int o = off.row[s] + 2 * kb * LaneOffsets<D, C::BC>::ROW16;
         sacc[kb] = E::mfma(lds_read16(kt + o), qf[s], sacc[kb]);
         pacc[kb] = E::mfma(lds_read16(vt + o), dof[s], pacc[kb]);
       }
     }
-    mfma_pipeline_hint<1, 4 * C::DK, 4 * C::DK, 6>();
-    uint32_t dsw[2][8];
+    mfma_pipeline_hint<1, 2 * C::KB * C::DK, 2 * C::KB * C::DK, 6>();
+    uint32_t dsw[C::KB][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -l2));
@@ -430,7 +431,7 @@ struct DqWave {
       const u32x4 b = acc_chunk(dsw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        dqacc[mb] = E::mfma(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D>::TR32), b,
+        dqacc[mb] = E::mfma(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D, C::BC>::TR32), b,
                                  dqacc[mb]);
     }
     mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
@@ -449,8 +450,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  tr_zero_pad<D>(kt_lds[0], tid, C::THREADS);
-  tr_zero_pad<D>(kt_lds[1], tid, C::THREADS);
+  tr_zero_pad<D, C::BC>(kt_lds[0], tid, C::THREADS);
+  tr_zero_pad<D, C::BC>(kt_lds[1], tid, C::THREADS);
   const int nrb = (Nq + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
   // K goes through registers (written row-major and transposed), V is copied
   // to LDS directly.
-  TrStage<D> kstage;
+  TrStage<D, C::BC> kstage;
   TileDma<D, C::BC, C::THREADS> vdma;
   kstage.init(tid, K.sr);
   vdma.init(tid, V.sr);

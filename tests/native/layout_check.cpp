@@ -127,27 +127,26 @@ void check_stage(int max_n, int R) {
   }
 }
 
-// Operand reads: row-major tiles of 64 rows are read at row[s] + 2*b*ROW16
-// (b = 32-row block 0..1, s = 16-feature chunk), 8 elements; transposed
-// tiles at tr + 16c + mb*TR32 (c = 16-token chunk 0..3, mb = 32-feature
-// block), 8 elements.  Each read must stay inside its tile and fetch the
+// Operand reads: row-major tiles of TOK rows are read at row[s] + 2*b*ROW16
+// (b = 32-row block, s = 16-feature chunk), 8 elements; transposed tiles at
+// tr + 16c + mb*TR32 (c = 16-token chunk, mb = 32-feature block), 8 elements.  Each read must stay inside its tile and fetch the
 // features / tokens the MFMA lane layout expects.
-template <int D>
+template <int D, int TOK = 64>
 void check_reads() {
-  using O = LaneOffsets<D, 64>;
+  using O = LaneOffsets<D, TOK>;
   using L = RowTile<D>;
-  using T = TrTile<D, 64>;
+  using T = TrTile<D, TOK>;
   for (int lane = 0; lane < 64; ++lane) {
     O o;
     o.init(lane);
     const int lr = lane & 31, lh = lane >> 5;
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TOK / 32; ++b)
       for (int s = 0; s < O::DK; ++s) {
         const int e = o.row[s] + 2 * b * O::ROW16;
-        CHECK(e >= 0 && e + 8 <= L::elems(64), "D=%d row read out of tile", D);
+        CHECK(e >= 0 && e + 8 <= L::elems(TOK), "D=%d row read out of tile", D);
         CHECK(e == L::elem(32 * b + lr, 16 * s + 8 * lh), "D=%d row read of lane %d b=%d s=%d", D, lane, b, s);
       }
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < TOK / 16; ++c)
       for (int mb = 0; mb < O::NDB; ++mb) {
         const int e = o.tr + 16 * c + mb * O::TR32;
         CHECK(e >= 0 && e + 8 <= T::ELEMS, "D=%d transposed read out of tile", D);
@@ -186,6 +185,15 @@ int main() {
   check_dma<80, 64, 512>(max_n, 88);
   check_stage<128, 64, 256>(max_n, 136);
   check_stage<80, 64, 256>(max_n, 88);
+  // 32-row tiles (the dQ kernel's key tile can be 32 keys for D = 64 and 128)
+  for (int mult : {1, 3}) {
+    check_dma<64, 32, 512>(max_n, 64 * mult);
+    check_dma<128, 32, 512>(max_n, 128 * mult);
+    check_stage<64, 32, 512>(max_n, 64 * mult);
+    check_stage<128, 32, 512>(max_n, 128 * mult);
+  }
+  check_reads<64, 32>();
+  check_reads<128, 32>();
   check_reads<64>();
   check_reads<80>();
   check_reads<96>();
