@@ -65,14 +65,14 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("0ba954ac8c11beaf", "c2", "bwd_dkdv"): 1359205533,
-    ("0ba954ac8c11beaf", "c2", "bwd_dq"): 770989685,
-    ("0ba954ac8c11beaf", "c2", "bwd_preprocess"): 138465620,
-    ("0ba954ac8c11beaf", "c2", "fwd"): 1166693803,
-    ("0ba954ac8c11beaf", "c4", "bwd_dkdv"): 869917203,
-    ("0ba954ac8c11beaf", "c4", "bwd_dq"): 773862746,
-    ("0ba954ac8c11beaf", "c4", "bwd_preprocess"): 138467476,
-    ("0ba954ac8c11beaf", "c4", "fwd"): 784457191,
+    ("9d5ea5d70b8ece77", "c2", "bwd_dkdv"): 1359233220,
+    ("9d5ea5d70b8ece77", "c2", "bwd_dq"): 771010052,
+    ("9d5ea5d70b8ece77", "c2", "bwd_preprocess"): 138472843,
+    ("9d5ea5d70b8ece77", "c2", "fwd"): 1163808843,
+    ("9d5ea5d70b8ece77", "c4", "bwd_dkdv"): 870085339,
+    ("9d5ea5d70b8ece77", "c4", "bwd_dq"): 768090853,
+    ("9d5ea5d70b8ece77", "c4", "bwd_preprocess"): 138474123,
+    ("9d5ea5d70b8ece77", "c4", "fwd"): 755478784,
 }
 
 

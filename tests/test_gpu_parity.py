@@ -106,7 +106,7 @@ def test_other_scales(scale):
 @pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 2, 1, 300, 128), (2, 1, 1, 64, 64), (1, 2, 77, 500, 64),
                                          (1, 1, 64, 1000, 128), (2, 2, 300, 130, 80),
                                          (1, 2, 513, 200, 128), (1, 1, 129, 257, 80),
-                                         (1, 2, 150, 270, 96),
+                                         (1, 2, 150, 270, 96), (1, 1, 1, 1, 64), (2, 1, 70, 1, 128),
                                          (1, 3, 200, 333, 128)])
 def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=3000 + Nq + Nk + d)
