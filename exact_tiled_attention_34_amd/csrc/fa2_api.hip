@@ -80,6 +80,10 @@ bool strided_view(const void* p, const fa2_strides* s, int B, int H, int N, int 
                   fa2::Strided* t, Span* sp) {
   if (!ptr_ok(p)) return false;
   *t = s ? fa2::Strided{p, s->batch, s->head, s->row} : fa2::contiguous(p, H, N, d);
+  // a dimension of extent 1 is never stepped over: its stride is ignored
+  if (B == 1) t->batch = 0;
+  if (H == 1) t->head = 0;
+  if (N == 1) t->row = 0;
   const long long st[3] = {t->batch, t->head, t->row};
   const long long ext[3] = {B, H, N};
   for (int i = 0; i < 3; ++i)

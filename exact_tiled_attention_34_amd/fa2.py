@@ -131,8 +131,10 @@ def _dtype_code(tensors):
 
 
 def _strides(t):
-    """fa2_strides of a [B, H, N, d] tensor (element strides), by reference."""
-    return ctypes.byref(Strides(t.stride(0), t.stride(1), t.stride(2)))
+    """fa2_strides of a [B, H, N, d] tensor (element strides), by reference.  A
+    dimension of size 1 is never stepped over, so its stride (which PyTorch may
+    report as any value) is passed as 0."""
+    return ctypes.byref(Strides(*(t.stride(i) if t.shape[i] > 1 else 0 for i in range(3))))
 
 
 def _check_f32(name, t, shape):

@@ -159,7 +159,7 @@ def test_strided_entry_points_reject(lib):
                                    B, H, N, N, d, 0.1, 1, dtype, None)
 
     assert fwd_s(sq=S(H * N * d, N * d, d + 4)) == INVALID        # row stride not a multiple of 8
-    assert fwd_s(sq=S(-8, N * d, d)) == INVALID                   # negative stride
+    assert fwd_s(sq=S(H * N * d, -8, d)) == INVALID               # negative stride
     assert fwd_s(so=S(H * N * d, N * d, d - 8)) == INVALID        # output rows overlap
     assert fwd_s(so=S(H * N * d, d, d)) == INVALID                # output heads overlap rows
     assert fwd_s(o=P[0] + 2 * d * 3, so=bshd) == INVALID          # output inside q's span

@@ -161,3 +161,16 @@ def test_qkvpacked_matches_oracle(B, S, H, d, causal, dtype):
     g = f64(qkv.grad)
     for j, r in enumerate(g_ref):
         assert rel(g[:, :, j].transpose(0, 2, 1, 3), r) <= G_TOL
+
+
+def test_strides_of_size_one_dimensions_are_ignored():
+    """PyTorch may report any stride for a dimension of size 1; such strides never matter."""
+    B, H, N, d = 1, 1, 90, 64
+    arrs = gen.make_arrays(B, H, N, d, seed=77)
+    q, k, v, do = (to_dev(arrs[n]) for n in ("q", "k", "v", "do"))
+    odd = [torch.as_strided(t, (B, H, N, d), (7, 3, d, 1)) for t in (q, k, v)]
+    assert not odd[0].is_contiguous() or odd[0].stride(0) == 7
+    o, lse = fa2.fwd(*odd, causal=True)
+    o_c, lse_c = fa2.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_c) and torch.equal(lse, lse_c)
