@@ -65,14 +65,14 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("9d5ea5d70b8ece77", "c2", "bwd_dkdv"): 1359233220,
-    ("9d5ea5d70b8ece77", "c2", "bwd_dq"): 771010052,
-    ("9d5ea5d70b8ece77", "c2", "bwd_preprocess"): 138472843,
-    ("9d5ea5d70b8ece77", "c2", "fwd"): 1163808843,
-    ("9d5ea5d70b8ece77", "c4", "bwd_dkdv"): 870085339,
-    ("9d5ea5d70b8ece77", "c4", "bwd_dq"): 768090853,
-    ("9d5ea5d70b8ece77", "c4", "bwd_preprocess"): 138474123,
-    ("9d5ea5d70b8ece77", "c4", "fwd"): 755478784,
+    ("b309c1520eb39506", "c2", "bwd_dkdv"): 1359254907,
+    ("b309c1520eb39506", "c2", "bwd_dq"): 771025799,
+    ("b309c1520eb39506", "c2", "bwd_preprocess"): 138473064,
+    ("b309c1520eb39506", "c2", "fwd"): 1164590249,
+    ("b309c1520eb39506", "c4", "bwd_dkdv"): 870594177,
+    ("b309c1520eb39506", "c4", "bwd_dq"): 776969371,
+    ("b309c1520eb39506", "c4", "bwd_preprocess"): 138474600,
+    ("b309c1520eb39506", "c4", "fwd"): 775939090,
 }
 
 
