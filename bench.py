@@ -320,6 +320,14 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel_source": src}
 
+    # compulsory HBM bytes per launch (every input read once, every output written
+    # once; bf16 tensors, fp32 row arrays padded to Npad rows) and the rate they imply
+    t16 = 2 * B * H * N * d
+    rows, prow = 4 * B * H * N, 4 * B * H * fa2.bwd_rows_padded(N)
+    compulsory = {"fwd": 4 * t16 + rows, "bwd_preprocess": 2 * t16 + rows + 2 * prow,
+                  "bwd_dkdv": 6 * t16 + 2 * prow, "bwd_dq": 5 * t16 + 2 * prow}
+    hbm_gbs = {n: round(compulsory[n] / (kern_ms[n] * 1e-3) / 1e9, 1) for n in names}
+
     props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -330,6 +338,7 @@ def main():
                    "scale": w.scale, "parallelism": "single GPU"},
         "phases": {k2: round(v2, 2) for k2, v2 in phases.items()},
         "kernel_ms": {k2: round(v2, 4) for k2, v2 in kern_ms.items()},
+        "compulsory_hbm_gbs": hbm_gbs,
         "roofline": roofline,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
