@@ -238,7 +238,7 @@ def main():
             sys.exit(f"{exe} is missing: build with `python -m exact_tiled_attention_34_amd.build`")
         sys.exit(subprocess.run([exe]).returncode)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads would shard "
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads would shard "
               "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.gpt_block:
