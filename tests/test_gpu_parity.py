@@ -141,7 +141,8 @@ def test_fp16_small_shapes(d, causal, B, H, N):
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(1, 2, 77, 300, 128, True), (2, 2, 250, 100, 80, True),
-                                                 (1, 3, 130, 130, 64, False)])
+                                                 (1, 3, 130, 130, 64, False), (1, 2, 1500, 2100, 128, True),
+                                                 (2, 1, 1024, 1024, 96, False)])
 def test_fp16_views_and_lengths(B, H, Nq, Nk, d, causal):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=7100 + Nq + Nk, dtype="fp16")
     q, k, v, do = (to_dev(arrs[n], "fp16") for n in ("q", "k", "v", "do"))
@@ -406,3 +407,47 @@ def test_phases_compose_to_bwd(d, causal, N):
     assert pad_delta == 0.0 and pad_inf
     rel = float(((lse2[:, :, :N] - lse * math.log2(math.e)).abs() / lse.abs().clamp_min(1e-3)).max())
     assert rel <= 1e-6, rel
+
+
+@pytest.mark.parametrize("key", ["c2", "c4"])
+def test_workload_full_size_fp16(key):
+    """The full-size workloads with float16 storage: one whole head element by element (c2), sampled
+    rows and columns of the last head, and the any-size properties on every head."""
+    w = gen.WORKLOADS[key]
+    arrs = gen.make_arrays(w.B, w.H, w.N, w.d, seed=1, sigma=w.sigma, spike=w.spike, dtype="fp16")
+    print(f"workload {key} fp16: {w.name}", flush=True)
+    out = run_gpu(arrs, w.causal, w.scale, dtype="fp16")
+    for n, t in out.items():
+        assert bool(torch.isfinite(t.float()).all()), f"non-finite values in {n}"
+    B, H, N = w.B, w.H, w.N
+    dec = lambda a: oracle.fp16_bits_to_float64(a)  # noqa: E731
+    if key == "c2":
+        x = {n: dec(arrs[n][0, 0]) for n in ("q", "k", "v", "do")}
+        o_ref, l_ref = A.forward_head(x["q"], x["k"], x["v"], w.scale, w.causal)
+        g_ref = A.backward_head(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal)
+        errs = {"O": float(np.max(np.abs(to_f64(out["o"][0, 0]) - o_ref))),
+                "L": float(np.max(np.abs(to_f64(out["lse"][0, 0]) - l_ref)))}
+        for n, r in zip(("dq", "dk", "dv"), g_ref):
+            errs[n] = frob_rel(to_f64(out[n][0, 0]), r)
+        print(f"{key} fp16 whole head (0,0):", errs, flush=True)
+        assert errs["O"] <= O_TOL and errs["L"] <= L_TOL, errs
+        assert max(errs["dq"], errs["dk"], errs["dv"]) <= G_TOL, errs
+    b, h = B - 1, H - 1
+    x = {n: dec(arrs[n][b, h]) for n in ("q", "k", "v", "do")}
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 1, N - 1], rng.integers(0, N, 13)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 14)]))
+    o_ref, l_ref = A.forward_rows(x["q"], x["k"], x["v"], w.scale, w.causal, rows)
+    stats = A.row_stats(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal)
+    dk_ref, dv_ref = A.backward_cols(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal, cols, stats=stats)
+    ri, ci = torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)
+    errs = {"O": float(np.max(np.abs(to_f64(out["o"][b, h, ri]) - o_ref))),
+            "L": float(np.max(np.abs(to_f64(out["lse"][b, h, ri]) - l_ref))),
+            "dK_cols": frob_rel(to_f64(out["dk"][b, h, ci]), dk_ref),
+            "dV_cols": frob_rel(to_f64(out["dv"][b, h, ci]), dv_ref)}
+    print(f"{key} fp16 sampled head ({b},{h}):", errs, flush=True)
+    assert errs["O"] <= O_TOL and errs["L"] <= L_TOL, errs
+    assert errs["dK_cols"] <= G_TOL and errs["dV_cols"] <= G_TOL, errs
+    dv_sum = out["dv"].float().sum(dim=2)
+    do_sum = to_dev(arrs["do"], "fp16").float().sum(dim=2)
+    assert float((dv_sum - do_sum).norm() / do_sum.norm()) <= G_TOL
