@@ -86,7 +86,7 @@ struct DkdvCfg {
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
   static constexpr int NQB = BQ / 32;
-  static constexpr int TILE = RowTile<D>::elems(BQ);
+  static constexpr int TILE = RowTileW<D>::elems(BQ);
   static constexpr int TTILE = TrTile<D, 64>::ELEMS;
   static_assert(BQ == 64, "transposed tiles hold 64 tokens");
 };
@@ -97,7 +97,7 @@ struct DkdvWave {
   u32x4 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
-  LaneOffsets<D> off;
+  LaneOffsets<D, 64, RowTileW<D>> off;
 
   // One 64-query step.  qt, dot: row-major Q and dO tiles; qtt, dott: their
   // transposes; l2s, dls: the step's L log2 e and delta; kq0: the last key
@@ -124,7 +124,7 @@ struct DkdvWave {
     u32x4 ra[NALL], rb[NALL];
     auto fetch = [&](int t) {
       if (t < NS) {
-        const int o = off.row[t % C::DK] + 2 * (t / C::DK) * LaneOffsets<D>::ROW16;
+        const int o = off.rd(t % C::DK, t / C::DK);
         ra[t] = lds_read16(qt + o);
         rb[t] = lds_read16(dot + o);
       } else {
@@ -273,9 +273,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   };
   auto store_step = [&](int buf) {
     qstage.store(qt_lds[buf]);
-    qstage.store_rows(q_lds[buf]);
+    qstage.template store_rows<RowTileW<D>>(q_lds[buf]);
     dostage.store(dot_lds[buf]);
-    dostage.store_rows(do_lds[buf]);
+    dostage.template store_rows<RowTileW<D>>(do_lds[buf]);
   };
   if (i_begin < n_qblk) {
     load_ld(ld_lds[0], i_begin * C::BQ);
@@ -404,7 +404,7 @@ struct DqWave {
       }
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
-        const int o = off.row[s] + 2 * kb * LaneOffsets<D, C::BC>::ROW16;
+        const int o = off.rd(s, kb);
         sacc[kb] = E::mfma(lds_read16(kt + o), qf[s], sacc[kb]);
         pacc[kb] = E::mfma(lds_read16(vt + o), dof[s], pacc[kb]);
       }
@@ -482,7 +482,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
   // K goes through registers (written row-major and transposed), V is copied
-  // to LDS directly.
+  // to LDS directly; both row-major tiles are RowTiles (one set of lane
+  // offsets reads them).
   TrStage<D, C::BC> kstage;
   TileDma<D, C::BC, C::THREADS> vdma;
   kstage.init(tid, K.sr);
@@ -527,11 +528,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
     }
     kstage.store(kt_lds[BUF ^ 1]);
-    kstage.store_rows(k_lds[BUF ^ 1]);
+    kstage.template store_rows<RowTile<D>>(k_lds[BUF ^ 1]);
   };
   if (n_tiles > 0) {
     kstage.store(kt_lds[0]);
-    kstage.store_rows(k_lds[0]);
+    kstage.template store_rows<RowTile<D>>(k_lds[0]);
   }
   for (int j = 0; j < n_tiles; j += 2) {
     iteration(std::integral_constant<int, 0>{}, j);

@@ -202,7 +202,7 @@ struct TileDma {
 // elements apart: begin() and the four load_k() issue the global loads (all
 // at once with load(), or spread over the compute that hides them), store()
 // (once the values are needed, typically after the current tile's compute)
-// writes the transposed tile, store_rows() the same tokens as a RowTile.
+// writes the transposed tile, store_rows<L>() the same tokens as a row-major tile.
 // Rows past n_rows are clamped to the last row.
 template <int D, int TOK = 64>
 struct TrStage {
@@ -247,13 +247,16 @@ struct TrStage {
       *reinterpret_cast<u32x2*>(dst + e * TrTile<D, TOK>::ROW) = out;
     }
   }
-  // The same tokens as rows 4g..4g+3 of a RowTile (the pad slot of a padded row is
-  // left as it is: no operand read reaches it).
+  // The same tokens as rows 4g..4g+3 of a row-major tile of layout L
+  // (RowTileW: conflict-free stores; RowTile: the layout of a tile that is
+  // read together with a DMA-filled one).  Pad slots are left as they are: no
+  // operand read reaches them.
+  template <class L>
   __device__ __forceinline__ void store_rows(uint16_t* tile) const {
     if (!act) return;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<u32x4*>(tile + RowTile<D>::elem(4 * g + k, 8 * c)) = r[k];
+      *reinterpret_cast<u32x4*>(tile + L::elem(4 * g + k, 8 * c)) = r[k];
   }
 };
 

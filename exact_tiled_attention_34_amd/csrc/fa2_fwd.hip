@@ -75,7 +75,7 @@ struct FwdWave {
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < C::DK; ++s)
-        sacc[kb] = E::mfma(lds_read16(kt + off.row[s] + 2 * kb * LaneOffsets<D, FwdCfg<D>::BC>::ROW16), qf[s],
+        sacc[kb] = E::mfma(lds_read16(kt + off.rd(s, kb)), qf[s],
                                 sacc[kb]);
     }
     mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, 6>();

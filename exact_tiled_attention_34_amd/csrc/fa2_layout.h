@@ -63,6 +63,53 @@ struct RowTile {
   }
   // bf16 elements to reserve for a tile.
   static constexpr int elems(int rows) { return rows * SLOTS * 8; }
+  // Row lr + 32 b, features 16 s + 8 h: the lane's block-0 offset for step
+  // perm(s, b) (= s: the permutation repeats every 16 rows) plus block(b).
+  static constexpr int perm(int s, int) { return s; }
+  static constexpr int block(int b) { return b * 32 * SLOTS * 8; }
+};
+
+// ---------------------------------------------------------------------------
+// Row-major tiles written from registers in 4-row groups.
+//
+// A register stage (StagePlan below) writes one chunk of rows 4g + k for the
+// 16 values of g in one store pass: under the RowTile permutation, which
+// depends on row % 16 only, those 16 rows share 4 chunk positions (a 4-way
+// bank conflict on every write).  These tiles keep the read pattern of a
+// RowTile (16 consecutive rows of one chunk on 16 distinct 4-bank groups) and
+// also spread rows 4 apart:
+//   D = 128:     the XOR key also takes rows 16..63 of each 64-row period
+//                into account (row bits 4-5 flip key bits 2-3);
+//   D = 64:      a spare slot after every 4 rows, and row bit 1 flips chunk
+//                bit 2;
+//   D = 80, 96:  the RowTile row padding plus a spare slot after every 16 rows.
+// Lane offsets computed for rows 0..31 serve every 32-row block: for D = 128
+// an odd block flips chunk bit 3 (feature step s ^ 4 of the same lane),
+// otherwise a block adds a constant.
+// ---------------------------------------------------------------------------
+template <int D>
+struct RowTileW {
+  static constexpr int CH = D / 8;
+  static constexpr bool PADDED = (CH & (CH - 1)) != 0;
+  static constexpr int SLOTS = PADDED ? CH + 1 : CH;
+  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16), "unsupported head dim");
+  // 16-byte slots per 32 rows
+  static constexpr int SLOTS32 = PADDED ? 32 * SLOTS + 2 : CH == 16 ? 512 : 32 * 8 + 8;
+
+  static FA2_HD int slot(int row, int chunk) {
+    if constexpr (PADDED) {
+      return row * SLOTS + (row >> 4) + chunk;
+    } else if constexpr (CH == 16) {
+      return row * 16 + (chunk ^ ((4 * ((row & 3) ^ ((row >> 4) & 3))) | ((row >> 2) & 3)));
+    } else {
+      return row * 8 + (row >> 2) + (chunk ^ (4 * ((row >> 1) & 1)));
+    }
+  }
+  static FA2_HD int elem(int row, int col) { return slot(row, col >> 3) * 8 + (col & 7); }
+  // bf16 elements to reserve for a tile of `rows` rows (a multiple of 32).
+  static constexpr int elems(int rows) { return rows / 32 * SLOTS32 * 8; }
+  static constexpr int perm(int s, int b) { return CH == 16 ? (s ^ (4 * (b & 1))) : s; }
+  static constexpr int block(int b) { return b * SLOTS32 * 8; }
 };
 
 // ---------------------------------------------------------------------------
@@ -185,24 +232,25 @@ struct StagePlan {
 };
 
 // Per-lane LDS element offsets of the two operand reads, computed once per
-// kernel.  The chunk permutation of a RowTile depends only on row % 16, so
-// moving by whole 16-row groups (32-row operand blocks, 16-token chunks) adds
-// a compile-time constant: every read in the hot loops is one precomputed
+// kernel for the lane's row (or feature row) in the first 32-row block; the
+// reads of other blocks and chunks (L::perm, L::block, TR32) differ by
+// compile-time constants: every read in the hot loops is one precomputed
 // register plus an immediate offset.
-template <int D, int TOK = 64>
+template <int D, int TOK = 64, class L = RowTile<D>>
 struct LaneOffsets {
   static constexpr int DK = D / 16;
   static constexpr int NDB = (D + 31) / 32;
-  static constexpr int ROW16 = 16 * RowTile<D>::SLOTS * 8;   // elements per 16 rows
   static constexpr int TR32 = 32 * TrTile<D, TOK>::ROW;     // elements per 32 feature rows
   int row[DK];   // row-major tile: features 16 s + 8 h .. +7 of row lane % 32
   int tr;        // transposed tile: tokens {4h..4h+3, 8+4h..8+4h+3} of feature row lane % 32
   FA2_HD void init(int lane) {
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < DK; ++s) row[s] = RowTile<D>::elem(lr, s * 16 + 8 * lh);
+    for (int s = 0; s < DK; ++s) row[s] = L::elem(lr, s * 16 + 8 * lh);
     tr = lr * TrTile<D, TOK>::ROW + 8 * lh;   // + 16 c (token chunk) + TR32 mb (feature block)
   }
+  // row-major read of 32-row block b, feature step s
+  FA2_HD int rd(int s, int b) const { return row[L::perm(s, b)] + L::block(b); }
 };
 
 }  // namespace fa2

@@ -3,10 +3,14 @@
 // small cases, every global address a tile copy or register stage computes
 // must lie inside its tensor and fetch the chunk the LDS layout assigns to
 // the slot it lands in; every slot of a tile must be written exactly once;
-// every MFMA operand read must stay inside its LDS tile.  Prints "ok" and
-// exits 0, or prints the first violation and exits 1.
+// every MFMA operand read must stay inside its LDS tile.  16-byte LDS
+// accesses are also checked for bank conflicts, taking 16 lanes per cycle
+// (64 banks of 4 bytes: 16 groups of 4 banks): every group of 16 lanes of a
+// register-stage row store or an operand read must reach 16 distinct groups.
+// Prints "ok" and exits 0, or prints the first violation and exits 1.
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 #include <vector>
 
 #include "fa2_layout.h"
@@ -73,11 +77,12 @@ void check_dma(int max_n, int R) {
   }
 }
 
-template <int D, int TOK, int THREADS>
+// L: the row-major layout the stage's row stores write (RowTileW for the
+// dK/dV pass's Q and dO tiles, RowTile for the dQ pass's K tile).
+template <int D, int TOK, int THREADS, class L>
 void check_stage(int max_n, int R) {
   using P = StagePlan<D, TOK>;
   using T = TrTile<D, TOK>;
-  using L = RowTile<D>;
   static_assert(P::THREADS_USED <= THREADS, "stage needs more threads than the workgroup has");
   const long row_bytes = 2L * R;
   for (int n = 1; n <= max_n; ++n) {
@@ -99,7 +104,7 @@ void check_stage(int max_n, int R) {
           CHECK(addr / row_bytes == want && (addr % row_bytes) / 16 == ch, "D=%d n=%d tid=%d k=%d row %ld want %d",
                 D, n, tid, k, addr / row_bytes, want);
           cover[(4 * g + k) * P::CH + ch]++;
-          // store_rows: 16 bytes at RowTile elem(4g + k, 8ch)
+          // store_rows: 16 bytes at RowTileW elem(4g + k, 8ch)
           const int re = L::elem(4 * g + k, 8 * ch);
           CHECK(re >= 0 && re + 8 <= L::elems(TOK), "D=%d row store out of tile", D);
           for (int e = 0; e < 8 && re >= 0 && re + 8 <= L::elems(TOK); ++e) row_written[re + e]++;
@@ -125,24 +130,44 @@ void check_stage(int max_n, int R) {
                 row_written[L::elem(r, c)]);
     }
   }
+  // RowTileW row stores: store k of 16 consecutive active threads reaches 16
+  // distinct bank groups
+  for (int t0 = 0; std::is_same<L, RowTileW<D>>::value && t0 < P::THREADS_USED; t0 += 16)
+    for (int k = 0; k < 4; ++k) {
+      int seen[16] = {0};
+      for (int tid = t0; tid < t0 + 16; ++tid) seen[(L::elem(4 * P::grp(tid) + k, 8 * P::chunk(tid)) / 8) % 16]++;
+      for (int q = 0; q < 16; ++q)
+        CHECK(seen[q] <= 1, "D=%d TOK=%d row store threads %d.. k=%d: bank group %d hit %d times", D, TOK, t0, k, q,
+              seen[q]);
+    }
 }
 
 // Operand reads: row-major tiles of TOK rows are read at row[s] + 2*b*ROW16
 // (b = 32-row block, s = 16-feature chunk), 8 elements; transposed tiles at
 // tr + 16c + mb*TR32 (c = 16-token chunk, mb = 32-feature block), 8 elements.  Each read must stay inside its tile and fetch the
 // features / tokens the MFMA lane layout expects.
-template <int D, int TOK = 64>
+template <int D, int TOK = 64, class L = RowTile<D>>
 void check_reads() {
-  using O = LaneOffsets<D, TOK>;
-  using L = RowTile<D>;
+  using O = LaneOffsets<D, TOK, L>;
   using T = TrTile<D, TOK>;
+  O lanes[64];
+  for (int lane = 0; lane < 64; ++lane) lanes[lane].init(lane);
+  // row-major reads: bank groups of each 16 lanes
+  for (int b = 0; b < TOK / 32; ++b)
+    for (int s = 0; s < O::DK; ++s)
+      for (int l0 = 0; l0 < 64; l0 += 16) {
+        int seen[16] = {0};
+        for (int lane = l0; lane < l0 + 16; ++lane) seen[(lanes[lane].rd(s, b) / 8) % 16]++;
+        for (int q = 0; q < 16; ++q)
+          CHECK(seen[q] <= 1, "D=%d TOK=%d row read b=%d s=%d lanes %d..: bank group %d hit %d times", D, TOK, b,
+                s, l0, q, seen[q]);
+      }
   for (int lane = 0; lane < 64; ++lane) {
-    O o;
-    o.init(lane);
+    const O& o = lanes[lane];
     const int lr = lane & 31, lh = lane >> 5;
     for (int b = 0; b < TOK / 32; ++b)
       for (int s = 0; s < O::DK; ++s) {
-        const int e = o.row[s] + 2 * b * O::ROW16;
+        const int e = o.rd(s, b);
         CHECK(e >= 0 && e + 8 <= L::elems(TOK), "D=%d row read out of tile", D);
         CHECK(e == L::elem(32 * b + lr, 16 * s + 8 * lh), "D=%d row read of lane %d b=%d s=%d", D, lane, b, s);
       }
@@ -172,25 +197,25 @@ int main() {
     check_dma<80, 64, 512>(max_n, 80 * mult);
     check_dma<96, 64, 512>(max_n, 96 * mult);
     check_dma<128, 64, 512>(max_n, 128 * mult);
-    check_stage<64, 64, 256>(max_n, 64 * mult);
-    check_stage<80, 64, 256>(max_n, 80 * mult);
-    check_stage<96, 64, 256>(max_n, 96 * mult);
-    check_stage<128, 64, 256>(max_n, 128 * mult);
-    check_stage<64, 64, 512>(max_n, 64 * mult);
-    check_stage<80, 64, 512>(max_n, 80 * mult);
-    check_stage<96, 64, 512>(max_n, 96 * mult);
-    check_stage<128, 64, 512>(max_n, 128 * mult);
+    check_stage<64, 64, 256, RowTileW<64>>(max_n, 64 * mult);
+    check_stage<80, 64, 256, RowTileW<80>>(max_n, 80 * mult);
+    check_stage<96, 64, 256, RowTileW<96>>(max_n, 96 * mult);
+    check_stage<128, 64, 256, RowTileW<128>>(max_n, 128 * mult);
+    check_stage<64, 64, 512, RowTile<64>>(max_n, 64 * mult);
+    check_stage<80, 64, 512, RowTile<80>>(max_n, 80 * mult);
+    check_stage<96, 64, 512, RowTile<96>>(max_n, 96 * mult);
+    check_stage<128, 64, 512, RowTile<128>>(max_n, 128 * mult);
   }
   check_dma<128, 64, 256>(max_n, 136);
   check_dma<80, 64, 512>(max_n, 88);
-  check_stage<128, 64, 256>(max_n, 136);
-  check_stage<80, 64, 256>(max_n, 88);
+  check_stage<128, 64, 256, RowTileW<128>>(max_n, 136);
+  check_stage<80, 64, 256, RowTileW<80>>(max_n, 88);
   // 32-row tiles (the dQ kernel's key tile can be 32 keys for D = 64 and 128)
   for (int mult : {1, 3}) {
     check_dma<64, 32, 512>(max_n, 64 * mult);
     check_dma<128, 32, 512>(max_n, 128 * mult);
-    check_stage<64, 32, 512>(max_n, 64 * mult);
-    check_stage<128, 32, 512>(max_n, 128 * mult);
+    check_stage<64, 32, 512, RowTile<64>>(max_n, 64 * mult);
+    check_stage<128, 32, 512, RowTile<128>>(max_n, 128 * mult);
   }
   check_reads<64, 32>();
   check_reads<128, 32>();
@@ -198,6 +223,10 @@ int main() {
   check_reads<80>();
   check_reads<96>();
   check_reads<128>();
+  check_reads<64, 64, RowTileW<64>>();
+  check_reads<80, 64, RowTileW<80>>();
+  check_reads<96, 64, RowTileW<96>>();
+  check_reads<128, 64, RowTileW<128>>();
   if (failures) {
     std::printf("%d violations\n", failures);
     return 1;
