@@ -14,6 +14,13 @@ Recipe (every workload):
     by 8 before rounding (a power of two, so exact), widening the score range
     the softmax must handle.
 
+Tensors too large to draw on the host (the maximum-size case, up to 2^31
+elements each) are drawn on the GPU instead (``make_device_tensors``):
+``torch.Generator`` seeded with ``seed``; Q, K, V, dO in that order, each batch
+index b in turn, ``torch.randn((H, N, d), float32)`` converted to bfloat16 by
+torch's round-to-nearest-even.  The oracle takes the bit patterns of the heads
+it checks from those tensors.
+
 Workload shapes follow the attention benchmark sweeps on the "FlashAttention-2:
 Faster Attention with Better Parallelism and Work Partitioning" page (Figures
 4-7: head dimension 64 / 128, causal and non-causal, sequence lengths up to
@@ -121,6 +128,21 @@ def make_arrays_qk(B, H, Nq, Nk, d, seed=0, dtype="bf16"):
     for name, n in (("q", Nq), ("k", Nk), ("v", Nk), ("do", Nq)):
         out[name] = _rounder(dtype)(rng.standard_normal((B, H, n, d), dtype=np.float32))
     out["spike_rows"] = None
+    return out
+
+
+def make_device_tensors(B, H, N, d, seed=0, device="cuda:0"):
+    """Q, K, V, dO as bf16 torch tensors [B,H,N,d] drawn on `device` (N(0,1) draws)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v", "do"):
+        t = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            t[b] = torch.randn((H, N, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+        out[name] = t
     return out
 
 

@@ -409,6 +409,64 @@ def test_phases_compose_to_bwd(d, causal, N):
     assert rel <= 1e-6, rel
 
 
+def head_bits(t, b, h):
+    """Exact uint16 bit patterns of head (b, h) of a 16-bit device tensor."""
+    return t[b, h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_maximum_element_count():
+    """The largest tensors the ABI accepts: B*H*N*d just under 2^31 elements (4 GiB per
+    bf16 tensor, so byte offsets pass 2^31), a ragged N, causal.  Sampled rows and
+    columns of the first, a middle and the last head against the oracle; properties
+    that hold at any size on every head."""
+    B, H, N, d = 8, 128, 16383, 128
+    assert B * H * N * d < 2 ** 31 and 2 * B * H * N * d > 2 ** 31 + 2 ** 30
+    causal, scale = True, 1.0 / math.sqrt(d)
+    print(f"maximum size: B={B} H={H} N={N} d={d} causal", flush=True)
+    x = gen.make_device_tensors(B, H, N, d, seed=7, device=DEV)
+    o, lse = fa2.fwd(x["q"], x["k"], x["v"], causal=causal, scale=scale)
+    dq, dk, dv = fa2.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), f"non-finite values in {name}"
+
+    rng = np.random.default_rng(5)
+    for b, h, with_cols in [(0, 0, True), (3, 77, False), (B - 1, H - 1, True)]:
+        xh = {n: oracle.bf16_bits_to_float64(head_bits(x[n], b, h)) for n in ("q", "k", "v", "do")}
+        rows = np.unique(np.concatenate([[0, 1, N - 1], rng.integers(0, N, 13)]))
+        o_ref, l_ref = A.forward_rows(xh["q"], xh["k"], xh["v"], scale, causal, rows)
+        dq_ref = A.backward_rows(xh["q"], xh["k"], xh["v"], xh["do"], scale, causal, rows)
+        ri = torch.as_tensor(rows, device=DEV)
+        errs = {
+            "O": float(np.max(np.abs(to_f64(o[b, h, ri]) - o_ref))),
+            "L": float(np.max(np.abs(to_f64(lse[b, h, ri]) - l_ref))),
+            "dQ_rows": frob_rel(to_f64(dq[b, h, ri]), dq_ref),
+        }
+        if with_cols:
+            cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 14)]))
+            stats = A.row_stats(xh["q"], xh["k"], xh["v"], xh["do"], scale, causal)
+            dk_ref, dv_ref = A.backward_cols(xh["q"], xh["k"], xh["v"], xh["do"], scale, causal, cols,
+                                             stats=stats)
+            ci = torch.as_tensor(cols, device=DEV)
+            errs["dK_cols"] = frob_rel(to_f64(dk[b, h, ci]), dk_ref)
+            errs["dV_cols"] = frob_rel(to_f64(dv[b, h, ci]), dv_ref)
+        print(f"maximum size, head ({b},{h}):", errs, flush=True)
+        assert errs["O"] <= O_TOL and errs["L"] <= L_TOL, errs
+        assert all(v <= G_TOL for k, v in errs.items() if k not in ("O", "L")), errs
+
+    # every head: O inside the hull of V; rows of P sum to one (sum_j dV_j = sum_i dO_i);
+    # sum_j dK_j = 0
+    for b in range(B):
+        o_g, v_g = o[b].float(), x["v"][b].float()
+        assert bool(((o_g >= v_g.amin(dim=1, keepdim=True) - 1e-2)
+                     & (o_g <= v_g.amax(dim=1, keepdim=True) + 1e-2)).all()), b
+        dv_sum, do_sum = dv[b].float().sum(dim=1), x["do"][b].float().sum(dim=1)
+        assert float((dv_sum - do_sum).norm() / do_sum.norm()) <= G_TOL, b
+        dk_b = dk[b].float()
+        assert float(dk_b.sum(dim=1).norm() / dk_b.norm(dim=(1, 2)).norm()) <= G_TOL, b
+        del o_g, v_g, dk_b
+
+
 @pytest.mark.parametrize("key", ["c2", "c4"])
 def test_workload_full_size_fp16(key):
     """The full-size workloads with float16 storage: one whole head element by element (c2), sampled
