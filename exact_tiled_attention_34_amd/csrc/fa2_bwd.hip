@@ -14,9 +14,9 @@
 //                 S  = Q K^T          P  = 2^(c S - L log2 e),  c = scale log2 e
 //                 dP = dO V^T         dS = P (dP - delta)
 //                 dV^T += dO^T P      dK^T += Q^T dS
-//               P and dS feed their MFMAs straight from registers; Q and dO are
-//               in LDS twice per step, row-major (loaded global -> LDS directly)
-//               and transposed (staged through registers).
+//               P and dS feed their MFMAs straight from registers; Q and dO go
+//               through registers once per step and are written to LDS twice,
+//               row-major and transposed.
 //   dq          one workgroup of 8 wavefronts per (256-query row block, batch*head),
 //               shaped like the forward: Q and dO stay in registers, K/V tiles (and a
 //               transposed copy of K) stream through LDS:
@@ -390,10 +390,13 @@ struct DqWave {
   int key_last;   // causal: last key this lane's query may see (q_lane + Nk - Nq)
   LaneOffsets<D, DqCfg<D>::BC> off;
 
-  // kt, vt: row-major K and V tiles; ktt: transposed K tile.
-  template <bool MASK>
-  __device__ __forceinline__ void tile(const uint16_t* kt, const uint16_t* vt, const uint16_t* ktt,
-                                       int key0, int Nk, float scale_log2) {
+  // kt, vt: row-major K and V tiles; ktt: transposed K tile.  mask: the tile
+  // may hold keys past the end or above the diagonal for some of this wave's
+  // rows.  It is a run-time branch that only sets such scores to -inf (so P
+  // = 0): one tile body for every tile, so the dQ accumulators keep one
+  // register assignment through the loop.
+  __device__ __forceinline__ void tile(bool mask, const uint16_t* kt, const uint16_t* vt,
+                                       const uint16_t* ktt, int key0, int Nk, float scale_log2) {
     f32x16 sacc[C::KB], pacc[C::KB];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
@@ -410,16 +413,21 @@ struct DqWave {
       }
     }
     mfma_pipeline_hint<1, 2 * C::KB * C::DK, 2 * C::KB * C::DK, 6>();
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+          if (key >= Nk || (CAUSAL && key > key_last)) sacc[kb][i] = -INFINITY;
+        }
+    }
     uint32_t dsw[C::KB][8];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -l2));
-        if (MASK) {
-          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= Nk || (CAUSAL && key > key_last)) p = 0.f;
-        }
+        const float p = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -l2));
         pacc[kb][i] = p * (pacc[kb][i] - dl);
       }
 #pragma unroll
@@ -522,11 +530,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     // itself into the idle buffers), so its registers never live across tiles.
     kstage.load(Kh, (more ? j + 1 : j) * C::BC, Nk);
     const int key0 = j * C::BC;
-    if (j < n_full) {
-      w.template tile<false>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
-    } else if (!CAUSAL || key0 <= w.q_wave + 31 + koff) {
-      w.template tile<true>(k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
-    }
+    // tiles from n_full on are masked; a wavefront whose rows all precede the
+    // tile's first key has nothing to do
+    if (j < n_full || !CAUSAL || key0 <= w.q_wave + 31 + koff)
+      w.tile(j >= n_full, k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
     kstage.store(kt_lds[BUF ^ 1]);
     kstage.template store_rows<RowTile<D>>(k_lds[BUF ^ 1]);
   };

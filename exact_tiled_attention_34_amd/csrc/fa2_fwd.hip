@@ -84,12 +84,13 @@ struct FwdWave {
   // Online-softmax step on the scores of the tile starting at key0: P packed to
   // bf16 (pw), running max and sum updated.  Returns the factor that O must be
   // multiplied by (exactly 1 in every lane whose max did not grow); `any` tells
-  // whether some lane's factor differs from 1.  MASK: the tile may hold keys past
-  // the end of the sequence or above the diagonal for some of this wave's rows.
-  template <bool MASK>
+  // whether some lane's factor differs from 1.  mask: the tile may hold keys past
+  // the end of the sequence or above the diagonal for some of this wave's rows
+  // (a run-time branch over the scores only: one tile body for every tile, so
+  // the O accumulators keep one register assignment through the loop).
   __device__ __forceinline__ float softmax(f32x16 (&sacc)[C::KB], uint32_t (&pw)[C::KB][8], bool& any,
-                                           int key0, int Nk, float scale_log2) {
-    if (MASK) {
+                                           bool mask, int key0, int Nk, float scale_log2) {
+    if (mask) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -109,7 +110,7 @@ struct FwdWave {
     // visible keys when Nq > Nk): its maximum stays -inf, and 0 stands in
     // for it so that P = 0 and alpha = 0 instead of NaN.
     const float m_new = grow ? mx : m_run;
-    const float m_use = (MASK && m_new == -INFINITY) ? 0.f : m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2_fast((m_run - m_use) * scale_log2);
     const float mc = m_use * scale_log2;
     float rs = 0.f;
@@ -152,14 +153,16 @@ struct FwdWave {
 // Tile j (PAR = j % 2, a compile-time constant so that LDS buffers are
 // immediate offsets): issue the loads of tile j+1, then scores, softmax, the
 // rare rescale and O += V(j) P(j), then the transposed store of V(j+1).
-template <int D, bool CAUSAL, class E, int PAR, bool MASK>
+// Tiles from n_full on are masked.
+template <int D, bool CAUSAL, class E, int PAR>
 __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
                                          const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
                                          uint16_t (*k_lds)[FwdCfg<D>::TILE],
                                          uint16_t (*v_lds)[FwdCfg<D>::VTILE], const uint16_t* Kh,
-                                         const uint16_t* Vh, int j, int n_tiles, int Nk, int tid,
+                                         const uint16_t* Vh, int j, int n_tiles, int n_full, int Nk,
                                          float scale_log2) {
   using C = FwdCfg<D>;
+  const bool mask = j >= n_full;
   wait_vmem();
   __syncthreads();   // tile j is in LDS; every wave is done with the other buffer
   const bool more = j + 1 < n_tiles;
@@ -168,29 +171,15 @@ __device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL, E>& w, TrStage<D, Fw
   // itself into the idle buffer), so its registers never live across tiles.
   vstage.load(Vh, (more ? j + 1 : j) * C::BC, Nk);
   // a wavefront whose rows all precede the tile's first key has nothing to do
-  if (!MASK || !CAUSAL || j * C::BC <= w.key_last_wave) {
+  if (!mask || !CAUSAL || j * C::BC <= w.key_last_wave) {
     w.scores(k_lds[PAR], w.sc[0]);
     uint32_t pw[C::KB][8];
     bool any;
-    const float alpha = w.template softmax<MASK>(w.sc[0], pw, any, j * C::BC, Nk, scale_log2);
+    const float alpha = w.softmax(w.sc[0], pw, any, mask, j * C::BC, Nk, scale_log2);
     if (any) w.rescale(alpha);
     w.pv(v_lds[PAR], pw);
   }
   vstage.store(v_lds[PAR ^ 1]);
-}
-
-template <int D, bool CAUSAL, class E, int PAR>
-__device__ __forceinline__ void fwd_tile_any(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
-                                             const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
-                                             uint16_t (*k_lds)[FwdCfg<D>::TILE],
-                                             uint16_t (*v_lds)[FwdCfg<D>::VTILE],
-                                             const uint16_t* Kh, const uint16_t* Vh, int j,
-                                             int n_tiles, int n_full, int Nk, int tid,
-                                             float scale_log2) {
-  if (j < n_full)
-    fwd_tile<D, CAUSAL, E, PAR, false>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
-  else
-    fwd_tile<D, CAUSAL, E, PAR, true>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, Nk, tid, scale_log2);
 }
 
 // Two workgroups per CU (three at D = 64, whose registers and LDS allow it:
@@ -269,10 +258,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? 3 : 2)) void fwd_kernel(CView Q, CV
 
   // Tile j uses buffer j % 2; unrolled by two so the buffer is an immediate.
   for (int j = 0; j < n_tiles; j += 2) {
-    fwd_tile_any<D, CAUSAL, E, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, Nk, tid, scale_log2);
+    fwd_tile<D, CAUSAL, E, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, Nk, scale_log2);
     if (j + 1 < n_tiles)
-      fwd_tile_any<D, CAUSAL, E, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, Nk, tid,
-                                 scale_log2);
+      fwd_tile<D, CAUSAL, E, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, Nk, scale_log2);
   }
 
   // Epilogue: one division by the row sum, then O (bf16) and L (fp32, natural
