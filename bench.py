@@ -65,14 +65,14 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("55ee64ea6073892d", "c2", "bwd_dkdv"): 1359240148,
-    ("55ee64ea6073892d", "c2", "bwd_dq"): 770983716,
-    ("55ee64ea6073892d", "c2", "bwd_preprocess"): 138472587,
-    ("55ee64ea6073892d", "c2", "fwd"): 1165561391,
-    ("55ee64ea6073892d", "c4", "bwd_dkdv"): 869698914,
-    ("55ee64ea6073892d", "c4", "bwd_dq"): 782954665,
-    ("55ee64ea6073892d", "c4", "bwd_preprocess"): 138474251,
-    ("55ee64ea6073892d", "c4", "fwd"): 792149881,
+    ("2647278e11d519f2", "c2", "bwd_dkdv"): 1359222534,
+    ("2647278e11d519f2", "c2", "bwd_dq"): 740469357,
+    ("2647278e11d519f2", "c2", "bwd_preprocess"): 138472686,
+    ("2647278e11d519f2", "c2", "fwd"): 1166669565,
+    ("2647278e11d519f2", "c4", "bwd_dkdv"): 870324601,
+    ("2647278e11d519f2", "c4", "bwd_dq"): 718281095,
+    ("2647278e11d519f2", "c4", "bwd_preprocess"): 138474158,
+    ("2647278e11d519f2", "c4", "fwd"): 774986530,
 }
 
 
