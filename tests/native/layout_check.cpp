@@ -197,6 +197,10 @@ int main() {
     check_dma<80, 64, 512>(max_n, 80 * mult);
     check_dma<96, 64, 512>(max_n, 96 * mult);
     check_dma<128, 64, 512>(max_n, 128 * mult);
+    check_dma<64, 64, 768>(max_n, 64 * mult);
+    check_dma<80, 64, 768>(max_n, 80 * mult);
+    check_dma<96, 64, 768>(max_n, 96 * mult);
+    check_dma<128, 64, 768>(max_n, 128 * mult);
     check_stage<64, 64, 256, RowTileW<64>>(max_n, 64 * mult);
     check_stage<80, 64, 256, RowTileW<80>>(max_n, 80 * mult);
     check_stage<96, 64, 256, RowTileW<96>>(max_n, 96 * mult);

@@ -200,5 +200,6 @@ def test_strerror_and_tiles(lib):
     for d in (64, 80, 96, 128):
         t = fa2.tile_config(d)
         assert t["fwd_block_q"] % 32 == 0 and t["bwd_block_k"] % 32 == 0
+        assert t["fwd_block_q"] == 32 * t["fwd_waves"]
     with pytest.raises(fa2.FA2Error):
         fa2.tile_config(112)
