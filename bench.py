@@ -65,14 +65,14 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("2647278e11d519f2", "c2", "bwd_dkdv"): 1359222534,
-    ("2647278e11d519f2", "c2", "bwd_dq"): 740469357,
-    ("2647278e11d519f2", "c2", "bwd_preprocess"): 138472686,
-    ("2647278e11d519f2", "c2", "fwd"): 1166669565,
-    ("2647278e11d519f2", "c4", "bwd_dkdv"): 870324601,
-    ("2647278e11d519f2", "c4", "bwd_dq"): 718281095,
-    ("2647278e11d519f2", "c4", "bwd_preprocess"): 138474158,
-    ("2647278e11d519f2", "c4", "fwd"): 774986530,
+    ("4e2d18c332c0213c", "c2", "bwd_dkdv"): 1359301361,
+    ("4e2d18c332c0213c", "c2", "bwd_dq"): 740469803,
+    ("4e2d18c332c0213c", "c2", "bwd_preprocess"): 138472634,
+    ("4e2d18c332c0213c", "c2", "fwd"): 672324382,
+    ("4e2d18c332c0213c", "c4", "bwd_dkdv"): 870594107,
+    ("4e2d18c332c0213c", "c4", "bwd_dq"): 703462267,
+    ("4e2d18c332c0213c", "c4", "bwd_preprocess"): 138474298,
+    ("4e2d18c332c0213c", "c4", "fwd"): 541263663,
 }
 
 
