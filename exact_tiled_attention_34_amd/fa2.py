@@ -75,7 +75,10 @@ class FA2Error(RuntimeError):
 
 
 def load(path=None):
-    """Load libfa2.so (built by ``exact_tiled_attention_34_amd.build``)."""
+    """Load libfa2.so (built by ``exact_tiled_attention_34_amd.build``).
+
+    With a path, that library is loaded and becomes the one every function of
+    this module calls."""
     global _lib
     if _lib is not None and path is None:
         return _lib
@@ -88,8 +91,7 @@ def load(path=None):
         fn = getattr(lib, name)
         fn.restype = restype
         fn.argtypes = argtypes
-    if path is None:
-        _lib = lib
+    _lib = lib
     return lib
 
 

@@ -86,7 +86,8 @@ def assert_full_parity(arrs, causal, scale, label="", dtype="bf16"):
 @pytest.mark.parametrize("d", [64, 80, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", [(1, 1, 1), (1, 1, 12), (1, 2, 64), (2, 1, 127), (1, 1, 128),
-                                   (1, 2, 129), (2, 2, 200), (1, 1, 256), (1, 1, 333)])
+                                   (1, 2, 129), (2, 2, 200), (1, 1, 256), (1, 1, 333),
+                                   (1, 2, 520), (1, 1, 777)])
 def test_small_shapes(d, causal, B, H, N):
     arrs = gen.make_arrays(B, H, N, d, seed=1000 + N + d)
     assert_full_parity(arrs, causal, 1.0 / math.sqrt(d), f"B{B} H{H} N{N} d{d} causal={causal}")
