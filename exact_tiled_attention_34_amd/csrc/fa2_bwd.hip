@@ -138,8 +138,17 @@ struct DkdvWave {
     for (int t = 0; t < PF; ++t) fetch(t);
 
     // Row statistics of group (qb, g): lane (lr, lh) needs queries
-    // qb*32 + 8g + 4lh + r; read one stage before the group's softmax.
+    // qb*32 + 8g + 4lh + r.  sm_stage(qb, g) is the stage whose end runs the
+    // group's softmax; its statistics are read LEAD stages earlier (from stage
+    // 0 on).  LDS reads complete in order, so a statistics read issued just
+    // before its use would make the softmax also wait for the operand reads
+    // prefetched ahead of it.
     f32x4 lv[C::NQB][4], dv[C::NQB][4];
+    auto sm_stage = [](int qb, int g) {
+      return qb == 0 ? C::DK + 1 + g * (C::DK - 1) / 4 : NS + 1 + g * (2 * C::NDB - 1) / 4;
+    };
+    constexpr int LEAD = 4;
+    auto stats_stage = [&](int qb, int g) { return max(0, sm_stage(qb, g) - LEAD); };
     auto load_stats = [&](int qb, int g) {
       lv[qb][g] = *reinterpret_cast<const f32x4*>(l2s + qb * 32 + 8 * g + 4 * lh);
       dv[qb][g] = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * g + 4 * lh);
@@ -181,8 +190,9 @@ struct DkdvWave {
       if (t + PF < NALL) fetch(t + PF);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (t == C::DK + g * (C::DK - 1) / 4) load_stats(0, g);
-        if (t == C::DK + 1 + g * (C::DK - 1) / 4) softmax_group(0, g);
+        if (t == stats_stage(0, g)) load_stats(0, g);
+        if (t == stats_stage(1, g)) load_stats(1, g);
+        if (t == sm_stage(0, g)) softmax_group(0, g);
       }
       issue(t);
       sched_fence();
@@ -197,8 +207,8 @@ struct DkdvWave {
       if (t + PF < NALL) fetch(t + PF);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (u == g * (2 * C::NDB - 1) / 4) load_stats(1, g);
-        if (u == 1 + g * (2 * C::NDB - 1) / 4) softmax_group(1, g);
+        if (t == stats_stage(1, g)) load_stats(1, g);
+        if (t == sm_stage(1, g)) softmax_group(1, g);
       }
       issue(t);
       sched_fence();
