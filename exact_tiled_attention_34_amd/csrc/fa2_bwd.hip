@@ -4,7 +4,7 @@
 //   preprocess  for every query row: delta_i = sum_k dO_ik O_ik and L_i log2(e),
 //               written to row-padded fp32 arrays (rows past Nq, and rows that saw
 //               no key (L = -inf): delta 0 or its value, L +inf, which makes every
-//               P of such a row exactly 0); HBM-bound, 16 lanes per row.
+//               P of such a row exactly 0); HBM-bound, 8 lanes per row.
 //   dkdv        one workgroup per (128-key column block, batch*head); each of its 4
 //               wavefronts owns 32 keys and keeps K and V (as MFMA operands) and its
 //               dK, dV accumulators in registers while walking the 64-query row
@@ -41,13 +41,20 @@ namespace {
 // ---------------------------------------------------------------------------
 // preprocess
 // ---------------------------------------------------------------------------
+// Lanes per row of the preprocess kernel: each lane reads 16-byte chunks
+// sub, sub + 8, ... of its row of O and dO (D / 8 chunks: every lane busy at
+// D = 64 and 128).
+constexpr int kPreLanes = 8;
+constexpr int kPreRows = 256 / kPreLanes;   // rows per workgroup
+
 template <int D, class E>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
     CView O, CView dO, const float* __restrict__ LSE, float* __restrict__ Delta,
     float* __restrict__ L2, int H, int N, int Npad, long rows_pad) {
   constexpr int CH = D / 8;
-  const long prow = (long)blockIdx.x * 16 + (threadIdx.x >> 4);   // padded row index
-  const int sub = threadIdx.x & 15;
+  constexpr int ITER = (CH + kPreLanes - 1) / kPreLanes;
+  const long prow = (long)blockIdx.x * kPreRows + (threadIdx.x / kPreLanes);   // padded row index
+  const int sub = threadIdx.x % kPreLanes;
   const long bh = prow / Npad;
   const int q = (int)(prow - bh * Npad);
   const bool valid = prow < rows_pad && q < N;
@@ -56,16 +63,27 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(
   if (valid) {
     const uint16_t* orow = O.head((int)(bh / H), (int)(bh % H)) + (size_t)q * O.sr;
     const uint16_t* grow = dO.head((int)(bh / H), (int)(bh % H)) + (size_t)q * dO.sr;
-    for (int ch = sub; ch < CH; ch += 16) {
-      const u32x4 o = ld_global16(orow + ch * 8);
-      const u32x4 g = ld_global16(grow + ch * 8);
+    // every load of the lane first, then the arithmetic
+    u32x4 o[ITER], g[ITER];
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        acc += E::lo(o[w]) * E::lo(g[w]) + E::hi(o[w]) * E::hi(g[w]);
+    for (int it = 0; it < ITER; ++it) {
+      const int ch = sub + it * kPreLanes;
+      if (ch < CH) {
+        o[it] = ld_global16(orow + ch * 8);
+        g[it] = ld_global16(grow + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      if (sub + it * kPreLanes < CH) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          acc += E::lo(o[it][w]) * E::lo(g[it][w]) + E::hi(o[it][w]) * E::hi(g[it][w]);
+      }
     }
   }
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  for (int off = kPreLanes / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (prow < rows_pad && sub == 0) {
     Delta[prow] = valid ? acc : 0.f;
     const float l = valid ? LSE[row] : -INFINITY;
@@ -578,7 +596,7 @@ hipError_t launch_pre_t(const Strided& o, const Strided& dout, const float* lse,
                         float* l2, int B, int H, int N, hipStream_t stream) {
   const int Npad = bwd_rows_padded(N);
   const long rows_pad = (long)B * H * Npad;
-  bwd_preprocess_kernel<D, E><<<dim3((unsigned)((rows_pad + 15) / 16)), 256, 0, stream>>>(
+  bwd_preprocess_kernel<D, E><<<dim3((unsigned)((rows_pad + kPreRows - 1) / kPreRows)), 256, 0, stream>>>(
       cview(o), cview(dout), lse, delta, l2, H, N, Npad, rows_pad);
   return hipGetLastError();
 }
