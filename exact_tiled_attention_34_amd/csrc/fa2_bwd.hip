@@ -285,8 +285,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // Q and dO go through registers once and are written twice per step:
   // row-major and transposed.
   TrStage<D> qstage, dostage;
-  qstage.init(tid, Q.sr);
-  dostage.init(tid, dO.sr);
+  // A tile stage needs StagePlan<D>::THREADS_USED threads: at D = 64 that is
+  // half the workgroup, so wavefronts 0-1 stage Q and 2-3 stage dO; otherwise
+  // every thread stages its part of both.  (A thread index past the plan
+  // leaves that stage idle.)
+  constexpr int SPLIT = 2 * StagePlan<D>::THREADS_USED <= C::THREADS ? StagePlan<D>::THREADS_USED : 0;
+  constexpr int IDLE = C::THREADS;
+  qstage.init(SPLIT && tid >= SPLIT ? IDLE : tid, Q.sr);
+  dostage.init(SPLIT ? (tid >= SPLIT ? tid - SPLIT : IDLE) : tid, dO.sr);
   auto load_stage = [&](int i) {
     qstage.load(Qh, i * C::BQ, Nq);
     dostage.load(dOh, i * C::BQ, Nq);
