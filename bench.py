@@ -65,14 +65,14 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("4e2d18c332c0213c", "c2", "bwd_dkdv"): 1359301361,
-    ("4e2d18c332c0213c", "c2", "bwd_dq"): 740469803,
-    ("4e2d18c332c0213c", "c2", "bwd_preprocess"): 138472634,
-    ("4e2d18c332c0213c", "c2", "fwd"): 672324382,
-    ("4e2d18c332c0213c", "c4", "bwd_dkdv"): 870594107,
-    ("4e2d18c332c0213c", "c4", "bwd_dq"): 703462267,
-    ("4e2d18c332c0213c", "c4", "bwd_preprocess"): 138474298,
-    ("4e2d18c332c0213c", "c4", "fwd"): 541263663,
+    ("4374d336cedb087a", "c2", "bwd_dkdv"): 1359235755,
+    ("4374d336cedb087a", "c2", "bwd_dq"): 740477739,
+    ("4374d336cedb087a", "c2", "bwd_preprocess"): 137427444,
+    ("4374d336cedb087a", "c2", "fwd"): 672324241,
+    ("4374d336cedb087a", "c4", "bwd_dkdv"): 871489337,
+    ("4374d336cedb087a", "c4", "bwd_dq"): 695180535,
+    ("4374d336cedb087a", "c4", "bwd_preprocess"): 137428260,
+    ("4374d336cedb087a", "c4", "fwd"): 542138171,
 }
 
 
