@@ -76,6 +76,24 @@ MEASURED_TRAFFIC = {
 }
 
 
+def kernel_flops(w):
+    """Flops per launch of each MFMA kernel, in the attention convention's units:
+    fwd 4 B H N^2 d; dK/dV 4/5 of the backward's 10 B H N^2 d (S, dP, dV, dK);
+    dQ 3/5 of it (its own recomputation of S and dP, and dQ).  Halved when causal."""
+    f_bwd = w.flops("bwd")
+    return {"fwd": w.flops("fwd"), "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.6 * f_bwd}
+
+
+def compulsory_bytes(w, n_pad):
+    """HBM bytes per launch if every input is read once and every output written
+    once: bf16 [B,H,N,d] tensors, fp32 [B,H,N] rows, fp32 row arrays padded to
+    n_pad rows (the backward's delta and L log2 e)."""
+    t16 = 2 * w.B * w.H * w.N * w.d
+    rows, prow = 4 * w.B * w.H * w.N, 4 * w.B * w.H * n_pad
+    return {"fwd": 4 * t16 + rows, "bwd_preprocess": 2 * t16 + rows + 2 * prow,
+            "bwd_dkdv": 6 * t16 + 2 * prow, "bwd_dq": 5 * t16 + 2 * prow}
+
+
 def kernel_source_hash():
     import hashlib
     d = os.path.join(ROOT, "exact_tiled_attention_34_amd", "csrc")
@@ -307,11 +325,8 @@ def main():
     }
     phases.update({k2 + "_pct_peak": 100.0 * v2 / PEAK_BF16_TFLOPS for k2, v2 in list(phases.items())})
 
-    # dominant kernel and its roofline: the three big kernels are dense bf16 MFMA
-    # work; conventional flops per launch: fwd 4 B H N^2 d, dK/dV 4/5 of the
-    # backward's 10 B H N^2 d (S, dP, dV, dK), dQ 2/5 of it (its own S and dP
-    # recomputation and dQ: 3 products, one of them the conventional dQ share).
-    algo_flops = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.6 * f_bwd}
+    # dominant kernel and its roofline: the three big kernels are dense bf16 MFMA work
+    algo_flops = kernel_flops(w)
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kern_ms[n])
     achieved = algo_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     src = kernel_source_hash()
@@ -320,12 +335,8 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel_source": src}
 
-    # compulsory HBM bytes per launch (every input read once, every output written
-    # once; bf16 tensors, fp32 row arrays padded to Npad rows) and the rate they imply
-    t16 = 2 * B * H * N * d
-    rows, prow = 4 * B * H * N, 4 * B * H * fa2.bwd_rows_padded(N)
-    compulsory = {"fwd": 4 * t16 + rows, "bwd_preprocess": 2 * t16 + rows + 2 * prow,
-                  "bwd_dkdv": 6 * t16 + 2 * prow, "bwd_dq": 5 * t16 + 2 * prow}
+    # compulsory HBM bytes per launch and the rate they imply
+    compulsory = compulsory_bytes(w, fa2.bwd_rows_padded(N))
     hbm_gbs = {n: round(compulsory[n] / (kern_ms[n] * 1e-3) / 1e9, 1) for n in names}
 
     props = torch.cuda.get_device_properties(dev)
