@@ -104,7 +104,12 @@ struct DkdvCfg {
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
   static constexpr int NQB = BQ / 32;
-  static constexpr int TILE = RowTileW<D>::elems(BQ);
+  // Row-major Q and dO tiles: at D = 80 and 96 rows are laid out as 128-wide
+  // RowTileW rows (10 or 12 of their 16 chunks used).  The padded RowTileW<80>
+  // and RowTileW<96> layouts measured 1.3e8 bank-conflict cycles per C5
+  // launch on MI355X; the 128-wide one, like D = 64 and 128, none.
+  using RowL = std::conditional_t<(D == 80 || D == 96), RowTileW<128>, RowTileW<D>>;
+  static constexpr int TILE = RowL::elems(BQ);
   static constexpr int TTILE = TrTile<D, 64>::ELEMS;
   static_assert(BQ == 64, "transposed tiles hold 64 tokens");
 };
@@ -115,7 +120,7 @@ struct DkdvWave {
   u32x4 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
-  LaneOffsets<D, 64, RowTileW<D>> off;
+  LaneOffsets<D, 64, typename C::RowL> off;
 
   // One 64-query step.  qt, dot: row-major Q and dO tiles; qtt, dott: their
   // transposes; l2s, dls: the step's L log2 e and delta; kq0: the last key
@@ -307,9 +312,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   };
   auto store_step = [&](int buf) {
     qstage.store(qt_lds[buf]);
-    qstage.template store_rows<RowTileW<D>>(q_lds[buf]);
+    qstage.template store_rows<typename C::RowL>(q_lds[buf]);
     dostage.store(dot_lds[buf]);
-    dostage.template store_rows<RowTileW<D>>(do_lds[buf]);
+    dostage.template store_rows<typename C::RowL>(do_lds[buf]);
   };
   if (i_begin < n_qblk) {
     load_ld(ld_lds[0], i_begin * C::BQ);

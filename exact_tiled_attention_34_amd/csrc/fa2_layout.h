@@ -241,12 +241,15 @@ struct LaneOffsets {
   static constexpr int DK = D / 16;
   static constexpr int NDB = (D + 31) / 32;
   static constexpr int TR32 = 32 * TrTile<D, TOK>::ROW;     // elements per 32 feature rows
-  int row[DK];   // row-major tile: features 16 s + 8 h .. +7 of row lane % 32
+  // feature steps of the layout's rows (more than DK when D features are
+  // stored in wider rows: L::perm may then name a step past DK)
+  static constexpr int NROW = L::CH / 2;
+  int row[NROW];   // row-major tile: features 16 s + 8 h .. +7 of row lane % 32
   int tr;        // transposed tile: tokens {4h..4h+3, 8+4h..8+4h+3} of feature row lane % 32
   FA2_HD void init(int lane) {
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < DK; ++s) row[s] = L::elem(lr, s * 16 + 8 * lh);
+    for (int s = 0; s < NROW; ++s) row[s] = L::elem(lr, s * 16 + 8 * lh);
     tr = lr * TrTile<D, TOK>::ROW + 8 * lh;   // + 16 c (token chunk) + TR32 mb (feature block)
   }
   // row-major read of 32-row block b, feature step s

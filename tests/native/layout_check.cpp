@@ -132,7 +132,8 @@ void check_stage(int max_n, int R) {
   }
   // RowTileW row stores: store k of 16 consecutive active threads reaches 16
   // distinct bank groups
-  for (int t0 = 0; std::is_same<L, RowTileW<D>>::value && t0 < P::THREADS_USED; t0 += 16)
+  for (int t0 = 0; (std::is_same<L, RowTileW<D>>::value || std::is_same<L, RowTileW<128>>::value) &&
+                  t0 < P::THREADS_USED; t0 += 16)
     for (int k = 0; k < 4; ++k) {
       int seen[16] = {0};
       for (int tid = t0; tid < t0 + 16; ++tid) seen[(L::elem(4 * P::grp(tid) + k, 8 * P::chunk(tid)) / 8) % 16]++;
@@ -214,6 +215,12 @@ int main() {
   check_dma<80, 64, 512>(max_n, 88);
   check_stage<128, 64, 256, RowTileW<128>>(max_n, 136);
   check_stage<80, 64, 256, RowTileW<80>>(max_n, 88);
+  // the dK/dV pass stores D = 80 and 96 rows in 128-wide rows
+  for (int mult : {1, 2, 3}) {
+    check_stage<80, 64, 256, RowTileW<128>>(max_n, 80 * mult);
+    check_stage<96, 64, 256, RowTileW<128>>(max_n, 96 * mult);
+  }
+  check_stage<80, 64, 256, RowTileW<128>>(max_n, 88);
   // 32-row tiles (the dQ kernel's key tile can be 32 keys for D = 64 and 128)
   for (int mult : {1, 3}) {
     check_dma<64, 32, 512>(max_n, 64 * mult);
@@ -231,6 +238,8 @@ int main() {
   check_reads<80, 64, RowTileW<80>>();
   check_reads<96, 64, RowTileW<96>>();
   check_reads<128, 64, RowTileW<128>>();
+  check_reads<80, 64, RowTileW<128>>();
+  check_reads<96, 64, RowTileW<128>>();
   if (failures) {
     std::printf("%d violations\n", failures);
     return 1;
