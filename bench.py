@@ -65,14 +65,22 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("4374d336cedb087a", "c2", "bwd_dkdv"): 1359235755,
-    ("4374d336cedb087a", "c2", "bwd_dq"): 740477739,
-    ("4374d336cedb087a", "c2", "bwd_preprocess"): 137427444,
-    ("4374d336cedb087a", "c2", "fwd"): 672324241,
-    ("4374d336cedb087a", "c4", "bwd_dkdv"): 871489337,
-    ("4374d336cedb087a", "c4", "bwd_dq"): 695180535,
-    ("4374d336cedb087a", "c4", "bwd_preprocess"): 137428260,
-    ("4374d336cedb087a", "c4", "fwd"): 542138171,
+    ("0d0fa140b5596705", "c2", "bwd_dkdv"): 1359237449,
+    ("0d0fa140b5596705", "c2", "bwd_dq"): 740480059,
+    ("0d0fa140b5596705", "c2", "bwd_preprocess"): 137426664,
+    ("0d0fa140b5596705", "c2", "fwd"): 672324560,
+    ("0d0fa140b5596705", "c3", "bwd_dkdv"): 1420419507,
+    ("0d0fa140b5596705", "c3", "bwd_dq"): 809647224,
+    ("0d0fa140b5596705", "c3", "bwd_preprocess"): 140566807,
+    ("0d0fa140b5596705", "c3", "fwd"): 755364162,
+    ("0d0fa140b5596705", "c4", "bwd_dkdv"): 872047810,
+    ("0d0fa140b5596705", "c4", "bwd_dq"): 711484805,
+    ("0d0fa140b5596705", "c4", "bwd_preprocess"): 137427736,
+    ("0d0fa140b5596705", "c4", "fwd"): 545804813,
+    ("0d0fa140b5596705", "c5", "bwd_dkdv"): 1782692175,
+    ("0d0fa140b5596705", "c5", "bwd_dq"): 1016767356,
+    ("0d0fa140b5596705", "c5", "bwd_preprocess"): 174126229,
+    ("0d0fa140b5596705", "c5", "fwd"): 1629081244,
 }
 
 
