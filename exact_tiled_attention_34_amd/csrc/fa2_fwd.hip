@@ -43,14 +43,15 @@ namespace fa2 {
 namespace {
 
 // Wavefronts per workgroup and workgroups per CU, chosen by timing on MI355X:
-// one large workgroup per CU (8 wavefronts at D = 64 and 128, 12 at D = 96:
-// two or three per SIMD) shares each staged K/V tile among more query rows;
-// at D = 80 two workgroups of 4 wavefronts are as fast as 12 wavefronts and
-// 5 % faster than 8.
+// a large workgroup (8 wavefronts at D = 64 and 128, 12 at D = 96) shares each
+// staged K/V tile among more query rows; one per CU at D = 96 and 128, two at
+// D = 64 (four wavefronts per SIMD in 124 VGPRs); at D = 80 two workgroups of
+// 4 wavefronts are as fast as 12 wavefronts and 5 % faster than 8.
 template <int D>
 struct FwdCfg {
   static constexpr int WAVES = D == 96 ? 12 : D == 80 ? 4 : 8;
-  static constexpr int WGS_PER_CU = D == 80 ? 2 : 1;
+  static constexpr int WGS_PER_CU = D == 64 || D == 80 ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = WAVES * WGS_PER_CU / 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
   static constexpr int BC = 64;                   // keys per K/V tile (32 or 64)
@@ -58,8 +59,16 @@ struct FwdCfg {
   static constexpr int DP = (D + 31) / 32 * 32;   // O^T rows padded to whole 32-row MFMA blocks
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;               // k-steps of K Q^T
-  static constexpr int TILE = RowTile<D>::elems(BC);
+  // Tiles per stage: a stage of SUB tiles is staged together and opened by one
+  // workgroup barrier (half the barriers at SUB = 2, and the V tiles of a stage
+  // are staged by twice as many threads).  Two at D = 64, where it also keeps
+  // the non-causal kernel within 128 VGPRs (B8 H16 N2048 d64: -12 %; C3 -1 %);
+  // at D = 96 and 128 it measured even or slower (C4 +1.5 %).
+  static constexpr int SUB = D == 64 ? 2 : 1;
+  static constexpr int STAGE = SUB * BC;          // keys per stage
+  static constexpr int TILE = RowTile<D>::elems(STAGE);
   static constexpr int VTILE = TrTile<D, BC>::ELEMS;
+  static constexpr int VSTAGERS = StagePlan<D, BC>::THREADS_USED;   // threads per V tile
 };
 
 template <int D, bool CAUSAL, class E>
@@ -157,50 +166,59 @@ struct FwdWave {
   }
 };
 
-// Tile j (PAR = j % 2, a compile-time constant so that LDS buffers are
-// immediate offsets): issue the loads of tile j+1, then scores, softmax, the
-// rare rescale and O += V(j) P(j), then the transposed store of V(j+1).
-// Tiles from n_full on are masked.
+// Stage J (PAR = J % 2, a compile-time constant so that LDS buffers are
+// immediate offsets) holds tiles J*SUB .. J*SUB + SUB - 1: issue the loads of
+// stage J+1, then per tile scores, softmax, the rare rescale and
+// O += V(j) P(j), then the transposed store of this thread's V tile of stage
+// J+1.  Tiles from n_full on are masked.  vsub: the tile of a stage whose V
+// this thread stages (>= SUB: none).
 template <int D, bool CAUSAL, class E, int PAR>
-__device__ __forceinline__ void fwd_tile(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
-                                         const TileDma<D, FwdCfg<D>::BC, FwdCfg<D>::THREADS>& kdma,
-                                         uint16_t (*k_lds)[FwdCfg<D>::TILE],
-                                         uint16_t (*v_lds)[FwdCfg<D>::VTILE], const uint16_t* Kh,
-                                         const uint16_t* Vh, int j, int n_tiles, int n_full, int Nk,
-                                         float scale_log2) {
+__device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
+                                          const TileDma<D, FwdCfg<D>::STAGE, FwdCfg<D>::THREADS>& kdma,
+                                          uint16_t (*k_lds)[FwdCfg<D>::TILE],
+                                          uint16_t (*v_lds)[FwdCfg<D>::SUB][FwdCfg<D>::VTILE],
+                                          const uint16_t* Kh, const uint16_t* Vh, int J, int vsub,
+                                          int n_tiles, int n_full, int Nk, float scale_log2) {
   using C = FwdCfg<D>;
-  const bool mask = j >= n_full;
   wait_vmem();
-  __syncthreads();   // tile j is in LDS; every wave is done with the other buffer
-  const bool more = j + 1 < n_tiles;
-  if (more) kdma.issue(k_lds[PAR ^ 1], Kh, (j + 1) * C::BC, Nk);
-  // The V stage is loaded and stored on every tile (the last one re-stages
-  // itself into the idle buffer), so its registers never live across tiles.
-  vstage.load(Vh, (more ? j + 1 : j) * C::BC, Nk);
-  // a wavefront whose rows all precede the tile's first key has nothing to do
-  if (!mask || !CAUSAL || j * C::BC <= w.key_last_wave) {
-    w.scores(k_lds[PAR], w.sc[0]);
-    uint32_t pw[C::KB][8];
-    bool any;
-    const float alpha = w.softmax(w.sc[0], pw, any, mask, j * C::BC, Nk, scale_log2);
-    if (any) w.rescale(alpha);
-    w.pv(v_lds[PAR], pw);
+  __syncthreads();   // stage J is in LDS; every wave is done with the other buffer
+  const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
+  const bool more = J + 1 < n_stages;
+  if (more) kdma.issue(k_lds[PAR ^ 1], Kh, (J + 1) * C::STAGE, Nk);
+  // The V stage is loaded and stored on every stage (the last one re-stages
+  // itself into the idle buffer), so its registers never live across stages.
+  const int jv = (more ? J + 1 : J) * C::SUB + vsub;
+  const bool vdo = vsub < C::SUB && jv < n_tiles;
+  if (vdo) vstage.load(Vh, jv * C::BC, Nk);
+#pragma unroll
+  for (int sub = 0; sub < C::SUB; ++sub) {
+    const int j = J * C::SUB + sub;
+    const bool mask = j >= n_full;
+    // a wavefront whose rows all precede the tile's first key has nothing to do
+    if (j < n_tiles && (!mask || !CAUSAL || j * C::BC <= w.key_last_wave)) {
+      w.scores(k_lds[PAR] + sub * RowTile<D>::block(C::KB), w.sc[0]);
+      uint32_t pw[C::KB][8];
+      bool any;
+      const float alpha = w.softmax(w.sc[0], pw, any, mask, j * C::BC, Nk, scale_log2);
+      if (any) w.rescale(alpha);
+      w.pv(v_lds[PAR][sub], pw);
+    }
   }
-  vstage.store(v_lds[PAR ^ 1]);
+  if (vdo) vstage.store(v_lds[PAR ^ 1][vsub]);
 }
 
 template <int D, bool CAUSAL, class E>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WGS_PER_CU) void fwd_kernel(CView Q, CView K, CView V, View O,
+__global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void fwd_kernel(CView Q, CView K, CView V, View O,
                                                      float* __restrict__ LSE, int BH, int H, int Nq,
                                                      int Nk, float scale_log2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::VTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::SUB][C::VTILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  tr_zero_pad<D, C::BC>(v_lds[0], tid, C::THREADS);
-  tr_zero_pad<D, C::BC>(v_lds[1], tid, C::THREADS);
+  for (int b = 0; b < 2; ++b)
+    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[b][t], tid, C::THREADS);
 
   // Linear workgroup id -> (row block, batch*head).  Consecutive ids take
   // different heads, so with the round-robin dispatch over the 8 XCDs all row
@@ -243,15 +261,16 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WGS_PER_CU) void fwd
   // tiles [0, n_full) hold only keys that every row of the block may see
   const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
-  // Tile 0 into LDS (K directly, V transposed through registers).
+  // Stage 0 into LDS (K directly, V transposed through registers: thread tid
+  // stages V tile tid / VSTAGERS of each stage).
   TrStage<D, C::BC> vstage;
-  TileDma<D, C::BC, C::THREADS> kdma;
-  vstage.init(tid, V.sr);
+  TileDma<D, C::STAGE, C::THREADS> kdma;
+  const int vsub = tid / C::VSTAGERS;
+  vstage.init(vsub < C::SUB ? tid % C::VSTAGERS : C::VSTAGERS, V.sr);
   kdma.init(tid, K.sr);
-  if (n_tiles > 0) {
-    kdma.issue(k_lds[0], Kh, 0, Nk);
-    vstage.load(Vh, 0, Nk);
-  }
+  const bool v0 = vsub < C::SUB && vsub < n_tiles;
+  if (n_tiles > 0) kdma.issue(k_lds[0], Kh, 0, Nk);
+  if (v0) vstage.load(Vh, vsub * C::BC, Nk);
   // Q fragments stay in registers for the whole pass (B operand of S^T = K Q^T).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
@@ -259,13 +278,16 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WGS_PER_CU) void fwd
     if (w.q_lane < Nq) z = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
     w.qf[s] = z;
   }
-  if (n_tiles > 0) vstage.store(v_lds[0]);
+  if (v0) vstage.store(v_lds[0][vsub]);
 
-  // Tile j uses buffer j % 2; unrolled by two so the buffer is an immediate.
-  for (int j = 0; j < n_tiles; j += 2) {
-    fwd_tile<D, CAUSAL, E, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j, n_tiles, n_full, Nk, scale_log2);
-    if (j + 1 < n_tiles)
-      fwd_tile<D, CAUSAL, E, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, j + 1, n_tiles, n_full, Nk, scale_log2);
+  // Stage J uses buffer J % 2; unrolled by two so the buffer is an immediate.
+  const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
+  for (int J = 0; J < n_stages; J += 2) {
+    fwd_stage<D, CAUSAL, E, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, J, vsub, n_tiles, n_full, Nk,
+                               scale_log2);
+    if (J + 1 < n_stages)
+      fwd_stage<D, CAUSAL, E, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, J + 1, vsub, n_tiles, n_full, Nk,
+                                 scale_log2);
   }
 
   // Epilogue: one division by the row sum, then O (bf16) and L (fp32, natural

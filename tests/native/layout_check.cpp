@@ -199,6 +199,9 @@ int main() {
     check_dma<96, 64, 512>(max_n, 96 * mult);
     check_dma<128, 64, 512>(max_n, 128 * mult);
     check_dma<64, 64, 768>(max_n, 64 * mult);
+    check_dma<64, 128, 512>(max_n, 64 * mult);
+    check_dma<96, 128, 768>(max_n, 96 * mult);
+    check_dma<128, 128, 512>(max_n, 128 * mult);
     check_dma<80, 64, 768>(max_n, 80 * mult);
     check_dma<96, 64, 768>(max_n, 96 * mult);
     check_dma<128, 64, 768>(max_n, 128 * mult);
