@@ -65,22 +65,22 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("c720b4aa8d3602b9", "c2", "bwd_dkdv"): 1359235619,
-    ("c720b4aa8d3602b9", "c2", "bwd_dq"): 740479708,
-    ("c720b4aa8d3602b9", "c2", "bwd_preprocess"): 137426814,
-    ("c720b4aa8d3602b9", "c2", "fwd"): 672329213,
-    ("c720b4aa8d3602b9", "c3", "bwd_dkdv"): 1420325298,
-    ("c720b4aa8d3602b9", "c3", "bwd_dq"): 809649307,
-    ("c720b4aa8d3602b9", "c3", "bwd_preprocess"): 140567134,
-    ("c720b4aa8d3602b9", "c3", "fwd"): 774234157,
-    ("c720b4aa8d3602b9", "c4", "bwd_dkdv"): 871259202,
-    ("c720b4aa8d3602b9", "c4", "bwd_dq"): 701536448,
-    ("c720b4aa8d3602b9", "c4", "bwd_preprocess"): 137428558,
-    ("c720b4aa8d3602b9", "c4", "fwd"): 543122942,
-    ("c720b4aa8d3602b9", "c5", "bwd_dkdv"): 1782624877,
-    ("c720b4aa8d3602b9", "c5", "bwd_dq"): 1016745656,
-    ("c720b4aa8d3602b9", "c5", "bwd_preprocess"): 174125758,
-    ("c720b4aa8d3602b9", "c5", "fwd"): 1621116963,
+    ("8a4b8c0230957349", "c2", "bwd_dkdv"): 1359235619,
+    ("8a4b8c0230957349", "c2", "bwd_dq"): 740479708,
+    ("8a4b8c0230957349", "c2", "bwd_preprocess"): 137426814,
+    ("8a4b8c0230957349", "c2", "fwd"): 672329213,
+    ("8a4b8c0230957349", "c3", "bwd_dkdv"): 1420325298,
+    ("8a4b8c0230957349", "c3", "bwd_dq"): 809649307,
+    ("8a4b8c0230957349", "c3", "bwd_preprocess"): 140567134,
+    ("8a4b8c0230957349", "c3", "fwd"): 774234157,
+    ("8a4b8c0230957349", "c4", "bwd_dkdv"): 871259202,
+    ("8a4b8c0230957349", "c4", "bwd_dq"): 701536448,
+    ("8a4b8c0230957349", "c4", "bwd_preprocess"): 137428558,
+    ("8a4b8c0230957349", "c4", "fwd"): 543122942,
+    ("8a4b8c0230957349", "c5", "bwd_dkdv"): 1782624877,
+    ("8a4b8c0230957349", "c5", "bwd_dq"): 1016745656,
+    ("8a4b8c0230957349", "c5", "bwd_preprocess"): 174125758,
+    ("8a4b8c0230957349", "c5", "fwd"): 1621116963,
 }
 
 

@@ -30,9 +30,10 @@
 // "How It Works" 2) and L = (c m + log2 l) ln 2 is stored.
 //
 // K tiles go global -> LDS directly (no registers); V tiles are transposed on
-// the way (global -> registers -> LDS).  Both are double-buffered: the loads
-// of tile j+1 are issued right after the barrier that opens tile j, and the
-// transposed V tile is written once tile j's products are issued.
+// the way (global -> registers -> LDS).  Tiles are staged in stages of one or
+// two tiles, double-buffered: the loads of stage J+1 are issued right after
+// the barrier that opens stage J, and its transposed V tiles are written once
+// stage J's products are issued.
 #include <type_traits>
 
 #include "fa2_device.h"
