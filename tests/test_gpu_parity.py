@@ -108,7 +108,7 @@ def test_other_scales(scale):
                                          (1, 1, 64, 1000, 128), (2, 2, 300, 130, 80),
                                          (1, 2, 513, 200, 128), (1, 1, 129, 257, 80),
                                          (1, 2, 150, 270, 96), (1, 1, 1, 1, 64), (2, 1, 70, 1, 128),
-                                         (1, 3, 200, 333, 128)])
+                                         (1, 3, 200, 333, 128), (1, 2, 600, 190, 64), (1, 1, 800, 300, 96)])
 def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=3000 + Nq + Nk + d)
     label = f"B{B} H{H} Nq{Nq} Nk{Nk} d{d} causal={causal}"
