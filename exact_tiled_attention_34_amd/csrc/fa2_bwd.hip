@@ -106,8 +106,9 @@ struct DkdvCfg {
   static constexpr int NQB = BQ / 32;
   // Row-major Q and dO tiles: at D = 80 and 96 rows are laid out as 128-wide
   // RowTileW rows (10 or 12 of their 16 chunks used).  The padded RowTileW<80>
-  // and RowTileW<96> layouts measured 1.3e8 bank-conflict cycles per C5
-  // launch on MI355X; the 128-wide one, like D = 64 and 128, none.
+  // and RowTileW<96> layouts measured 1.3e8 bank-conflict cycles per launch
+  // at B2 H32 N8192 d80 causal on MI355X; the 128-wide one, like D = 64 and
+  // 128, none.
   using RowL = std::conditional_t<(D == 80 || D == 96), RowTileW<128>, RowTileW<D>>;
   static constexpr int TILE = RowL::elems(BQ);
   static constexpr int TTILE = TrTile<D, 64>::ELEMS;

@@ -63,8 +63,9 @@ struct FwdCfg {
   // Tiles per stage: a stage of SUB tiles is staged together and opened by one
   // workgroup barrier (half the barriers at SUB = 2, and the V tiles of a stage
   // are staged by twice as many threads).  Two at D = 64, where it also keeps
-  // the non-causal kernel within 128 VGPRs (B8 H16 N2048 d64: -12 %; C3 -1 %);
-  // at D = 96 and 128 it measured even or slower (C4 +1.5 %).
+  // the non-causal kernel within 128 VGPRs (B8 H16 N2048 d64: -12 %; B4 H32
+  // N4096 d64 causal: -1 %); at D = 96 and 128 it measured even or slower
+  // (B1 H16 N16384 d128 causal: +1.5 %).
   static constexpr int SUB = D == 64 ? 2 : 1;
   static constexpr int STAGE = SUB * BC;          // keys per stage
   static constexpr int TILE = RowTile<D>::elems(STAGE);
