@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--calibrate-mfma", action="store_true",
                     help="instead of the benchmark, run the register-only MFMA rate probe "
                          "(zero and random bf16 operands)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed "
+                         "(graph_replay_ms_per_step: what a launch-bound caller gains)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB (read + write "
                          "of known size: the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -323,6 +326,26 @@ def main():
             kern_ms[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
+    graph_ms = None
+    if args.graph:
+        # the same four launches, captured on torch's capture stream and replayed
+        def step_on_current_stream():
+            fa2.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fa2.bwd_preprocess(o, do, lse, delta, lse_log2)
+            fa2.bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=w.causal, scale=w.scale)
+            fa2.bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=w.causal, scale=w.scale)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_on_current_stream()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     f_fwd, f_bwd, f_all = w.flops("fwd"), w.flops("bwd"), w.flops("fwdbwd")
     value = f_all / (ms_per_step * 1e-3) / 1e12
     bwd_ms = kern_ms["bwd_preprocess"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
@@ -359,6 +382,7 @@ def main():
         "kernel_ms": {k2: round(v2, 4) for k2, v2 in kern_ms.items()},
         "compulsory_hbm_gbs": hbm_gbs,
         "roofline": roofline,
+        **({"graph_replay_ms_per_step": round(graph_ms, 4)} if graph_ms is not None else {}),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
