@@ -39,8 +39,10 @@ DEFAULT_CONFIG = "c2"        # B8 H16 N2048 d128 non-causal
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # untimed steps first: the GPU's clocks take tens of milliseconds to settle
+    # (B8 H16 N2048 d128: 1.39 ms per step after 5 warm-up steps, 1.32 ms after 200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(gen.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
