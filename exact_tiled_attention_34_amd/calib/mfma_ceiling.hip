@@ -6,10 +6,14 @@
 // instruction competes, so the rate is the matrix cores' own under the power
 // and clock behaviour of each operand kind: the practical ceiling against
 // which the attention kernels' MFMA rates can be read (the published dense
-// peak assumes the maximum clock).  Prints one JSON line.
+// peak assumes the maximum clock).  Prints one JSON line; with an argument
+// C > 0 it instead prints, random operands first (from an idle GPU), the rate
+// of each of C chunks of 20 launches (about 50 ms each), to show that the rate
+// holds over time.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -55,7 +59,8 @@ __global__ __launch_bounds__(256) void mfma_loop(const bf16x8* __restrict__ a, c
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-int main() {
+int main(int argc, char** argv) {
+  const int chunks = argc > 1 ? std::atoi(argv[1]) : 0;
   const size_t n_vec = (size_t)kSets * 1024;   // bf16x8 elements per operand buffer
   bf16x8 *a = nullptr, *b = nullptr;
   float* out = nullptr;
@@ -64,7 +69,8 @@ int main() {
   CHECK(hipMalloc(&out, (size_t)kGrid * 256 * 4));
   std::vector<uint16_t> h(n_vec * 8);
   double tflops[2];
-  for (int kind = 0; kind < 2; ++kind) {
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kind = chunks > 0 ? 1 - kk : kk;
     uint32_t x = 12345u;   // linear congruential draws, top 23 bits -> [-2, 2)
     for (size_t i = 0; i < h.size(); ++i) {
       x = x * 1664525u + 1013904223u;
@@ -75,13 +81,25 @@ int main() {
     }
     CHECK(hipMemcpy(a, h.data(), n_vec * 16, hipMemcpyHostToDevice));
     CHECK(hipMemcpy(b, h.data(), n_vec * 16, hipMemcpyHostToDevice));
-    for (int w = 0; w < 3; ++w) mfma_loop<<<kGrid, 256>>>(a, b, out);
-    CHECK(hipGetLastError());
-    CHECK(hipDeviceSynchronize());
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
     const int reps = 20;
+    const double chunk_flops = (double)reps * kGrid * 4 * kIters * 16 * (2.0 * 32 * 32 * 16);
+    for (int c = 0; c < chunks; ++c) {
+      CHECK(hipEventRecord(e0));
+      for (int r = 0; r < reps; ++r) mfma_loop<<<kGrid, 256>>>(a, b, out);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      float ms = 0.f;
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      std::printf("{\"operands\": \"%s\", \"chunk\": %d, \"ms\": %.2f, \"tflops\": %.1f}\n",
+                  kind ? "random" : "zero", c, ms, chunk_flops / (ms * 1e-3) / 1e12);
+    }
+    if (chunks > 0) continue;
+    for (int w = 0; w < 3; ++w) mfma_loop<<<kGrid, 256>>>(a, b, out);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
     CHECK(hipEventRecord(e0));
     for (int r = 0; r < reps; ++r) mfma_loop<<<kGrid, 256>>>(a, b, out);
     CHECK(hipEventRecord(e1));
@@ -91,6 +109,7 @@ int main() {
     const double flops = (double)reps * kGrid * 4 * kIters * 16 * (2.0 * 32 * 32 * 16);
     tflops[kind] = flops / (ms * 1e-3) / 1e12;
   }
+  if (chunks > 0) return 0;
   std::printf("{\"mfma_bf16_32x32x16_tflops_zero_operands\": %.1f, "
               "\"mfma_bf16_32x32x16_tflops_random_operands\": %.1f}\n", tflops[0], tflops[1]);
   return 0;
