@@ -290,7 +290,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   };
   // Q and dO go through registers once and are written twice per step:
   // row-major and transposed.
-  TrStage<D> qstage, dostage;
+  // (at D = 128 every thread stages its part of both tiles)
+  constexpr bool ALL_STAGE = StagePlan<D>::THREADS_USED == C::THREADS;
+  TrStage<D, 64, ALL_STAGE> qstage, dostage;
   // A tile stage needs StagePlan<D>::THREADS_USED threads: at D = 64 that is
   // half the workgroup, so wavefronts 0-1 stage Q and 2-3 stage dO; otherwise
   // every thread stages its part of both.  (A thread index past the plan

@@ -203,8 +203,9 @@ struct TileDma {
 // at once with load(), or spread over the compute that hides them), store()
 // (once the values are needed, typically after the current tile's compute)
 // writes the transposed tile, store_rows<L>() the same tokens as a row-major tile.
-// Rows past n_rows are clamped to the last row.
-template <int D, int TOK = 64>
+// Rows past n_rows are clamped to the last row.  ALL: every thread of the
+// workgroup stages (known at compile time, so no thread tests its `act`).
+template <int D, int TOK = 64, bool ALL = false>
 struct TrStage {
   using P = StagePlan<D, TOK>;
   u32x4 r[4];
@@ -226,7 +227,7 @@ struct TrStage {
     lastk = P::last_k(g, tok0, n_rows);
   }
   __device__ __forceinline__ void load_k(int k) {
-    if (act) r[k] = ld_global16(src + (uint32_t)P::source_k(off, k, lastk, R));
+    if (ALL || act) r[k] = ld_global16(src + (uint32_t)P::source_k(off, k, lastk, R));
   }
   __device__ __forceinline__ void load(const uint16_t* head, int tok0, int n_rows) {
     begin(head, tok0, n_rows);
@@ -234,7 +235,7 @@ struct TrStage {
     for (int k = 0; k < 4; ++k) load_k(k);
   }
   __device__ __forceinline__ void store(uint16_t* tile) const {
-    if (!act) return;
+    if (!ALL && !act) return;
     uint16_t* dst = tile + TrTile<D, TOK>::elem(8 * c, 4 * g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -253,7 +254,7 @@ struct TrStage {
   // operand read reaches them.
   template <class L>
   __device__ __forceinline__ void store_rows(uint16_t* tile) const {
-    if (!act) return;
+    if (!ALL && !act) return;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       *reinterpret_cast<u32x4*>(tile + L::elem(4 * g + k, 8 * c)) = r[k];
