@@ -70,22 +70,22 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("a70684d36842534f", "c2", "bwd_dkdv"): 1359235619,
-    ("a70684d36842534f", "c2", "bwd_dq"): 740479708,
-    ("a70684d36842534f", "c2", "bwd_preprocess"): 137426814,
-    ("a70684d36842534f", "c2", "fwd"): 672329213,
-    ("a70684d36842534f", "c3", "bwd_dkdv"): 1420325298,
-    ("a70684d36842534f", "c3", "bwd_dq"): 809649307,
-    ("a70684d36842534f", "c3", "bwd_preprocess"): 140567134,
-    ("a70684d36842534f", "c3", "fwd"): 774234157,
-    ("a70684d36842534f", "c4", "bwd_dkdv"): 871259202,
-    ("a70684d36842534f", "c4", "bwd_dq"): 701536448,
-    ("a70684d36842534f", "c4", "bwd_preprocess"): 137428558,
-    ("a70684d36842534f", "c4", "fwd"): 543122942,
-    ("a70684d36842534f", "c5", "bwd_dkdv"): 1782624877,
-    ("a70684d36842534f", "c5", "bwd_dq"): 1016745656,
-    ("a70684d36842534f", "c5", "bwd_preprocess"): 174125758,
-    ("a70684d36842534f", "c5", "fwd"): 1621116963,
+    ("40b93f02b47a6977", "c2", "bwd_dkdv"): 1359205265,
+    ("40b93f02b47a6977", "c2", "bwd_dq"): 740472364,
+    ("40b93f02b47a6977", "c2", "bwd_preprocess"): 137427265,
+    ("40b93f02b47a6977", "c2", "fwd"): 672329195,
+    ("40b93f02b47a6977", "c3", "bwd_dkdv"): 1420435343,
+    ("40b93f02b47a6977", "c3", "bwd_dq"): 809649517,
+    ("40b93f02b47a6977", "c3", "bwd_preprocess"): 140566881,
+    ("40b93f02b47a6977", "c3", "fwd"): 780752408,
+    ("40b93f02b47a6977", "c4", "bwd_dkdv"): 869634717,
+    ("40b93f02b47a6977", "c4", "bwd_dq"): 706051529,
+    ("40b93f02b47a6977", "c4", "bwd_preprocess"): 137429281,
+    ("40b93f02b47a6977", "c4", "fwd"): 548783344,
+    ("40b93f02b47a6977", "c5", "bwd_dkdv"): 1782683570,
+    ("40b93f02b47a6977", "c5", "bwd_dq"): 1016626945,
+    ("40b93f02b47a6977", "c5", "bwd_preprocess"): 174125858,
+    ("40b93f02b47a6977", "c5", "fwd"): 1620821836,
 }
 
 
