@@ -13,7 +13,7 @@ causal).  ``roofline`` describes the kernel that takes most of the step time;
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
 workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4]
        python bench.py --gpt-block 2k|8k   (the GPT-3-2.7B-shaped attention sublayer:
                                             model TFLOP/s by the page's end-to-end formula)
 """
@@ -33,7 +33,9 @@ import fa2_inputs as gen  # noqa: E402
 METRIC = "attention fwd/bwd/fwd+bwd TFLOP/s and % of bf16 MFMA peak, d=64/128"
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-DEFAULT_CONFIG = "c2"        # B8 H16 N2048 d128 non-causal
+DEFAULT_CONFIG = "c4"        # B1 H16 N16384 d128 causal: the long-sequence workload, largest by work
+MFMA_PROBE_SRC = os.path.join(ROOT, "bench_mfma_ceiling.hip")
+MFMA_PROBE_EXE = os.path.join(ROOT, "_build", "mfma_ceiling")
 
 
 def parse():
@@ -54,7 +56,12 @@ def parse():
                          "operands (the dense MFMA rate this GPU sustains under realistic data)")
     ap.add_argument("--calibrate-mfma", action="store_true",
                     help="instead of the benchmark, run the register-only MFMA rate probe "
-                         "(zero and random bf16 operands)")
+                         "(zero and random bf16 operands; build it first with --build-mfma-probe)")
+    ap.add_argument("--build-mfma-probe", action="store_true",
+                    help="compile the MFMA rate probe (bench_mfma_ceiling.hip) with hipcc and exit")
+    ap.add_argument("--no-ratio", action="store_true",
+                    help="for a causal workload, skip timing the same shape without the mask "
+                         "(the causal / non-causal time ratio)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed "
                          "(graph_replay_ms_per_step: what a launch-bound caller gains)")
@@ -157,16 +164,33 @@ def calibrate_gemm(n, steps=20):
                       "peak_bf16_tflops": PEAK_BF16_TFLOPS}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, arrs, budget_s):
-    """Time the float64 oracle (fwd + bwd, whole heads) for about budget_s seconds."""
-    import numpy as np
+    """Time the float64 oracle (fwd + bwd, whole heads) for about budget_s seconds
+    (always at least one whole head).  Threads: the CPUs this process may run on
+    (sched_getaffinity), capped by OMP_NUM_THREADS when that is set (a share of a
+    larger host); the BLAS pool is limited to that count."""
     import oracle
     from oracle import attention as A
+    affinity = len(os.sched_getaffinity(0))
+    threads = affinity
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = max(1, min(affinity, int(os.environ["OMP_NUM_THREADS"])))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads, user_api="blas")
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        limiter = None
     heads, t0 = 0, time.perf_counter()
     for b in range(w.B):
         for h in range(w.H):
@@ -179,10 +203,13 @@ def cpu_baseline(w, arrs, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     flops = w.flops("fwdbwd") / (w.B * w.H) * heads
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, fwd+bwd in float64 numpy "
-                      f"({dt:.1f} s); conventional flops of those heads / wall time"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} whole (batch, head) pairs, fwd+bwd in float64 numpy "
+                      f"({dt:.1f} s); conventional flops of those heads / wall time",
+            "cpu_model": cpu_model(), "affinity_cpus": affinity}
 
 
 def gpt_block_bench(args):
@@ -260,14 +287,19 @@ def main():
     if args.calibrate_gemm:
         calibrate_gemm(args.calibrate_gemm)
         return
-    if args.calibrate_mfma:
-        # a separate program (built by the package's build step); this process
-        # has not touched the GPU, and runs it as a child
+    if args.build_mfma_probe:
         import subprocess
-        exe = os.path.join(ROOT, "exact_tiled_attention_34_amd", "calib", "mfma_ceiling")
-        if not os.path.exists(exe):
-            sys.exit(f"{exe} is missing: build with `python -m exact_tiled_attention_34_amd.build`")
-        sys.exit(subprocess.run([exe]).returncode)
+        from exact_tiled_attention_34_amd.build import COMMON_FLAGS, hipcc
+        os.makedirs(os.path.dirname(MFMA_PROBE_EXE), exist_ok=True)
+        r = subprocess.run([hipcc(), *COMMON_FLAGS, MFMA_PROBE_SRC, "-o", MFMA_PROBE_EXE])
+        sys.exit(r.returncode)
+    if args.calibrate_mfma:
+        # a separate program, built beforehand on the host; this process has
+        # not touched the GPU, and runs it as a child
+        import subprocess
+        if not os.path.exists(MFMA_PROBE_EXE):
+            sys.exit(f"{MFMA_PROBE_EXE} is missing: build it with `python bench.py --build-mfma-probe`")
+        sys.exit(subprocess.run([MFMA_PROBE_EXE]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (heads would shard "
               "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
@@ -296,37 +328,49 @@ def main():
     stream = torch.cuda.current_stream(dev)
     names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
 
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        fa2.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
-        mark(1)
-        fa2.bwd_preprocess(o, do, lse, delta, lse_log2, stream=stream)
-        mark(2)
-        fa2.bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=w.causal, scale=w.scale, stream=stream)
-        mark(3)
-        fa2.bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=w.causal, scale=w.scale, stream=stream)
-        mark(4)
+    def timed_steps(causal):
+        """W untimed steps, then exactly K timed ones; returns (ms per step by the
+        host clock around the K steps, mean ms of each kernel by its HIP events)."""
+        def step(ev=None):
+            def mark(i):
+                if ev is not None:
+                    ev[i].record(stream)
+            mark(0)
+            fa2.fwd(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse, stream=stream)
+            mark(1)
+            fa2.bwd_preprocess(o, do, lse, delta, lse_log2, stream=stream)
+            mark(2)
+            fa2.bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=causal, scale=w.scale, stream=stream)
+            mark(3)
+            fa2.bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=causal, scale=w.scale, stream=stream)
+            mark(4)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()            # one process, one GPU: no barrier to wait for
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            step(events[s_])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        km = {n: 0.0 for n in names}
+        for ev in events:
+            for i, n in enumerate(names):
+                km[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps
+        return wall * 1e3 / args.steps, km
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()            # one process, one GPU: no barrier to wait for
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    kern_ms = {n: 0.0 for n in names}
-    for ev in events:
-        for i, n in enumerate(names):
-            kern_ms[n] += ev[i].elapsed_time(ev[i + 1]) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, kern_ms = timed_steps(w.causal)
+    # The pages report causal attention running 1.7-1.8x faster than non-causal
+    # at the same shape (blocks above the diagonal skipped): the same shape
+    # without the mask, timed the same way, gives this implementation's ratio.
+    ratio = None
+    if w.causal and not args.no_ratio:
+        nc_ms, nc_kern = timed_steps(False)
+        ratio = {"noncausal_ms_per_step": round(nc_ms, 4),
+                 "noncausal_kernel_ms": {k2: round(v2, 4) for k2, v2 in nc_kern.items()},
+                 "noncausal_over_causal_time": round(nc_ms / ms_per_step, 3)}
 
     graph_ms = None
     if args.graph:
@@ -385,6 +429,7 @@ def main():
         "compulsory_hbm_gbs": hbm_gbs,
         "roofline": roofline,
         **({"graph_replay_ms_per_step": round(graph_ms, 4)} if graph_ms is not None else {}),
+        **({"causal_speedup": ratio} if ratio is not None else {}),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }

@@ -67,21 +67,7 @@ def build(verbose=False, extra_flags=()):
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
-    build_calibration()
     return LIB_PATH
-
-
-CALIB_SRC = os.path.join(PKG, "calib", "mfma_ceiling.hip")
-CALIB_EXE = os.path.join(PKG, "calib", "mfma_ceiling")
-
-
-def build_calibration():
-    """The MFMA-rate probe that ``bench.py --calibrate-mfma`` runs (a separate program)."""
-    cmd = [hipcc(), *COMMON_FLAGS, CALIB_SRC, "-o", CALIB_EXE]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {CALIB_SRC}:\n{res.stderr}")
-    return CALIB_EXE
 
 
 if __name__ == "__main__":

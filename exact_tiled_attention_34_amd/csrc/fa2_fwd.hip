@@ -48,7 +48,7 @@ namespace {
 // staged K/V tile among more query rows; one per CU at D = 96 and 128, two at
 // D = 64 (four wavefronts per SIMD in 124 VGPRs); at D = 80 two workgroups of
 // 4 wavefronts are as fast as 12 wavefronts and 5 % faster than 8.
-template <int D>
+template <int D, bool CAUSAL = false>
 struct FwdCfg {
   static constexpr int WAVES = D == 96 ? 12 : D == 80 ? 4 : 8;
   static constexpr int WGS_PER_CU = D == 64 || D == 80 ? 2 : 1;
@@ -66,7 +66,7 @@ struct FwdCfg {
   // the non-causal kernel within 128 VGPRs (B8 H16 N2048 d64: -12 %; B4 H32
   // N4096 d64 causal: -1 %); at D = 96 and 128 it measured even or slower
   // (B1 H16 N16384 d128 causal: +1.5 %).
-  static constexpr int SUB = D == 64 ? 2 : 1;
+  static constexpr int SUB = D == 64 && !CAUSAL ? 2 : 1;
   static constexpr int STAGE = SUB * BC;          // keys per stage
   static constexpr int TILE = RowTile<D>::elems(STAGE);
   static constexpr int VTILE = TrTile<D, BC>::ELEMS;
@@ -75,7 +75,7 @@ struct FwdCfg {
 
 template <int D, bool CAUSAL, class E>
 struct FwdWave {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, CAUSAL>;
   u32x4 qf[C::DK];
   f32x16 oacc[C::NDB];
   f32x16 sc[1][C::KB];  // scores of the current tile
@@ -83,7 +83,7 @@ struct FwdWave {
   int lane, lr, lh, q_wave, q_lane;
   int key_last;        // causal: last key this lane's query may see (q_lane + Nk - Nq)
   int key_last_wave;   // the same for the wavefront's last query row
-  LaneOffsets<D, FwdCfg<D>::BC> off;
+  LaneOffsets<D, FwdCfg<D, CAUSAL>::BC> off;
 
   // S^T (64 keys x this wave's 32 queries) of the K tile at kt.
   __device__ __forceinline__ void scores(const uint16_t* kt, f32x16 (&sacc)[C::KB]) const {
@@ -161,7 +161,7 @@ struct FwdWave {
       const u32x4 b = acc_chunk(pw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        oacc[mb] = E::mfma(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D>::BC>::TR32), b,
+        oacc[mb] = E::mfma(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D, CAUSAL>::BC>::TR32), b,
                                 oacc[mb]);
     }
     mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
@@ -175,13 +175,13 @@ struct FwdWave {
 // J+1.  Tiles from n_full on are masked.  vsub: the tile of a stage whose V
 // this thread stages (>= SUB: none).
 template <int D, bool CAUSAL, class E, int PAR>
-__device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D>::BC>& vstage,
-                                          const TileDma<D, FwdCfg<D>::STAGE, FwdCfg<D>::THREADS>& kdma,
-                                          uint16_t (*k_lds)[FwdCfg<D>::TILE],
-                                          uint16_t (*v_lds)[FwdCfg<D>::SUB][FwdCfg<D>::VTILE],
+__device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D, CAUSAL>::BC>& vstage,
+                                          const TileDma<D, FwdCfg<D, CAUSAL>::STAGE, FwdCfg<D, CAUSAL>::THREADS>& kdma,
+                                          uint16_t (*k_lds)[FwdCfg<D, CAUSAL>::TILE],
+                                          uint16_t (*v_lds)[FwdCfg<D, CAUSAL>::SUB][FwdCfg<D, CAUSAL>::VTILE],
                                           const uint16_t* Kh, const uint16_t* Vh, int J, int vsub,
                                           int n_tiles, int n_full, int Nk, float scale_log2) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, CAUSAL>;
   wait_vmem();
   __syncthreads();   // stage J is in LDS; every wave is done with the other buffer
   const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
@@ -210,10 +210,10 @@ __device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, F
 }
 
 template <int D, bool CAUSAL, class E>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void fwd_kernel(CView Q, CView K, CView V, View O,
+__global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::WAVES_PER_SIMD)) void fwd_kernel(CView Q, CView K, CView V, View O,
                                                      float* __restrict__ LSE, int BH, int H, int Nq,
                                                      int Nk, float scale_log2) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, CAUSAL>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::SUB][C::VTILE];
 
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void
 template <int D, bool CAUSAL, class E>
 hipError_t launch_fwd_t(const Strided& q, const Strided& k, const Strided& v, const Strided& o,
                         float* lse, int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, CAUSAL>;
   const int BH = B * H;
   const int nrb = (Nq + C::BR - 1) / C::BR;
   fwd_kernel<D, CAUSAL, E><<<dim3((unsigned)(nrb * BH)), C::THREADS, 0, stream>>>(

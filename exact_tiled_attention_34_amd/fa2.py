@@ -249,16 +249,44 @@ def bwd_row_arrays(B, H, N, device):
             torch.empty(shape, dtype=torch.float32, device=device))
 
 
+def _check_phase_tensors(named, rows_shape):
+    """The phase entry points take contiguous bfloat16 [B,H,N,d] tensors and the two
+    padded fp32 row arrays [B,H,bwd_rows_padded(Nq)]: anything else (another dtype,
+    a strided or expanded view) is rejected here, before any pointer reaches the C ABI."""
+    import torch
+    for name, t, shape in named:
+        _check_qkv(name, t, shape)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name}: the phase entry points take bfloat16 tensors, got {t.dtype}")
+    for name, t in rows_shape[1]:
+        _check_f32(name, t, rows_shape[0])
+
+
 def bwd_preprocess(o, do, lse, delta, lse_log2, stream=None):
+    """delta = rowsum(do * o) and lse_log2 = lse * log2(e) into the padded row arrays."""
+    _check_qkv("o", o)
     B, H, N, d = o.shape
+    _check_f32("lse", lse, (B, H, N))
+    _check_phase_tensors((("o", o, o.shape), ("do", do, o.shape)),
+                         ((B, H, bwd_rows_padded(N)), (("delta", delta), ("lse_log2", lse_log2))))
     st = load().fa2_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), delta.data_ptr(),
                                    lse_log2.data_ptr(), B, H, N, d, _stream_handle(o.device, stream))
     _check(st, "fa2_bwd_preprocess")
 
 
-def bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=False, scale=None, stream=None):
+def _phase_shapes(q, k):
+    _check_qkv("q", q)
+    _check_qkv("k", k)
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    return B, H, N, d, k.shape[2], (B, H, k.shape[2], d)
+
+
+def bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=False, scale=None, stream=None):
+    """dK, dV from the row arrays of bwd_preprocess (contiguous bf16 tensors only)."""
+    B, H, N, d, Nk, kshape = _phase_shapes(q, k)
+    _check_phase_tensors((("q", q, q.shape), ("k", k, kshape), ("v", v, kshape), ("do", do, q.shape),
+                          ("dk", dk, kshape), ("dv", dv, kshape)),
+                         ((B, H, bwd_rows_padded(N)), (("lse_log2", lse_log2), ("delta", delta))))
     scale = default_scale(d) if scale is None else float(scale)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
             lse_log2.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr())
@@ -271,8 +299,11 @@ def bwd_dkdv(q, k, v, do, lse_log2, delta, dk, dv, causal=False, scale=None, str
 
 
 def bwd_dq(q, k, v, do, lse_log2, delta, dq, causal=False, scale=None, stream=None):
-    B, H, N, d = q.shape
-    Nk = k.shape[2]
+    """dQ from the row arrays of bwd_preprocess (contiguous bf16 tensors only)."""
+    B, H, N, d, Nk, kshape = _phase_shapes(q, k)
+    _check_phase_tensors((("q", q, q.shape), ("k", k, kshape), ("v", v, kshape), ("do", do, q.shape),
+                          ("dq", dq, q.shape)),
+                         ((B, H, bwd_rows_padded(N)), (("lse_log2", lse_log2), ("delta", delta))))
     scale = default_scale(d) if scale is None else float(scale)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
             lse_log2.data_ptr(), delta.data_ptr(), dq.data_ptr())
