@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "fa2.h"
 #include "fa2_launch.h"
@@ -117,6 +118,44 @@ bool strided_view(const void* p, const fa2_strides* s, int B, int H, int N, int 
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free backward (fa2_bwd_qk_noalloc): the two padded
+// fp32 row arrays live in this fixed device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy for the life of
+// the process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return FA2_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return FA2_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA2_OK;
+}
 
 }  // namespace
 
@@ -293,6 +332,31 @@ int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const
                  B, H, Nq, Nk, d, scale, causal, FA2_BF16, workspace, stream);
 }
 
+int fa2_bwd_qk_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                       int d, float scale, int causal, void* stream) {
+  int st = check_sizes2(B, H, Nq, Nk, d);
+  if (st != FA2_OK) return st;
+  if ((st = check_scale_causal(scale, causal)) != FA2_OK) return st;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dout) ||
+      !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
+    return FA2_ERR_INVALID_ARG;
+  if (fa2_bwd_workspace_bytes(B, H, Nq, d) > kScratchBytes) return FA2_ERR_WORKSPACE;
+  const size_t qb = (size_t)B * H * Nq * d * 2, kb = (size_t)B * H * Nk * d * 2;
+  const size_t rows = (size_t)B * H * Nq;
+  const Span ins[6] = {span(q, qb), span(k, kb), span(v, kb),
+                       span(o, qb), span(lse, rows * 4), span(dout, qb)};
+  const Span outs[3] = {span(dq, qb), span(dk, kb), span(dv, kb)};
+  if (!disjoint(outs, 3, ins, 6)) return FA2_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if ((st = current_scratch(&ws)) != FA2_OK) return st;
+  return bwd_run(dense(q, H, Nq, d), dense(k, H, Nk, d), dense(v, H, Nk, d), dense(o, H, Nq, d), lse,
+                 dense(dout, H, Nq, d), dense(dq, H, Nq, d), dense(dk, H, Nk, d), dense(dv, H, Nk, d),
+                 B, H, Nq, Nk, d, scale, causal, FA2_BF16, ws, stream);
+}
+
+size_t fa2_bwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
 int fa2_bwd_strided(const void* q, const fa2_strides* sq, const void* k, const fa2_strides* sk,
                     const void* v, const fa2_strides* sv, const void* o, const fa2_strides* so,
                     const float* lse, const void* dout, const fa2_strides* sdo, void* dq,
@@ -343,7 +407,7 @@ const char* fa2_strerror(int status) {
     case FA2_OK: return "ok";
     case FA2_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, size, scale, causal flag or aliasing)";
     case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (supported: 64, 80, 96, 128)";
-    case FA2_ERR_WORKSPACE: return "workspace too small (see fa2_bwd_workspace_bytes)";
+    case FA2_ERR_WORKSPACE: return "workspace too small (see fa2_bwd_workspace_bytes; fa2_bwd_qk_noalloc: fa2_bwd_noalloc_max_bytes)";
     case FA2_ERR_HIP: return "HIP launch error (see fa2_last_error)";
     default: return "unknown status";
   }

@@ -51,6 +51,8 @@ _SIGNATURES = {
     "fa2_fwd": (_c_int, [_c_ptr] * 5 + [_c_int] * 4 + [_c_float, _c_int, _c_ptr]),
     "fa2_fwd_qk": (_c_int, [_c_ptr] * 5 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
     "fa2_bwd_qk": (_c_int, [_c_ptr] * 9 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "fa2_bwd_qk_noalloc": (_c_int, [_c_ptr] * 9 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
+    "fa2_bwd_noalloc_max_bytes": (_c_size, []),
     "fa2_bwd_dkdv_qk": (_c_int, [_c_ptr] * 8 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
     "fa2_bwd_dq_qk": (_c_int, [_c_ptr] * 7 + [_c_int] * 5 + [_c_float, _c_int, _c_ptr]),
     "fa2_bwd_rows_padded": (_c_int, [_c_int]),
@@ -235,6 +237,31 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None
         st = load().fa2_bwd_strided(*args, B, H, N, Nk, d, scale, int(bool(causal)), code, *ws)
     _check(st, "fa2_bwd")
     return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal=False, scale=None, stream=None):
+    """fa2_bwd_qk_noalloc: the backward with the library's fixed device scratch instead
+    of a workspace.  Contiguous bfloat16 tensors; the caller passes the outputs dq
+    [B,H,Nq,d], dk and dv [B,H,Nk,d], so that nothing is allocated.  Calls that
+    overlap in time on one GPU share (and race on) its scratch."""
+    import torch
+    B, H, N, d, Nk, kshape = _phase_shapes(q, k)
+    for name, t, shape in (("q", q, q.shape), ("k", k, kshape), ("v", v, kshape), ("o", o, q.shape),
+                           ("do", do, q.shape), ("dq", dq, q.shape), ("dk", dk, kshape), ("dv", dv, kshape)):
+        _check_qkv(name, t, shape)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name}: fa2_bwd_qk_noalloc takes bfloat16 tensors, got {t.dtype}")
+    _check_f32("lse", lse, (B, H, N))
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load().fa2_bwd_qk_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   B, H, N, Nk, d, scale, int(bool(causal)), _stream_handle(q.device, stream))
+    _check(st, "fa2_bwd_qk_noalloc")
+    return dq, dk, dv
+
+
+def bwd_noalloc_max_bytes():
+    return int(load().fa2_bwd_noalloc_max_bytes())
 
 
 def bwd_rows_padded(N):

@@ -184,6 +184,32 @@ int fa2_bwd_qk(const void* q, const void* k, const void* v, const void* o, const
                int B, int H, int Nq, int Nk, int d, float scale, int causal,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass that allocates nothing and takes no workspace: as fa2_bwd_qk,
+ * with the two padded row arrays kept in a fixed device-resident scratch array
+ * inside the library (fa2_bwd_noalloc_max_bytes() bytes, held by every GPU the
+ * library runs on until the process ends).  For callers that cannot allocate
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It calls no allocating routine.
+ *   Sizes: fa2_bwd_workspace_bytes(B,H,Nq,d) must not exceed
+ *   fa2_bwd_noalloc_max_bytes() (32 MiB: B*H*Nq up to about 4 million query
+ *   rows), else FA2_ERR_WORKSPACE and nothing is written.
+ *   The scratch of the CURRENT device is used: `stream` must belong to it.
+ *   Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ *   contents (nothing in it needs to start at zero: every row the kernels read
+ *   is written first by the same call).  Calls that overlap in time on one GPU
+ *   (on different streams, or from different threads) race on it; serialise
+ *   them, for example by issuing them on one stream.
+ * Other conventions and errors as for fa2_bwd_qk; the first call on a device
+ * looks up the scratch's device address (a failure returns FA2_ERR_HIP).
+ */
+int fa2_bwd_qk_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv,
+                       int B, int H, int Nq, int Nk, int d, float scale, int causal, void* stream);
+
+/* Bytes of device scratch behind fa2_bwd_qk_noalloc (its size limit). */
+size_t fa2_bwd_noalloc_max_bytes(void);
+
 /* Backward phase 1 (HBM-bound, elementwise): for every row i of every head,
  * delta_i = sum_k dout_ik * o_ik and lse_log2_i = lse_i * log2(e); rows from N
  * up to fa2_bwd_rows_padded(N) get delta 0 and lse_log2 +inf, and so does the

@@ -203,3 +203,21 @@ def test_strerror_and_tiles(lib):
         assert t["fwd_block_q"] == 32 * t["fwd_waves"]
     with pytest.raises(fa2.FA2Error):
         fa2.tile_config(112)
+
+
+@host_only
+def test_noalloc_backward_rejects_before_any_hip_call(lib):
+    """fa2_bwd_qk_noalloc validates like fa2_bwd_qk, and rejects sizes whose row
+    arrays exceed its fixed scratch with FA2_ERR_WORKSPACE (checked before the
+    scratch's device address is looked up, i.e. before any HIP call)."""
+    assert lib.fa2_bwd_noalloc_max_bytes() == 32 << 20
+    # (q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, stream)
+    assert lib.fa2_bwd_qk_noalloc(*P[:9], 1, 2, 10, 0, 64, 0.1, 1, None) == INVALID
+    assert lib.fa2_bwd_qk_noalloc(*P[:9], 1, 2, 10, 10, 72, 0.1, 1, None) == UNSUPPORTED
+    assert lib.fa2_bwd_qk_noalloc(*P[:9], 1, 2, 10, 10, 64, -0.1, 1, None) == INVALID
+    assert lib.fa2_bwd_qk_noalloc(*P[:8], P[1] + 4096, 1, 2, 10, 300, 64, 0.1, 1, None) == INVALID  # dv in k
+    assert lib.fa2_bwd_qk_noalloc(None, *P[1:9], 1, 2, 10, 10, 64, 0.1, 1, None) == INVALID
+    # 64 heads of 131072 rows: two fp32 row arrays of 32 MiB each do not fit
+    assert lib.fa2_bwd_workspace_bytes(1, 64, 131072, 64) > lib.fa2_bwd_noalloc_max_bytes()
+    assert lib.fa2_bwd_qk_noalloc(*P[:9], 1, 64, 131072, 131072, 64, 0.1, 1, None) == WORKSPACE
+    assert lib.fa2_last_error() == b""
