@@ -12,7 +12,8 @@ representable answer) are reported as diagnostics.
 """
 
 import os
-from concurrent.futures import ThreadPoolExecutor
+import time
+from concurrent.futures import ThreadPoolExecutor, as_completed
 
 import numpy as np
 
@@ -75,9 +76,16 @@ def compare_all_heads(got, arrs, scale, causal, dtype="bf16", workers=None, head
         limiter = threadpool_limits(limits=blas_threads, user_api="blas")
     except Exception:
         limiter = None
+    results = []
+    t0 = time.perf_counter()
     try:
         with ThreadPoolExecutor(max_workers=workers) as ex:
-            results = list(ex.map(one, range(B * H)))
+            futs = [ex.submit(one, bh) for bh in range(B * H)]
+            every = max(1, len(futs) // 8)
+            for n, f in enumerate(as_completed(futs), 1):
+                results.append(f.result())
+                if n % every == 0 or n == len(futs):
+                    print(f"  oracle: {n}/{len(futs)} heads, {time.perf_counter() - t0:.0f} s", flush=True)
     finally:
         if limiter is not None:
             limiter.unregister()
