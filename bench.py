@@ -45,7 +45,7 @@ def parse():
     # untimed steps first: the GPU's clocks take tens of milliseconds to settle
     # (B8 H16 N2048 d128: 1.39 ms per step after 5 warm-up steps, 1.32 ms after 200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(gen.WORKLOADS) + sorted(gen.EXTRA_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
@@ -55,8 +55,9 @@ def parse():
                     help="instead of the benchmark, time a library bf16 GEMM of N x N x N on random "
                          "operands (the dense MFMA rate this GPU sustains under realistic data)")
     ap.add_argument("--calibrate-mfma", action="store_true",
-                    help="instead of the benchmark, run the register-only MFMA rate probe "
-                         "(zero and random bf16 operands; build it first with --build-mfma-probe)")
+                    help="instead of the benchmark, run the MFMA rate probe: register operands (zero and "
+                         "random bf16), then one operand per MFMA read from LDS or L1 (build it first "
+                         "with --build-mfma-probe)")
     ap.add_argument("--build-mfma-probe", action="store_true",
                     help="compile the MFMA rate probe (bench_mfma_ceiling.hip) with hipcc and exit")
     ap.add_argument("--no-ratio", action="store_true",
@@ -299,7 +300,8 @@ def main():
         import subprocess
         if not os.path.exists(MFMA_PROBE_EXE):
             sys.exit(f"{MFMA_PROBE_EXE} is missing: build it with `python bench.py --build-mfma-probe`")
-        sys.exit(subprocess.run([MFMA_PROBE_EXE]).returncode)
+        rc = subprocess.run([MFMA_PROBE_EXE]).returncode
+        sys.exit(rc or subprocess.run([MFMA_PROBE_EXE, "fed"]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (heads would shard "
               "across GPUs with no communication); run with --gpus 1", file=sys.stderr)
@@ -421,7 +423,8 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO)",
+        "data": "synthetic (seeded bf16 Q/K/V/dO, " + (f"N(0,{w.sigma}^2)" if w.sigma != 1.0 else "N(0,1)")
+                + (", one x8 row of Q and K per head)" if w.spike else ")"),
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "parallelism": "single GPU"},
         "phases": {k2: round(v2, 2) for k2, v2 in phases.items()},

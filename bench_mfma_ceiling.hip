@@ -59,7 +59,84 @@ __global__ __launch_bounds__(256) void mfma_loop(const bf16x8* __restrict__ a, c
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// One operand per MFMA from memory.  SRC 0: LDS read per MFMA; 1: LDS read per
+// two MFMAs; 2: global load per MFMA (a 64 KiB window per workgroup, L1-resident
+// after the first pass).  Every address is masked into its buffer.
+template <int SRC>
+__global__ void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[32768];   // 64 KiB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 32768; i += blockDim.x) lds[i] = g[i];
+  __syncthreads();
+  const bf16x8 b = *reinterpret_cast<const bf16x8*>(lds + 8 * lane);
+  f32x16 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
+  const char* lbase = reinterpret_cast<const char*>(lds);
+  const char* gbase = reinterpret_cast<const char*>(g) + (size_t)(blockIdx.x % 64) * 65536;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 16; u += (SRC == 1 ? 2 : 1)) {
+      const uint32_t off = (uint32_t)(lane * 16 + u * 1024 + wave * 4096 + it * 256) & 0xFFF0u;
+      const bf16x8 a = SRC == 2 ? *reinterpret_cast<const bf16x8*>(gbase + off)
+                                : *reinterpret_cast<const bf16x8*>(lbase + off);
+      acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u & 3], 0, 0, 0);
+      if (SRC == 1) acc[(u + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[(u + 1) & 3], 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) s += acc[n][0] + acc[n][15];
+  out[blockIdx.x * blockDim.x + tid] = s;
+}
+
+// rates of mfma_fed: 256 workgroups (one per CU) of 4, 8 or 16 wavefronts
+int run_fed() {
+  const size_t n = (size_t)64 * 65536 / 2;   // bf16 elements: 64 windows of 64 KiB
+  std::vector<uint16_t> h(n);
+  uint32_t x = 12345u;
+  for (size_t i = 0; i < n; ++i) {
+    x = x * 1664525u + 1013904223u;
+    const float f = ((float)(x >> 9) * (1.0f / 8388608.0f) - 0.5f) * 4.f;
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    h[i] = (uint16_t)(u >> 16);
+  }
+  uint16_t* g = nullptr;
+  float* out = nullptr;
+  CHECK(hipMalloc(&g, n * 2));
+  CHECK(hipMalloc(&out, (size_t)256 * 1024 * 4));
+  CHECK(hipMemcpy(g, h.data(), n * 2, hipMemcpyHostToDevice));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  const int iters = 2048;
+  const char* names[3] = {"LDS read per MFMA", "LDS read per 2 MFMAs", "L1 global load per MFMA"};
+  for (int src = 0; src < 3; ++src)
+    for (int waves : {4, 8, 16}) {
+      float ms = 0.f;
+      for (int rep = 0; rep < 3; ++rep) {   // the last of three runs is reported
+        CHECK(hipEventRecord(e0));
+        if (src == 0) mfma_fed<0><<<256, 64 * waves>>>(g, out, iters);
+        else if (src == 1) mfma_fed<1><<<256, 64 * waves>>>(g, out, iters);
+        else mfma_fed<2><<<256, 64 * waves>>>(g, out, iters);
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+      }
+      const double flops = 256.0 * waves * iters * 16 * (2.0 * 32 * 32 * 16);
+      std::printf("{\"operand_source\": \"%s\", \"wavefronts_per_simd\": %d, \"ms\": %.3f, \"tflops\": %.1f}\n",
+                  names[src], waves / 4, ms, flops / (ms * 1e-3) / 1e12);
+    }
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
+  return 0;
+}
+
 int main(int argc, char** argv) {
+  if (argc > 1 && std::strcmp(argv[1], "fed") == 0) return run_fed();
   const int chunks = argc > 1 ? std::atoi(argv[1]) : 0;
   const size_t n_vec = (size_t)kSets * 1024;   // bf16x8 elements per operand buffer
   bf16x8 *a = nullptr, *b = nullptr;

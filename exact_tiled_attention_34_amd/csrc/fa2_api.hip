@@ -36,7 +36,7 @@ bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 // kernels' 32-bit row indices.
 int check_sizes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
-  if (d != 64 && d != 80 && d != 96 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if (d != 64 && d != 80 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED;
   const long long elems = (long long)B * H * N * d;
   if (elems >= (1LL << 31)) return FA2_ERR_INVALID_ARG;
   return FA2_OK;
@@ -406,7 +406,7 @@ const char* fa2_strerror(int status) {
   switch (status) {
     case FA2_OK: return "ok";
     case FA2_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, size, scale, causal flag or aliasing)";
-    case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (supported: 64, 80, 96, 128)";
+    case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (supported: 64, 80, 96, 128, 256)";
     case FA2_ERR_WORKSPACE: return "workspace too small (see fa2_bwd_workspace_bytes; fa2_bwd_qk_noalloc: fa2_bwd_noalloc_max_bytes)";
     case FA2_ERR_HIP: return "HIP launch error (see fa2_last_error)";
     default: return "unknown status";
@@ -417,7 +417,7 @@ const char* fa2_last_error(void) { return g_last_error; }
 
 int fa2_tile_config(int d, int* fwd_block_q, int* fwd_block_k, int* bwd_block_k, int* bwd_block_q,
                     int* fwd_waves, int* bwd_waves) {
-  if (d != 64 && d != 80 && d != 96 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if (d != 64 && d != 80 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED;
   if (!fwd_block_q || !fwd_block_k || !bwd_block_k || !bwd_block_q || !fwd_waves || !bwd_waves)
     return FA2_ERR_INVALID_ARG;
   fa2::fwd_tiles(d, fwd_block_q, fwd_block_k, fwd_waves);

@@ -406,20 +406,313 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV at head dimension 256
+// ---------------------------------------------------------------------------
+// The kernel above keeps K, V and the dK, dV accumulators of a wavefront's 32
+// keys in its registers: at D = 256 that alone would be 384 registers.  Here
+// each 32-key block is shared by a pair of wavefronts (waves p and p + PAIRS):
+// both hold all of K and V (the S and dP products reduce over every feature),
+// each accumulates dK and dV for one half of the features.  Per 64-query step:
+//   phase 1  member h computes S = Q K^T and dP = dO V^T for query half h
+//            (32 queries), then P and dS, which it keeps in registers and
+//            writes to LDS for its partner;
+//   barrier;
+//   phase 2  member h accumulates dV^T += dO^T P and dK^T += Q^T dS for its
+//            feature half over all 64 queries (its own half's P and dS from
+//            registers, the partner's from LDS).
+// One wavefront per SIMD (4 wavefronts, 64 keys per workgroup), and every tile
+// single-buffered to fit LDS: the row-major Q and dO tiles of step i + 1 are
+// written after the phase barrier of step i (phase 1 no longer reads them),
+// their transposed tiles at the start of step i + 1 (phase 2 of step i is
+// done), both from registers loaded during phase 1 of step i.
+template <int D>
+struct DkdvSplitCfg {
+  static constexpr int PAIRS = 2;
+  static constexpr int WAVES = 2 * PAIRS;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BKC = 32 * PAIRS;          // keys per workgroup
+  static constexpr int BQ = 64;                   // queries per step
+  static constexpr int NDB = D / 32;              // 32-feature blocks
+  static constexpr int NBH = NDB / 2;             // feature blocks per member
+  static constexpr int DK = D / 16;               // k-steps of S and dP
+  using RowL = RowTileW<D>;
+  static constexpr int TILE = RowL::elems(BQ);
+  static constexpr int TTILE = TrTile<D, 64>::ELEMS;
+  static constexpr int XV = 2 * 2 * 64;           // u32x4 per member: [P | dS][word quad][lane]
+  // register stages per thread: the Q and dO tiles need
+  // StagePlan<D>::THREADS_USED stagers each
+  static constexpr int NSTAGE = 2 * StagePlan<D>::THREADS_USED / THREADS;
+  static_assert(D % 64 == 0, "feature halves made of whole 32-feature blocks");
+  static_assert(2 * StagePlan<D>::THREADS_USED % THREADS == 0, "whole stages per thread");
+};
+
+template <int D, bool CAUSAL, class E>
+struct DkdvSplitWave {
+  using C = DkdvSplitCfg<D>;
+  u32x4 kf[C::DK], vf[C::DK];
+  f32x16 dkacc[C::NBH], dvacc[C::NBH];
+  int lane, lr, lh, h, key_w, key_lane;
+  int qrow[C::DK];          // row-major tiles: features 16 s + 8 lh of query 32 h + lr
+  int tr_own, tr_partner;   // transposed tiles: the member's first feature block, own / partner's query half
+
+  __device__ __forceinline__ void init_offsets() {
+#pragma unroll
+    for (int s = 0; s < C::DK; ++s) qrow[s] = C::RowL::elem(32 * h + lr, 16 * s + 8 * lh);
+    const int base = lr * TrTile<D, 64>::ROW + 8 * lh + h * C::NBH * LaneOffsets<D>::TR32;
+    tr_own = base + 32 * h;
+    tr_partner = base + 32 * (1 - h);
+  }
+
+  // S and dP for query half h (row-major tiles qt, dot), then P (packed to the
+  // storage type as soon as it is computed, under the dP products) and
+  // dS = P (dP - delta) from that P.  l2s, dls: the step's L log2 e and delta;
+  // kq0: the key position of the step's first query.  mask: some keys of the
+  // block lie past the end or above the diagonal for some of the half's
+  // queries (a run-time branch, so that one body serves every step).
+  __device__ __forceinline__ void phase1(bool mask, const uint16_t* qt, const uint16_t* dot,
+                                         const float* l2s, const float* dls, int kq0, int Nk,
+                                         float scale_log2, uint32_t (&pw)[8], uint32_t (&dsw)[8]) {
+    constexpr int NS = 2 * C::DK;   // S (t < DK), then dP
+    constexpr int PF = 3;
+    u32x4 ra[NS];
+    auto fetch = [&](int t) { ra[t] = lds_read16((t < C::DK ? qt : dot) + qrow[t % C::DK]); };
+#pragma unroll
+    for (int t = 0; t < PF; ++t) fetch(t);
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = 0.f;
+      pacc[i] = 0.f;
+    }
+    // queries of register 4 g + r: 32 h + 8 g + 4 lh + r
+    const float* l2h = l2s + 32 * h + 4 * lh;
+    const float* dlh = dls + 32 * h + 4 * lh;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if (t < C::DK) sacc = E::mfma(ra[t], kf[t], sacc);
+      else pacc = E::mfma(ra[t], vf[t - C::DK], pacc);
+      if (t + PF < NS) fetch(t + PF);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (t == C::DK + g * C::DK / 4) {
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(l2h + 8 * g);
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = exp2_fast(__builtin_fmaf(sacc[4 * g + r], scale_log2, -lv[r]));
+          if (mask) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key_lane >= Nk || (CAUSAL && key_lane > kq0 + 32 * h + 8 * g + 4 * lh + r)) x[r] = 0.f;
+          }
+          pw[2 * g] = E::pack2(x[0], x[1]);
+          pw[2 * g + 1] = E::pack2(x[2], x[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(dlh + 8 * g);
+      const float p0 = E::lo(pw[2 * g]), p1 = E::hi(pw[2 * g]);
+      const float p2 = E::lo(pw[2 * g + 1]), p3 = E::hi(pw[2 * g + 1]);
+      dsw[2 * g] = E::pack2(p0 * (pacc[4 * g] - dv[0]), p1 * (pacc[4 * g + 1] - dv[1]));
+      dsw[2 * g + 1] = E::pack2(p2 * (pacc[4 * g + 2] - dv[2]), p3 * (pacc[4 * g + 3] - dv[3]));
+    }
+  }
+
+  // dV^T += dO^T P and dK^T += Q^T dS for the member's feature blocks over the
+  // step's four 16-query chunks: the own half's two (B operands pw, dsw), then
+  // the partner's two (px: its P and dS words in LDS).
+  __device__ __forceinline__ void phase2(const uint16_t* qtt, const uint16_t* dott, const u32x4* px,
+                                         const uint32_t (&pw)[8], const uint32_t (&dsw)[8]) {
+    u32x4 xp[2], xd[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 2; ++q4) {
+      xp[q4] = px[q4 * 64 + lane];
+      xd[q4] = px[(2 + q4) * 64 + lane];
+    }
+    constexpr int NT = 4 * C::NBH;   // stage u: chunk k = u / NBH, block j = u % NBH
+    constexpr int PF = 3;
+    u32x4 ra[NT], rb[NT];
+    auto fetch = [&](int u) {
+      const int k = u / C::NBH, j = u % C::NBH;
+      const int o = (k < 2 ? tr_own : tr_partner) + 16 * (k % 2) + j * LaneOffsets<D>::TR32;
+      ra[u] = lds_read16(dott + o);
+      rb[u] = lds_read16(qtt + o);
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u) fetch(u);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int k = u / C::NBH, j = u % C::NBH;
+      const u32x4 bp = k < 2 ? acc_chunk(pw, k) : xp[k - 2];
+      const u32x4 bd = k < 2 ? acc_chunk(dsw, k) : xd[k - 2];
+      dvacc[j] = E::mfma(ra[u], bp, dvacc[j]);
+      dkacc[j] = E::mfma(rb[u], bd, dkacc[j]);
+      if (u + PF < NT) fetch(u + PF);
+    }
+  }
+};
+
+template <int D, bool CAUSAL, class E>
+__global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_kernel(
+    CView Q, CView K, CView V, CView dO, const float* __restrict__ L2,
+    const float* __restrict__ Delta, View dK, View dV, int BH, int H, int Nq, int Nk, int Npad,
+    float scale, float scale_log2) {
+  using C = DkdvSplitCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[C::TTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[C::TTILE];
+  __shared__ __attribute__((aligned(16))) u32x4 x_lds[C::WAVES][C::XV];
+  __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * C::BQ];   // [L log2e | delta]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  // Linear id -> (key block, batch*head), as in the kernel above.
+  const int bh = blockIdx.x % BH;
+  const int kblk = blockIdx.x / BH;
+  const float* L2h = L2 + (size_t)bh * Npad;
+  const float* Dh = Delta + (size_t)bh * Npad;
+  const int koff = Nk - Nq;   // causal: query i sees keys j <= i + koff
+  const int key_wg = kblk * C::BKC;
+  const int n_qblk = (Nq + C::BQ - 1) / C::BQ;
+  const int i_begin = CAUSAL ? max(0, key_wg - koff) / C::BQ : 0;
+
+  auto load_ld = [&](float* dst, int q0) {
+    if (wave == 0) {
+      const int lane = tid & 63;
+      if (lane < C::BQ / 4)
+        global_load_lds16(L2h + q0, 16u * lane, dst);
+      else if (lane < C::BQ / 2)
+        global_load_lds16(Dh + q0, 16u * (lane - C::BQ / 4), dst);
+    }
+  };
+  // Register stages: stage k of thread tid is stager (tid + k THREADS) % S of
+  // Q (first S stagers) or dO (the next S), S = StagePlan<D>::THREADS_USED.
+  constexpr int S = StagePlan<D>::THREADS_USED;
+  const uint16_t* Qh = Q.head(bh / H, bh % H);
+  const uint16_t* dOh = dO.head(bh / H, bh % H);
+  TrStage<D, 64, true> st[C::NSTAGE];
+#pragma unroll
+  for (int k = 0; k < C::NSTAGE; ++k) {
+    const int g = tid + k * C::THREADS;
+    st[k].init(g % S, g < S ? Q.sr : dO.sr);
+  }
+  auto load_stages = [&](int i) {
+#pragma unroll
+    for (int k = 0; k < C::NSTAGE; ++k) st[k].load((tid + k * C::THREADS) < S ? Qh : dOh, i * C::BQ, Nq);
+  };
+  auto store_tr = [&]() {
+#pragma unroll
+    for (int k = 0; k < C::NSTAGE; ++k) st[k].store((tid + k * C::THREADS) < S ? qt_lds : dot_lds);
+  };
+  auto store_rows = [&]() {
+#pragma unroll
+    for (int k = 0; k < C::NSTAGE; ++k)
+      st[k].template store_rows<typename C::RowL>((tid + k * C::THREADS) < S ? q_lds : do_lds);
+  };
+  if (i_begin < n_qblk) {
+    load_ld(ld_lds[0], i_begin * C::BQ);
+    load_stages(i_begin);
+    store_rows();
+  }
+
+  DkdvSplitWave<D, CAUSAL, E> w;
+  w.lane = tid & 63;
+  w.lr = w.lane & 31;
+  w.lh = w.lane >> 5;
+  w.h = wave / C::PAIRS;
+  w.key_w = key_wg + (wave % C::PAIRS) * 32;
+  w.key_lane = w.key_w + w.lr;
+  w.init_offsets();
+#pragma unroll
+  for (int s = 0; s < C::DK; ++s) {
+    u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+    if (w.key_lane < Nk) {
+      zk = ld_global16(K.head(bh / H, bh % H) + (size_t)w.key_lane * K.sr + s * 16 + 8 * w.lh);
+      zv = ld_global16(V.head(bh / H, bh % H) + (size_t)w.key_lane * V.sr + s * 16 + 8 * w.lh);
+    }
+    w.kf[s] = zk;
+    w.vf[s] = zv;
+  }
+#pragma unroll
+  for (int j = 0; j < C::NBH; ++j)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      w.dkacc[j][t] = 0.f;
+      w.dvacc[j][t] = 0.f;
+    }
+  u32x4* x_own = x_lds[wave];
+  const u32x4* x_partner = x_lds[(wave + C::PAIRS) % C::WAVES];
+  wait_vmem();
+  __syncthreads();   // the first step's row tiles and statistics are in LDS
+
+  for (int i = i_begin; i < n_qblk; ++i) {
+    const int buf = (i - i_begin) & 1;   // statistics buffer of step i
+    store_tr();   // transposed tiles of step i (phase 2 of step i - 1 is done with them)
+    const bool more = i + 1 < n_qblk;
+    // staged on every step (the last re-stages itself)
+    load_stages(more ? i + 1 : i);
+    if (more) load_ld(ld_lds[buf ^ 1], (i + 1) * C::BQ);
+    const int kq0 = i * C::BQ + koff;   // key position of the step's first query
+    // Every pair runs every step of the workgroup: a block whose keys all lie
+    // above a step's queries (at most the first step of the second pair) is
+    // masked to P = 0 rather than skipped, which keeps one straight-line body.
+    const bool need_mask = (CAUSAL && w.key_w + 31 > kq0 + 32 * w.h) || (w.key_w + 32 > Nk);
+    uint32_t pw[8], dsw[8];
+    w.phase1(need_mask, q_lds, do_lds, ld_lds[buf], ld_lds[buf] + C::BQ, kq0, Nk, scale_log2, pw, dsw);
+#pragma unroll
+    for (int q4 = 0; q4 < 2; ++q4) {
+      x_own[q4 * 64 + w.lane] = acc_chunk(pw, q4);
+      x_own[(2 + q4) * 64 + w.lane] = acc_chunk(dsw, q4);
+    }
+    __syncthreads();   // P, dS and the transposed tiles visible; the row tiles are free
+    store_rows();      // row tiles of step i + 1
+    w.phase2(qt_lds, dot_lds, x_partner, pw, dsw);
+    wait_vmem();
+    __syncthreads();   // row tiles and statistics of step i + 1 in LDS; X and the transposed tiles free
+  }
+
+  // Epilogue: dK = scale * dS^T Q, dV = P^T dO (bf16), the member's features.
+  if (w.key_lane < Nk) {
+    uint16_t* dkrow = dK.head(bh / H, bh % H) + (size_t)w.key_lane * dK.sr;
+    uint16_t* dvrow = dV.head(bh / H, bh % H) + (size_t)w.key_lane * dV.sr;
+    const int lh = (int)(__lane_id() >> 5);
+#pragma unroll
+    for (int j = 0; j < C::NBH; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = (w.h * C::NBH + j) * 32 + 8 * g + 4 * lh;
+        u32x2 wk = {E::pack2(w.dkacc[j][4 * g] * scale, w.dkacc[j][4 * g + 1] * scale),
+                    E::pack2(w.dkacc[j][4 * g + 2] * scale, w.dkacc[j][4 * g + 3] * scale)};
+        u32x2 wv = {E::pack2(w.dvacc[j][4 * g], w.dvacc[j][4 * g + 1]),
+                    E::pack2(w.dvacc[j][4 * g + 2], w.dvacc[j][4 * g + 3])};
+        *reinterpret_cast<u32x2*>(dkrow + d0) = wk;
+        *reinterpret_cast<u32x2*>(dvrow + d0) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
-  static constexpr int WAVES = 8;
+  // At D = 256 the Q and dO operands (128 registers) and dQ accumulators (128)
+  // leave room for one wavefront per SIMD: 4 wavefronts and 32-key tiles (so
+  // that the K, V and K^T tiles fit LDS twice).
+  static constexpr int WAVES = D == 256 ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per K/V tile (32 or 64)
+  static constexpr int BC = D == 256 ? 32 : 64;   // keys per K/V tile (32 or 64)
   static constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
   static constexpr int TILE = RowTile<D>::elems(BC);
   static constexpr int TTILE = TrTile<D, BC>::ELEMS;
+  // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint)
+  static constexpr int READ_AHEAD = D == 256 ? 2 : 6;
 };
 
 template <int D, bool CAUSAL, class E>
@@ -454,7 +747,7 @@ struct DqWave {
         pacc[kb] = E::mfma(lds_read16(vt + o), dof[s], pacc[kb]);
       }
     }
-    mfma_pipeline_hint<1, 2 * C::KB * C::DK, 2 * C::KB * C::DK, 6>();
+    mfma_pipeline_hint<1, 2 * C::KB * C::DK, 2 * C::KB * C::DK, C::READ_AHEAD>();
     if (mask) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -484,12 +777,12 @@ struct DqWave {
         dqacc[mb] = E::mfma(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D, C::BC>::TR32), b,
                                  dqacc[mb]);
     }
-    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
+    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, C::READ_AHEAD>();
   }
 };
 
 template <int D, bool CAUSAL, class E>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
     CView Q, CView K, CView V, CView dO, const float* __restrict__ L2,
     const float* __restrict__ Delta, View dQ, int BH, int H, int Nq, int Nk, int Npad, float scale,
     float scale_log2) {
@@ -573,9 +866,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     kstage.load(Kh, (more ? j + 1 : j) * C::BC, Nk);
     const int key0 = j * C::BC;
     // tiles from n_full on are masked; a wavefront whose rows all precede the
-    // tile's first key has nothing to do
-    if (j < n_full || !CAUSAL || key0 <= w.q_wave + 31 + koff)
-      w.tile(j >= n_full, k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
+    // tile's first key has nothing to do.  Without the causal mask every tile
+    // is visited; at D = 256 that is written as the same run-time test with a
+    // bound past every key (Nq + Nk), because the straight-line loop the
+    // compiler otherwise builds needs more than the 512 registers of a lane.
+    const bool visit = CAUSAL ? (j < n_full || key0 <= w.q_wave + 31 + koff)
+                              : (D != 256 || key0 <= w.q_wave + 31 + koff + Nq + Nk);
+    if (visit) w.tile(j >= n_full, k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
     kstage.store(kt_lds[BUF ^ 1]);
     kstage.template store_rows<RowTile<D>>(k_lds[BUF ^ 1]);
   };
@@ -619,11 +916,19 @@ template <int D, bool CAUSAL, class E>
 hipError_t launch_dkdv_t(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
                          const float* l2, const float* delta, const Strided& dk, const Strided& dv,
                          int B, int H, int Nq, int Nk, float scale, hipStream_t stream) {
-  using C = DkdvCfg<D>;
-  const int nkb = (Nk + C::BKC - 1) / C::BKC;
-  bwd_dkdv_kernel<D, CAUSAL, E><<<dim3((unsigned)(nkb * B * H)), C::THREADS, 0, stream>>>(
-      cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dk), view(dv), B * H, H, Nq, Nk,
-      bwd_rows_padded(Nq), scale, scale * kLog2e);
+  if constexpr (D == 256) {
+    using C = DkdvSplitCfg<D>;
+    const int nkb = (Nk + C::BKC - 1) / C::BKC;
+    bwd_dkdv_split_kernel<D, CAUSAL, E><<<dim3((unsigned)(nkb * B * H)), C::THREADS, 0, stream>>>(
+        cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dk), view(dv), B * H, H, Nq, Nk,
+        bwd_rows_padded(Nq), scale, scale * kLog2e);
+  } else {
+    using C = DkdvCfg<D>;
+    const int nkb = (Nk + C::BKC - 1) / C::BKC;
+    bwd_dkdv_kernel<D, CAUSAL, E><<<dim3((unsigned)(nkb * B * H)), C::THREADS, 0, stream>>>(
+        cview(q), cview(k), cview(v), cview(dout), l2, delta, view(dk), view(dv), B * H, H, Nq, Nk,
+        bwd_rows_padded(Nq), scale, scale * kLog2e);
+  }
   return hipGetLastError();
 }
 
@@ -670,7 +975,12 @@ hipError_t launch_bwd_dq(const Strided& q, const Strided& k, const Strided& v, c
 }
 
 void bwd_tiles(int d, int* block_k, int* block_q, int* waves) {
-  (void)d;
+  if (d == 256) {
+    *block_k = DkdvSplitCfg<256>::BKC;
+    *block_q = DkdvSplitCfg<256>::BQ;
+    *waves = DkdvSplitCfg<256>::WAVES;
+    return;
+  }
   *block_k = DkdvCfg<128>::BKC;
   *block_q = DkdvCfg<128>::BQ;
   *waves = DkdvCfg<128>::WAVES;

@@ -50,6 +50,11 @@ struct BF16 {
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  // acc + lo(w) + hi(w) in one instruction (v_dot2c_f32_bf16 with (1, 1))
+  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
 };
 
 struct F16 {
@@ -67,6 +72,11 @@ struct F16 {
   }
   static __device__ __forceinline__ float hi(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  // acc + lo(w) + hi(w) in one instruction (v_dot2c_f32_f16 with (1, 1))
+  static __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
   }
 };
 
@@ -190,7 +200,7 @@ struct TileDma {
       if (first < P::TOTAL) {
         int base_row;
         uint32_t o;
-        const int i = P::PERIODIC ? 0 : t;
+        const int i = P::off_index(t);
         P::source(off[i], lrow[i], t, row0, n_rows, R, &base_row, &o);
         global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
       }
@@ -304,6 +314,7 @@ inline hipError_t dispatch(int d, int causal, int dtype, F&& f) {
     case 80:  return by_causal(std::integral_constant<int, 80>{});
     case 96:  return by_causal(std::integral_constant<int, 96>{});
     case 128: return by_causal(std::integral_constant<int, 128>{});
+    case 256: return by_causal(std::integral_constant<int, 256>{});
     default:  return hipErrorInvalidValue;
   }
 }

@@ -47,15 +47,18 @@ namespace {
 // a large workgroup (8 wavefronts at D = 64 and 128, 12 at D = 96) shares each
 // staged K/V tile among more query rows; one per CU at D = 96 and 128, two at
 // D = 64 (four wavefronts per SIMD in 124 VGPRs); at D = 80 two workgroups of
-// 4 wavefronts are as fast as 12 wavefronts and 5 % faster than 8.
+// 4 wavefronts are as fast as 12 wavefronts and 5 % faster than 8.  At D = 256
+// a wavefront's Q operands (64 registers) and O accumulators (128) leave room
+// for one wavefront per SIMD only: 4 wavefronts, 32-key tiles (the 64-key
+// K and V^T tiles would not fit LDS twice).
 template <int D, bool CAUSAL = false>
 struct FwdCfg {
-  static constexpr int WAVES = D == 96 ? 12 : D == 80 ? 4 : 8;
+  static constexpr int WAVES = D == 96 ? 12 : D == 80 || D == 256 ? 4 : 8;
   static constexpr int WGS_PER_CU = D == 64 || D == 80 ? 2 : 1;
   static constexpr int WAVES_PER_SIMD = WAVES * WGS_PER_CU / 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per K/V tile (32 or 64)
+  static constexpr int BC = D == 256 ? 32 : 64;   // keys per K/V tile (32 or 64)
   static constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
   static constexpr int DP = (D + 31) / 32 * 32;   // O^T rows padded to whole 32-row MFMA blocks
   static constexpr int NDB = DP / 32;
@@ -71,6 +74,9 @@ struct FwdCfg {
   static constexpr int TILE = RowTile<D>::elems(STAGE);
   static constexpr int VTILE = TrTile<D, BC>::ELEMS;
   static constexpr int VSTAGERS = StagePlan<D, BC>::THREADS_USED;   // threads per V tile
+  // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint);
+  // fewer at D = 96, whose three wavefronts per SIMD have 170 registers each
+  static constexpr int READ_AHEAD = D == 96 ? 4 : 6;
 };
 
 template <int D, bool CAUSAL, class E>
@@ -79,7 +85,10 @@ struct FwdWave {
   u32x4 qf[C::DK];
   f32x16 oacc[C::NDB];
   f32x16 sc[1][C::KB];  // scores of the current tile
-  float m_run, l_run;
+  // running max, running sum of P (for L) and running sum of P as rounded to
+  // the storage type (the weights the P V product actually uses: O is divided
+  // by this sum, so its rows are exact convex combinations of V's rows)
+  float m_run, l_run, lr_run;
   int lane, lr, lh, q_wave, q_lane;
   int key_last;        // causal: last key this lane's query may see (q_lane + Nk - Nq)
   int key_last_wave;   // the same for the wavefront's last query row
@@ -96,7 +105,7 @@ struct FwdWave {
         sacc[kb] = E::mfma(lds_read16(kt + off.rd(s, kb)), qf[s],
                                 sacc[kb]);
     }
-    mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, 6>();
+    mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, C::READ_AHEAD>();
   }
 
   // Online-softmax step on the scores of the tile starting at key0: P packed to
@@ -131,7 +140,7 @@ struct FwdWave {
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2_fast((m_run - m_use) * scale_log2);
     const float mc = m_use * scale_log2;
-    float rs = 0.f;
+    float rs = 0.f, rsr = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -139,9 +148,12 @@ struct FwdWave {
         const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -mc));
         const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][i + 1], scale_log2, -mc));
         rs += p0 + p1;
-        pw[kb][i >> 1] = E::pack2(p0, p1);
+        const uint32_t w = E::pack2(p0, p1);
+        pw[kb][i >> 1] = w;
+        rsr = E::add_pair(w, rsr);
       }
     l_run = l_run * alpha + rs;
+    lr_run = lr_run * alpha + rsr;
     m_run = m_new;
     any = __any(grow);
     return alpha;
@@ -164,7 +176,7 @@ struct FwdWave {
         oacc[mb] = E::mfma(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D, CAUSAL>::BC>::TR32), b,
                                 oacc[mb]);
     }
-    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, 6>();
+    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, C::READ_AHEAD>();
   }
 };
 
@@ -248,6 +260,7 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
   w.key_last_wave = w.q_wave + 31 + koff;
   w.m_run = -INFINITY;
   w.l_run = 0.f;
+  w.lr_run = 0.f;
   w.off.init(w.lane);
 #pragma unroll
   for (int mb = 0; mb < C::NDB; ++mb)
@@ -292,11 +305,13 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
                                  scale_log2);
   }
 
-  // Epilogue: one division by the row sum, then O (bf16) and L (fp32, natural
-  // log).  A row that saw no key (l = 0) gets O = 0 and L = -inf.
+  // Epilogue: one division by the row sum of the rounded P, then O (bf16) and
+  // L (fp32, natural log, from the unrounded sum).  A row that saw no key
+  // (l = 0) gets O = 0 and L = -inf.
   const float l_tot = w.l_run + swap_halves(w.l_run);
+  const float lr_tot = w.lr_run + swap_halves(w.lr_run);
   if (w.q_lane < Nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     uint16_t* orow = Oh + (size_t)w.q_lane * O.sr;
 #pragma unroll
     for (int mb = 0; mb < C::NDB; ++mb)
@@ -347,6 +362,7 @@ void fwd_tiles(int d, int* block_q, int* block_k, int* waves) {
   if (d == 64) set(FwdCfg<64>{});
   else if (d == 80) set(FwdCfg<80>{});
   else if (d == 96) set(FwdCfg<96>{});
+  else if (d == 256) set(FwdCfg<256>{});
   else set(FwdCfg<128>{});
 }
 

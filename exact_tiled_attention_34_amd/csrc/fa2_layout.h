@@ -25,23 +25,24 @@ namespace fa2 {
 // chunk order inside a row is permuted per row so that 16-byte reads of one
 // chunk by 32 consecutive rows (the MFMA operands whose reduction index is
 // the feature: Q K^T, dO V^T, K Q^T, V dO^T) spread over the LDS banks.
-// D = 128 (16 chunks) and D = 64 (8 chunks) use an XOR of the chunk index;
-// D = 80 (10 chunks) and D = 96 (12 chunks) pad every row by one chunk slot
-// instead (11 and 13 slots: 176- and 208-byte rows, whose first 16 rows start
-// on 16 distinct 4-bank groups).
+// D = 256 (32 chunks), D = 128 (16 chunks) and D = 64 (8 chunks) use an XOR
+// of the chunk index (at D = 256 of its low four bits); D = 80 (10 chunks) and
+// D = 96 (12 chunks) pad every row by one chunk slot instead (11 and 13 slots:
+// 176- and 208-byte rows, whose first 16 rows start on 16 distinct 4-bank
+// groups).
 // ---------------------------------------------------------------------------
 template <int D>
 struct RowTile {
   static constexpr int CH = D / 8;
   static constexpr bool PADDED = (CH & (CH - 1)) != 0;
   static constexpr int SLOTS = PADDED ? CH + 1 : CH;
-  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16), "unsupported head dim");
+  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16 || CH == 32), "unsupported head dim");
 
   // XOR key of a row (an involution on the chunk index); depends on row % 16.
   static FA2_HD int swz(int row) {
     if constexpr (PADDED) {
       return 0;
-    } else if constexpr (CH == 16) {
+    } else if constexpr (CH >= 16) {
       return (4 * (row & 3)) | ((row >> 2) & 3);
     } else {
       const int g = (row >> 1) & 7;
@@ -79,7 +80,8 @@ struct RowTile {
 // RowTile (16 consecutive rows of one chunk on 16 distinct 4-bank groups) and
 // also spread rows 4 apart:
 //   D = 128:     the XOR key also takes rows 16..63 of each 64-row period
-//                into account (row bits 4-5 flip key bits 2-3);
+//                into account (row bits 4-5 flip key bits 2-3); D = 256
+//                applies the same key to the low four chunk bits;
 //   D = 64:      a spare slot after every 4 rows, and row bit 1 flips chunk
 //                bit 2;
 //   D = 80, 96:  the RowTile row padding plus a spare slot after every 16 rows.
@@ -92,15 +94,15 @@ struct RowTileW {
   static constexpr int CH = D / 8;
   static constexpr bool PADDED = (CH & (CH - 1)) != 0;
   static constexpr int SLOTS = PADDED ? CH + 1 : CH;
-  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16), "unsupported head dim");
+  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16 || CH == 32), "unsupported head dim");
   // 16-byte slots per 32 rows
-  static constexpr int SLOTS32 = PADDED ? 32 * SLOTS + 2 : CH == 16 ? 512 : 32 * 8 + 8;
+  static constexpr int SLOTS32 = PADDED ? 32 * SLOTS + 2 : CH >= 16 ? 32 * CH : 32 * 8 + 8;
 
   static FA2_HD int slot(int row, int chunk) {
     if constexpr (PADDED) {
       return row * SLOTS + (row >> 4) + chunk;
-    } else if constexpr (CH == 16) {
-      return row * 16 + (chunk ^ ((4 * ((row & 3) ^ ((row >> 4) & 3))) | ((row >> 2) & 3)));
+    } else if constexpr (CH >= 16) {
+      return row * CH + (chunk ^ ((4 * ((row & 3) ^ ((row >> 4) & 3))) | ((row >> 2) & 3)));
     } else {
       return row * 8 + (row >> 2) + (chunk ^ (4 * ((row >> 1) & 1)));
     }
@@ -108,7 +110,7 @@ struct RowTileW {
   static FA2_HD int elem(int row, int col) { return slot(row, col >> 3) * 8 + (col & 7); }
   // bf16 elements to reserve for a tile of `rows` rows (a multiple of 32).
   static constexpr int elems(int rows) { return rows / 32 * SLOTS32 * 8; }
-  static constexpr int perm(int s, int b) { return CH == 16 ? (s ^ (4 * (b & 1))) : s; }
+  static constexpr int perm(int s, int b) { return CH >= 16 ? (s ^ (4 * (b & 1))) : s; }
   static constexpr int block(int b) { return b * SLOTS32 * 8; }
 };
 
@@ -148,9 +150,11 @@ struct TrTile {
 // writes lane l's 16 bytes at its wavefront base + 16 l).  Rows of the source
 // tensor lie R elements apart (R >= D, a multiple of 8: the row pitch, D for a
 // contiguous [.., N, D] tensor).  The chunk swizzle repeats every 16 rows, so
-// when a pass spans a multiple of 16 rows (PERIODIC) a lane's source offset
-// relative to the first row of its pass is the same in every pass and one
-// register holds it.
+// when a pass spans whole rows and PERIOD passes span a multiple of 16 rows
+// (PERIODIC) a lane's source offset in pass t is that of pass t % PERIOD moved
+// by whole rows, and PERIOD registers hold every offset (one at D = 64 and
+// 128 with 256 or more threads; two at D = 256 with 256 threads, whose passes
+// span 8 rows).
 // ---------------------------------------------------------------------------
 template <int D, int ROWS, int THREADS>
 struct DmaPlan {
@@ -158,17 +162,21 @@ struct DmaPlan {
   static constexpr int TOTAL = ROWS * L::SLOTS;   // 16-byte slots per tile
   static constexpr int ITER = (TOTAL + THREADS - 1) / THREADS;
   static constexpr int RPP = THREADS / L::SLOTS;  // rows per pass (PERIODIC only)
-  static constexpr bool PERIODIC = !L::PADDED && THREADS % L::SLOTS == 0 && RPP % 16 == 0;
-  static constexpr int NOFF = PERIODIC ? 1 : ITER;
+  static constexpr bool PERIODIC =
+      !L::PADDED && THREADS % L::SLOTS == 0 && RPP > 0 && (RPP % 16 == 0 || 16 % RPP == 0);
+  static constexpr int PERIOD = !PERIODIC ? 1 : RPP % 16 == 0 ? 1 : 16 / RPP;   // passes
+  static constexpr int NOFF = PERIODIC ? (PERIOD < ITER ? PERIOD : ITER) : ITER;
   static_assert(TOTAL % 64 == 0 && THREADS % 64 == 0, "whole wavefronts per pass");
 
   // First slot of pass t for wavefront `wave` (uniform); the pass exists for
   // that wavefront iff the result is < TOTAL.
   static FA2_HD int pass_slot(int wave, int t) { return wave * 64 + t * THREADS; }
+  // Which stored offset serves pass t, and the first pass of its period.
+  static FA2_HD int off_index(int t) { return PERIODIC ? t % PERIOD : t; }
+  static FA2_HD int period_start(int t) { return PERIODIC ? t - t % PERIOD : 0; }
 
-  // Row (from the first row of the tile, or of the pass when PERIODIC) and
-  // byte offset of the source chunk of lane `lane` in pass t, stored once per
-  // lane (t < NOFF).
+  // Row (from the first row of the tile) and byte offset of the source chunk
+  // of lane `lane` in pass t, stored once per lane (t < NOFF).
   static FA2_HD int lane_row(int wave, int lane, int t) { return (pass_slot(wave, t) + lane) / L::SLOTS; }
   static FA2_HD uint32_t lane_offset(int wave, int lane, int t, int R) {
     const int s = pass_slot(wave, t) + lane;
@@ -176,20 +184,21 @@ struct DmaPlan {
   }
 
   // Source of pass t given the stored offset `off` and row `lrow` (those of
-  // pass PERIODIC ? 0 : t): the load reads the 16 bytes at
+  // pass off_index(t)): the load reads the 16 bytes at
   //   head + base_row * R elements + byte_off bytes.
   // Rows at or past n_rows are clamped to n_rows - 1.  Requires
   // 0 <= row0 < n_rows; then base_row <= row0 (it never points past the
   // tensor) and byte_off is a non-negative offset into it.
   static FA2_HD void source(uint32_t off, int lrow, int t, int row0, int n_rows, int R, int* base_row,
                             uint32_t* byte_off) {
+    const int shift = period_start(t) * RPP;   // rows between the stored pass and pass t
     if (row0 + ROWS <= n_rows) {
       // full tile: for PERIODIC the pass moves the scalar base instead
-      *base_row = PERIODIC ? row0 + t * RPP : row0;
+      *base_row = row0 + (PERIODIC ? shift : 0);
       *byte_off = off;
       return;
     }
-    const int rt = lrow + (PERIODIC ? t * RPP : 0);   // row of the chunk within the tile
+    const int rt = lrow + (PERIODIC ? shift : 0);   // row of the chunk within the tile
     const int last = n_rows - 1 - row0;
     const int rc = rt < last ? rt : last;
     *base_row = row0;

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
 
 FA2_OK = 0
 FA2_BF16, FA2_FP16 = 0, 1
-SUPPORTED_HEAD_DIMS = (64, 80, 96, 128)
+SUPPORTED_HEAD_DIMS = (64, 80, 96, 128, 256)
 
 _lib = None
 

@@ -167,6 +167,13 @@ def make_gpt_block(B, S, hidden, seed=0, w_std=0.02):
     return {n: round_to_bf16_bits(a) for n, a in (("x", x), ("w_qkv", w_qkv), ("w_out", w_out), ("dy", dy))}
 
 
+# Further shapes for measurement only (not among the five configured
+# workloads): head dimension 256 on a long causal sequence.
+EXTRA_WORKLOADS = {
+    "d256": Workload("d256", "B1 H16 N8192 d256 causal (head dim 256)", 1, 16, 8192, 256, True),
+}
+
+
 def make_workload(key, seed=0):
-    w = WORKLOADS[key]
+    w = WORKLOADS[key] if key in WORKLOADS else EXTRA_WORKLOADS[key]
     return w, make_arrays(w.B, w.H, w.N, w.d, seed=seed, sigma=w.sigma, spike=w.spike)

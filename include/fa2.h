@@ -41,7 +41,7 @@
  *    element strides of each bf16 tensor (fa2_strides).  q, k, v, o, dout, dq, dk, dv hold bfloat16 values stored as
  *    16-bit words.  lse is fp32 [B, H, N]; the backward's delta and lse_log2
  *    are fp32 [B, H, fa2_bwd_rows_padded(N)].
- *  - Supported: B, H, N >= 1 with B*H*N*d < 2^31; d in {64, 80, 96, 128};
+ *  - Supported: B, H, N >= 1 with B*H*N*d < 2^31; d in {64, 80, 96, 128, 256};
  *    causal in {0, 1}; scale finite and > 0 (the usual 1/sqrt(d)).
  *  - Every pointer must be non-null and 16-byte aligned.  Outputs must not
  *    overlap inputs or each other.
@@ -69,7 +69,7 @@ extern "C" {
 typedef enum fa2_status {
     FA2_OK = 0,
     FA2_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, aliasing, bad scale/causal */
-    FA2_ERR_UNSUPPORTED = 2, /* head dimension not in {64, 80, 96, 128} */
+    FA2_ERR_UNSUPPORTED = 2, /* head dimension not in {64, 80, 96, 128, 256} */
     FA2_ERR_WORKSPACE = 3,   /* workspace too small */
     FA2_ERR_HIP = 4          /* a HIP launch failed; see fa2_last_error() */
 } fa2_status;

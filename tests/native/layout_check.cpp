@@ -49,7 +49,7 @@ void check_dma(int max_n, int R) {
             CHECK(slot < P::TOTAL, "D=%d slot %d", D, slot);
             if (slot >= P::TOTAL) continue;
             written[slot]++;
-            const int ti = P::PERIODIC ? 0 : t;
+            const int ti = P::off_index(t);
             const uint32_t off = P::lane_offset(wave, lane, ti, R);
             int base_row;
             uint32_t o;
@@ -231,6 +231,17 @@ int main() {
     check_stage<64, 32, 512, RowTile<64>>(max_n, 64 * mult);
     check_stage<128, 32, 512, RowTile<128>>(max_n, 128 * mult);
   }
+  // head dim 256: 32-key tiles of the forward and dQ kernels (256 threads),
+  // 64-query tiles of the dK/dV kernel staged by 256 threads in two halves
+  for (int mult : {1, 2, 3}) {
+    check_dma<256, 32, 256>(max_n, 256 * mult);
+    check_stage<256, 32, 256, RowTile<256>>(max_n, 256 * mult);
+    check_stage<256, 64, 512, RowTileW<256>>(max_n, 256 * mult);
+  }
+  check_dma<256, 32, 256>(max_n, 264);
+  check_stage<256, 64, 512, RowTileW<256>>(max_n, 264);
+  check_reads<256, 32>();
+  check_reads<256, 64, RowTileW<256>>();
   check_reads<64, 32>();
   check_reads<128, 32>();
   check_reads<64>();

@@ -62,7 +62,7 @@ def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=128, d=64, sc
 @host_only
 @pytest.mark.parametrize("kw,want", [
     (dict(N=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID),
-    (dict(d=112), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(d=112), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(d=192), UNSUPPORTED), (dict(d=512), UNSUPPORTED),
     (dict(causal=2), INVALID), (dict(causal=-1), INVALID),
     (dict(scale=0.0), INVALID), (dict(scale=-0.125), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
@@ -197,7 +197,7 @@ def test_strerror_and_tiles(lib):
         assert lib.fa2_strerror(s)
     assert b"unknown" in lib.fa2_strerror(99)
     assert lib.fa2_last_error() == b""
-    for d in (64, 80, 96, 128):
+    for d in (64, 80, 96, 128, 256):
         t = fa2.tile_config(d)
         assert t["fwd_block_q"] % 32 == 0 and t["bwd_block_k"] % 32 == 0
         assert t["fwd_block_q"] == 32 * t["fwd_waves"]

@@ -85,7 +85,7 @@ def assert_full_parity(arrs, causal, scale, label="", dtype="bf16"):
 # small shapes, every element
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", [(1, 1, 1), (1, 1, 12), (1, 2, 64), (2, 1, 127), (1, 1, 128),
                                    (1, 2, 129), (2, 2, 200), (1, 1, 256), (1, 1, 333),
@@ -110,7 +110,8 @@ def test_other_scales(scale):
                                          (1, 1, 64, 1000, 128), (2, 2, 300, 130, 80),
                                          (1, 2, 513, 200, 128), (1, 1, 129, 257, 80),
                                          (1, 2, 150, 270, 96), (1, 1, 1, 1, 64), (2, 1, 70, 1, 128),
-                                         (1, 3, 200, 333, 128), (1, 2, 600, 190, 64), (1, 1, 800, 300, 96)])
+                                         (1, 3, 200, 333, 128), (1, 2, 600, 190, 64), (1, 1, 800, 300, 96),
+                                         (1, 2, 77, 500, 256), (2, 1, 300, 130, 256), (1, 1, 1, 200, 256)])
 def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=3000 + Nq + Nk + d)
     label = f"B{B} H{H} Nq{Nq} Nk{Nk} d{d} causal={causal}"
@@ -133,7 +134,7 @@ def test_separate_query_and_key_lengths(causal, B, H, Nq, Nk, d):
 
 # float16 storage: the same kernels with the f16 matrix instruction, through the
 # strided entry points (contiguous, [B, N, H, d] views, Nq != Nk)
-@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", [(1, 1, 12), (2, 2, 200), (1, 1, 333)])
 def test_fp16_small_shapes(d, causal, B, H, N):
@@ -145,7 +146,7 @@ def test_fp16_small_shapes(d, causal, B, H, N):
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(1, 2, 77, 300, 128, True), (2, 2, 250, 100, 80, True),
                                                  (1, 3, 130, 130, 64, False), (1, 2, 1500, 2100, 128, True),
-                                                 (2, 1, 1024, 1024, 96, False)])
+                                                 (2, 1, 1024, 1024, 96, False), (1, 2, 300, 420, 256, True)])
 def test_fp16_views_and_lengths(B, H, Nq, Nk, d, causal):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=7100 + Nq + Nk, dtype="fp16")
     q, k, v, do = (to_dev(arrs[n], "fp16") for n in ("q", "k", "v", "do"))
@@ -251,11 +252,24 @@ def test_workload_full_size(key):
     assert_any_size_properties(key, out, arrs)
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(1, 4, 4096, True), (2, 2, 2000, False)])
+def test_head_dim_256_long(B, H, N, causal):
+    """Head dimension 256 at a long sequence (many key and query blocks per head,
+    a ragged tail in the second case): every head against the oracle."""
+    d = 256
+    arrs = gen.make_arrays(B, H, N, d, seed=2560 + N)
+    w = gen.Workload("d256", f"B{B} H{H} N{N} d256", B, H, N, d, causal)
+    out = run_gpu(arrs, causal, w.scale)
+    assert_whole_tensor_parity(f"d256 B{B} H{H} N{N} causal={causal}", out, arrs, w)
+    out["scale"] = w.scale
+    assert_any_size_properties("d256", out, arrs)
+
+
 # ---------------------------------------------------------------------------
 # closed forms on the GPU
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_uniform_scores_give_mean_of_v(d, causal):
     N = 300
@@ -287,7 +301,7 @@ def test_constant_v_gives_ones(causal):
     assert err <= 4e-3, err
 
 
-@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
 def test_single_token_and_causal_row0(d):
     arrs = gen.make_arrays(2, 3, 1, d, seed=23)
     out = run_gpu(arrs, True, 1.0 / math.sqrt(d))
@@ -330,7 +344,7 @@ def test_causal_isolation_is_bitwise():
         assert same_o and same_l, i
 
 
-@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
 def test_every_output_element_written(d):
     B, H, N = 1, 3, 333
     arrs = gen.make_arrays(B, H, N, d, seed=27)
@@ -348,7 +362,7 @@ def test_every_output_element_written(d):
         assert finite, f"{name} has unwritten (NaN) elements"
 
 
-@pytest.mark.parametrize("d", [64, 80, 96, 128])
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
 def test_run_to_run_determinism(d):
     """No kernel accumulates with atomics (dQ has its own pass), so every output,
     dQ included, is bit-identical from run to run."""
@@ -373,7 +387,8 @@ def test_errors_raise():
         fa2.fwd(q.float(), q, q)
 
 
-@pytest.mark.parametrize("d,causal,N", [(64, True, 200), (80, False, 129), (96, True, 150), (128, True, 333)])
+@pytest.mark.parametrize("d,causal,N", [(64, True, 200), (80, False, 129), (96, True, 150), (128, True, 333),
+                                        (256, True, 333), (256, False, 200)])
 def test_phases_compose_to_bwd(d, causal, N):
     """fa2_bwd == preprocess + dkdv + dq called one by one (the way bench.py times them)."""
     B, H = 2, 2
