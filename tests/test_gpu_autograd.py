@@ -41,7 +41,8 @@ def rel(got, ref):
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(2, 2, 150, 150, 64, True), (1, 3, 97, 230, 128, True),
-                                                 (2, 1, 200, 120, 80, False), (1, 2, 64, 64, 96, True)])
+                                                 (2, 1, 200, 120, 80, False), (1, 2, 64, 64, 96, True),
+                                                 (1, 2, 150, 190, 256, True)])
 def test_autograd_attention_matches_oracle(B, H, Nq, Nk, d, causal):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=4000 + Nq + d)
     q, k, v = (to_dev(arrs[n], grad=True) for n in ("q", "k", "v"))
@@ -114,7 +115,8 @@ def padded_rows(t, pad=8):
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [(2, 3, 140, 140, 128, True), (1, 2, 77, 260, 80, False),
-                                                 (2, 2, 200, 90, 64, True), (1, 2, 129, 129, 96, False)])
+                                                 (2, 2, 200, 90, 64, True), (1, 2, 129, 129, 96, False),
+                                                 (1, 2, 100, 100, 256, True)])
 def test_strided_views_match_oracle(B, H, Nq, Nk, d, causal):
     arrs = gen.make_arrays_qk(B, H, Nq, Nk, d, seed=5000 + Nq + Nk + d)
     q, k, v, do = (to_dev(arrs[n]) for n in ("q", "k", "v", "do"))
@@ -143,7 +145,8 @@ def test_strided_views_match_oracle(B, H, Nq, Nk, d, causal):
 
 
 @pytest.mark.parametrize("B,S,H,d,causal,dtype", [(2, 150, 2, 80, True, "bf16"), (1, 257, 3, 128, False, "bf16"),
-                                                   (2, 64, 4, 64, True, "bf16"), (2, 150, 2, 80, True, "fp16")])
+                                                   (2, 64, 4, 64, True, "bf16"), (2, 150, 2, 80, True, "fp16"),
+                                                   (1, 130, 2, 256, True, "bf16")])
 def test_qkvpacked_matches_oracle(B, S, H, d, causal, dtype):
     arrs = gen.make_arrays(B, H, S, d, seed=6000 + S + d, dtype=dtype)
     qkv_bits = np.stack([arrs[n].transpose(0, 2, 1, 3) for n in ("q", "k", "v")], axis=2)  # [B, S, 3, H, d]

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 from exact_tiled_attention_34_amd import fa2  # noqa: E402
 
 
-@pytest.mark.parametrize("d,causal", [(64, True), (128, False), (80, True)])
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False), (80, True), (256, True)])
 def test_graph_replays_match_eager(d, causal):
     B, H, N = 2, 3, 300
     scale = 1.0 / math.sqrt(d)

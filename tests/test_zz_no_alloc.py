@@ -38,6 +38,7 @@ def both_ways(B, H, Nq, Nk, d, causal, seed):
 
 @pytest.mark.parametrize("seq", [
     [(2, 3, 700, 700, 128, True), (1, 2, 150, 150, 64, False)],
+    [(1, 2, 500, 500, 256, True), (1, 1, 100, 230, 256, False)],
     [(1, 4, 1024, 1024, 80, True), (2, 1, 77, 300, 96, True), (1, 1, 1, 1, 64, False)],
 ])
 def test_noalloc_matches_workspace_backward(seq):
