@@ -39,6 +39,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // rounded to the storage type to nearest-even.
 struct BF16 {
   static constexpr int kId = 0;
+  static constexpr uint16_t kOne = 0x3F80;   // 1.0
   static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -59,6 +60,7 @@ struct BF16 {
 
 struct F16 {
   static constexpr int kId = 1;
+  static constexpr uint16_t kOne = 0x3C00;   // 1.0
   static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -271,13 +273,14 @@ struct TrStage {
   }
 };
 
-// Zero the padding feature rows [D, DP) of a transposed tile (once; staging
-// never writes them).
+// Fill the padding feature rows [D, DP) of a transposed tile (once; staging
+// never writes them): zero, or with first_row = the storage type's 1.0, the
+// first padding row holds ones (a product with it sums over the tokens).
 template <int D, int TOK = 64>
-__device__ __forceinline__ void tr_zero_pad(uint16_t* t, int tid, int nthreads) {
+__device__ __forceinline__ void tr_zero_pad(uint16_t* t, int tid, int nthreads, uint16_t first_row = 0) {
   using T = TrTile<D, TOK>;
   if constexpr (T::DP != D)
-    for (int i = tid; i < (T::DP - D) * T::ROW; i += nthreads) t[D * T::ROW + i] = 0;
+    for (int i = tid; i < (T::DP - D) * T::ROW; i += nthreads) t[D * T::ROW + i] = i < T::ROW ? first_row : 0;
 }
 
 // One bf16 [B, H, N, D] tensor addressed through element strides (the last

@@ -77,6 +77,14 @@ struct FwdCfg {
   // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint);
   // fewer at D = 96, whose three wavefronts per SIMD have 170 registers each
   static constexpr int READ_AHEAD = D == 96 ? 4 : 6;
+  // When V^T is padded to whole 32-feature blocks (D = 80), its first padding
+  // row holds ones: O^T row D then accumulates the row sum of the rounded P
+  // (scaled with O by every rescale), at no cost, instead of a sum in the
+  // vector unit.  That row sits in accumulator block D / 32, register
+  // ONES_REG, of the lanes of half ONES_HALF.
+  static constexpr bool ONES_ROW = DP != D;
+  static constexpr int ONES_REG = 4 * ((D % 32) / 8) + D % 4;
+  static constexpr int ONES_HALF = (D % 8) / 4;
 };
 
 template <int D, bool CAUSAL, class E>
@@ -150,7 +158,7 @@ struct FwdWave {
         rs += p0 + p1;
         const uint32_t w = E::pack2(p0, p1);
         pw[kb][i >> 1] = w;
-        rsr = E::add_pair(w, rsr);
+        if constexpr (!C::ONES_ROW) rsr = E::add_pair(w, rsr);
       }
     l_run = l_run * alpha + rs;
     lr_run = lr_run * alpha + rsr;
@@ -232,7 +240,7 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   for (int b = 0; b < 2; ++b)
-    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[b][t], tid, C::THREADS);
+    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[b][t], tid, C::THREADS, E::kOne);
 
   // Linear workgroup id -> (row block, batch*head).  Consecutive ids take
   // different heads, so with the round-robin dispatch over the 8 XCDs all row
@@ -309,7 +317,14 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
   // L (fp32, natural log, from the unrounded sum).  A row that saw no key
   // (l = 0) gets O = 0 and L = -inf.
   const float l_tot = w.l_run + swap_halves(w.l_run);
-  const float lr_tot = w.lr_run + swap_halves(w.lr_run);
+  float lr_tot;
+  if constexpr (C::ONES_ROW) {
+    const float own = w.oacc[D / 32][C::ONES_REG];
+    const float other = swap_halves(own);
+    lr_tot = w.lh == C::ONES_HALF ? own : other;
+  } else {
+    lr_tot = w.lr_run + swap_halves(w.lr_run);
+  }
   if (w.q_lane < Nq) {
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     uint16_t* orow = Oh + (size_t)w.q_lane * O.sr;
