@@ -78,22 +78,30 @@ def parse():
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
     # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("40b93f02b47a6977", "c2", "bwd_dkdv"): 1359205265,
-    ("40b93f02b47a6977", "c2", "bwd_dq"): 740472364,
-    ("40b93f02b47a6977", "c2", "bwd_preprocess"): 137427265,
-    ("40b93f02b47a6977", "c2", "fwd"): 672329195,
-    ("40b93f02b47a6977", "c3", "bwd_dkdv"): 1420435343,
-    ("40b93f02b47a6977", "c3", "bwd_dq"): 809649517,
-    ("40b93f02b47a6977", "c3", "bwd_preprocess"): 140566881,
-    ("40b93f02b47a6977", "c3", "fwd"): 780752408,
-    ("40b93f02b47a6977", "c4", "bwd_dkdv"): 869634717,
-    ("40b93f02b47a6977", "c4", "bwd_dq"): 706051529,
-    ("40b93f02b47a6977", "c4", "bwd_preprocess"): 137429281,
-    ("40b93f02b47a6977", "c4", "fwd"): 548783344,
-    ("40b93f02b47a6977", "c5", "bwd_dkdv"): 1782683570,
-    ("40b93f02b47a6977", "c5", "bwd_dq"): 1016626945,
-    ("40b93f02b47a6977", "c5", "bwd_preprocess"): 174125858,
-    ("40b93f02b47a6977", "c5", "fwd"): 1620821836,
+    ("c670850b0f8c2893", "c1", "bwd_dkdv"): 127358,
+    ("c670850b0f8c2893", "c1", "bwd_dq"): 101886,
+    ("c670850b0f8c2893", "c1", "bwd_preprocess"): 89598,
+    ("c670850b0f8c2893", "c1", "fwd"): 88318,
+    ("c670850b0f8c2893", "c2", "bwd_dkdv"): 1359289906,
+    ("c670850b0f8c2893", "c2", "bwd_dq"): 740476444,
+    ("c670850b0f8c2893", "c2", "bwd_preprocess"): 137428318,
+    ("c670850b0f8c2893", "c2", "fwd"): 672325245,
+    ("c670850b0f8c2893", "c3", "bwd_dkdv"): 1420485359,
+    ("c670850b0f8c2893", "c3", "bwd_dq"): 809646939,
+    ("c670850b0f8c2893", "c3", "bwd_preprocess"): 140568798,
+    ("c670850b0f8c2893", "c3", "fwd"): 762922139,
+    ("c670850b0f8c2893", "c4", "bwd_dkdv"): 869348112,
+    ("c670850b0f8c2893", "c4", "bwd_dq"): 701174150,
+    ("c670850b0f8c2893", "c4", "bwd_preprocess"): 137429086,
+    ("c670850b0f8c2893", "c4", "fwd"): 541150701,
+    ("c670850b0f8c2893", "c5", "bwd_dkdv"): 1782705580,
+    ("c670850b0f8c2893", "c5", "bwd_dq"): 1016431597,
+    ("c670850b0f8c2893", "c5", "bwd_preprocess"): 174125902,
+    ("c670850b0f8c2893", "c5", "fwd"): 1617790744,
+    ("c670850b0f8c2893", "d256", "bwd_dkdv"): 866515644,
+    ("c670850b0f8c2893", "d256", "bwd_dq"): 671293837,
+    ("c670850b0f8c2893", "d256", "bwd_preprocess"): 135866630,
+    ("c670850b0f8c2893", "d256", "fwd"): 500551011,
 }
 
 
