@@ -22,12 +22,14 @@
 //                          tile (then every factor is exactly 1), which after
 //                          the first tiles is the common case
 //                          ("FlashAttention-2" summary page, "How It Works" 2:
-//                          scaling kept out of the inner loop).  The largest P
-//                          of a row is exactly 1, so it is exact in bf16.
+//                          scaling kept out of the inner loop).  Except at
+//                          head dim 64 the maximum pass itself is skipped
+//                          while every P against the current m stays <= 2^8.
 //   O^T += V^T P^T         bf16 MFMA; V^T is a transposed LDS tile, P^T comes
 //                          straight from registers
-// After the last tile, O is divided by l once ("FlashAttention-2" summary page,
-// "How It Works" 2) and L = (c m + log2 l) ln 2 is stored.
+// After the last tile, O is divided once by the row sum of P as rounded for
+// the product ("FlashAttention-2" summary page, "How It Works" 2) and
+// L = (c m + log2 l) ln 2 is stored.
 //
 // K tiles go global -> LDS directly (no registers); V tiles are transposed on
 // the way (global -> registers -> LDS).  Tiles are staged in stages of one or
@@ -83,9 +85,26 @@ struct FwdCfg {
   // vector unit.  That row sits in accumulator block D / 32, register
   // ONES_REG, of the lanes of half ONES_HALF.
   static constexpr bool ONES_ROW = DP != D;
+  // The softmax step first tries P against the current reference maximum
+  // (no maximum pass); the scores stay live until it knows whether the
+  // maximum pass is due.  That fits the registers of every head dimension but
+  // 64, whose four wavefronts per SIMD have 128 registers each (it spills).
+  // Forward time on MI355X: B1 H16 N16384 d128 causal -7 %, B8 H16 N2048 d128
+  // -7 %, B1 H16 N8192 d256 causal -19 %.
+  static constexpr bool LAZY = D != 64;
+  // With the lazy maximum, one softmax step per 32-key block instead of one
+  // per tile, so that the exponentials of block 1 can run under the products
+  // of block 0: B2 H32 N8192 d80 causal -6 %, B2 H24 N8192 d96 causal -5 %
+  // (and at D = 96 the whole-tile step spills), but B1 H16 N16384 d128
+  // causal +6 %.
+  static constexpr bool BLOCK_STEPS = LAZY && KB == 2 && (D == 80 || D == 96);
   static constexpr int ONES_REG = 4 * ((D % 32) / 8) + D % 4;
   static constexpr int ONES_HALF = (D % 8) / 4;
 };
+
+// Bound on a lane's share of a row's P sum above which the softmax step moves
+// the row's reference maximum (so every P stays at most 2^8).
+constexpr float kLazyBound = 256.f;
 
 template <int D, bool CAUSAL, class E>
 struct FwdWave {
@@ -116,27 +135,72 @@ struct FwdWave {
     mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, C::READ_AHEAD>();
   }
 
-  // Online-softmax step on the scores of the tile starting at key0: P packed to
-  // bf16 (pw), running max and sum updated.  Returns the factor that O must be
-  // multiplied by (exactly 1 in every lane whose max did not grow); `any` tells
-  // whether some lane's factor differs from 1.  mask: the tile may hold keys past
-  // the end of the sequence or above the diagonal for some of this wave's rows
-  // (a run-time branch over the scores only: one tile body for every tile, so
-  // the O accumulators keep one register assignment through the loop).
-  __device__ __forceinline__ float softmax(f32x16 (&sacc)[C::KB], uint32_t (&pw)[C::KB][8], bool& any,
-                                           bool mask, int key0, int Nk, float scale_log2) {
-    if (mask) {
+  // P = 2^(c S - mc) for score blocks [KB0, KB0 + NKB), packed to the storage
+  // type (pw), with the row sums of P in fp32 (rs) and of P as rounded (rsr).
+  template <int KB0, int NKB>
+  __device__ __forceinline__ void exps(const f32x16 (&sacc)[C::KB], uint32_t (&pw)[C::KB][8], float mc,
+                                       float scale_log2, float& rs, float& rsr) const {
+    float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = KB0; kb < KB0 + NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= Nk || (CAUSAL && key > key_last)) sacc[kb][i] = -INFINITY;
-        }
-    }
-    float mx = fmaxf(sacc[0][0], sacc[0][1]);
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -mc));
+        const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][i + 1], scale_log2, -mc));
+        const float pp = p0 + p1;
+        r0 = kb == KB0 && i == 0 ? pp : r0 + pp;
+        const uint32_t w = E::pack2(p0, p1);
+        pw[kb][i >> 1] = w;
+        if constexpr (!C::ONES_ROW) r1 = E::add_pair(w, r1);
+      }
+    rs = r0;
+    rsr = r1;
+  }
+
+  // Scores of keys past the end of the sequence, and above the diagonal, to
+  // -inf: applied to a whole tile that may hold such keys for some of this
+  // wave's rows, as a run-time branch over the scores only (one tile body for
+  // every tile, so the O accumulators keep one register assignment through the
+  // loop).
+  __device__ __forceinline__ void apply_mask(f32x16 (&sacc)[C::KB], int key0, int Nk) const {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (key >= Nk || (CAUSAL && key > key_last)) sacc[kb][i] = -INFINITY;
+      }
+  }
+
+  // Online-softmax step on score blocks [KB0, KB0 + NKB): P packed to the
+  // storage type (pw), running sums updated.  Returns the factor that O must
+  // be multiplied by; `any` tells whether some lane's factor differs from 1.
+  //
+  // LAZY: the reference m of a row need not be its running maximum; any m
+  // works as long as no 2^(c (S - m)) overflows, and the final division by the
+  // row sum cancels it ("FlashAttention-2" summary page, "How It Works" 2: the
+  // scaling leaves the inner loop).  So P is first computed against the
+  // current m, without a maximum pass over the scores, and kept if every
+  // lane's share of the row sum is at most 2^8 (then so is every P, and no
+  // rescale is due).  Otherwise (the first block, where m = -inf makes the sum
+  // inf or NaN, or a score more than 8 / c above m) m moves to the row maximum
+  // as below and P is recomputed.
+  template <int KB0, int NKB>
+  __device__ __forceinline__ float softmax(f32x16 (&sacc)[C::KB], uint32_t (&pw)[C::KB][8], bool& any,
+                                           float scale_log2) {
+    float rs, rsr;
+    if constexpr (C::LAZY) {
+      exps<KB0, NKB>(sacc, pw, m_run * scale_log2, scale_log2, rs, rsr);
+      if (__all(rs <= kLazyBound)) {   // false for NaN
+        l_run += rs;
+        lr_run += rsr;
+        any = false;
+        return 1.f;
+      }
+    }
+    float mx = fmaxf(sacc[KB0][0], sacc[KB0][1]);
+#pragma unroll
+    for (int kb = KB0; kb < KB0 + NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = fmaxf(mx, swap_halves(mx));
@@ -147,19 +211,7 @@ struct FwdWave {
     const float m_new = grow ? mx : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2_fast((m_run - m_use) * scale_log2);
-    const float mc = m_use * scale_log2;
-    float rs = 0.f, rsr = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -mc));
-        const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][i + 1], scale_log2, -mc));
-        rs += p0 + p1;
-        const uint32_t w = E::pack2(p0, p1);
-        pw[kb][i >> 1] = w;
-        if constexpr (!C::ONES_ROW) rsr = E::add_pair(w, rsr);
-      }
+    exps<KB0, NKB>(sacc, pw, m_use * scale_log2, scale_log2, rs, rsr);
     l_run = l_run * alpha + rs;
     lr_run = lr_run * alpha + rsr;
     m_run = m_new;
@@ -174,17 +226,29 @@ struct FwdWave {
       for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
   }
 
-  // O^T (d x query) += V^T (d x 16 keys) P^T (16 keys x query), four key chunks.
+  // O^T (d x query) += V^T (d x 16 keys) P^T (16 keys x query) over the 16-key
+  // chunks of score blocks [KB0, KB0 + NKB).
+  template <int KB0, int NKB>
   __device__ __forceinline__ void pv(const uint16_t* vt, const uint32_t (&pw)[C::KB][8]) {
 #pragma unroll
-    for (int c = 0; c < C::BC / 16; ++c) {
+    for (int c = 2 * KB0; c < 2 * (KB0 + NKB); ++c) {
       const u32x4 b = acc_chunk(pw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
         oacc[mb] = E::mfma(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D, CAUSAL>::BC>::TR32), b,
                                 oacc[mb]);
     }
-    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, C::READ_AHEAD>();
+    mfma_pipeline_hint<2, 2 * NKB * C::NDB, 2 * NKB * C::NDB, C::READ_AHEAD>();
+  }
+
+  // Softmax and O += V P over score blocks [KB0, KB0 + NKB) of the tile.
+  template <int KB0, int NKB>
+  __device__ __forceinline__ void softmax_pv(const uint16_t* vt, float scale_log2) {
+    uint32_t pw[C::KB][8];
+    bool any;
+    const float alpha = softmax<KB0, NKB>(sc[0], pw, any, scale_log2);
+    if (any) rescale(alpha);
+    pv<KB0, NKB>(vt, pw);
   }
 };
 
@@ -219,11 +283,15 @@ __device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, F
     // a wavefront whose rows all precede the tile's first key has nothing to do
     if (j < n_tiles && (!mask || !CAUSAL || j * C::BC <= w.key_last_wave)) {
       w.scores(k_lds[PAR] + sub * RowTile<D>::block(C::KB), w.sc[0]);
-      uint32_t pw[C::KB][8];
-      bool any;
-      const float alpha = w.softmax(w.sc[0], pw, any, mask, j * C::BC, Nk, scale_log2);
-      if (any) w.rescale(alpha);
-      w.pv(v_lds[PAR][sub], pw);
+      if (mask) w.apply_mask(w.sc[0], j * C::BC, Nk);
+      // With the lazy maximum each 32-key block is a softmax step of its own,
+      // so the exponentials of block 1 can run under the products of block 0.
+      if constexpr (C::BLOCK_STEPS) {
+        w.template softmax_pv<0, 1>(v_lds[PAR][sub], scale_log2);
+        w.template softmax_pv<1, 1>(v_lds[PAR][sub], scale_log2);
+      } else {
+        w.template softmax_pv<0, C::KB>(v_lds[PAR][sub], scale_log2);
+      }
     }
   }
   if (vdo) vstage.store(v_lds[PAR ^ 1][vsub]);

@@ -292,6 +292,49 @@ def test_uniform_scores_give_mean_of_v(d, causal):
     assert dk_max == 0.0, dk_max
 
 
+# Per-head score growth per 64 keys for test_growing_scores: the running row
+# maximum climbs by 12 (far past the 2^8 bound on P, every tile), 6 and 3 (P
+# sums past 2^8 on some tiles, no single P near it), 0.5 (never past it after
+# the first tile) and falls by 3.
+GROWTH = (12.0, 6.0, 3.0, 0.5, -3.0)
+
+
+@pytest.mark.parametrize("d", [64, 80, 96, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores(d, causal):
+    """Scores that ramp along the keys: the forward's softmax must move each
+    row's reference maximum tile after tile (and, where P against the old
+    reference is first tried, fall back to the maximum pass on exactly the
+    tiles that need it).  Q = u + Q0/4 and K_j = t_j sqrt(d) u/|u|^2 + K0/4 for
+    a head's first query u, so the scores are about t_j = g j / 64 plus noise.
+
+    O and L are compared element by element.  The gradients are not: with keys
+    of norm up to ~t_j and a nearly one-hot softmax, dQ = scale sum_j dS_ij K_j
+    cancels almost completely, so the rounding of dS to the storage type alone
+    (relative 2^-9, times t_j ~ 80) moves dQ by several per cent of its norm;
+    no backward kernel depends on how the forward reached its maximum."""
+    N, H = 333, len(GROWTH)
+    arrs = gen.make_arrays(1, H, N, d, seed=31 + d)
+    x = decode(arrs)
+    u = x["q"][:, :, :1, :]
+    t = np.array(GROWTH)[None, :, None, None] * np.arange(N)[None, None, :, None] / 64.0
+    q = u + 0.25 * x["q"]
+    k = t * math.sqrt(d) * u / np.sum(u * u, axis=-1, keepdims=True) + 0.25 * x["k"]
+    arrs["q"] = gen.round_to_bf16_bits(q.astype(np.float32))
+    arrs["k"] = gen.round_to_bf16_bits(k.astype(np.float32))
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd = (to_dev(arrs[n]) for n in ("q", "k", "v"))
+    o, lse = fa2.fwd(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    x = decode(arrs)
+    o_ref, l_ref = A.forward(x["q"], x["k"], x["v"], scale, causal)
+    err_o = float(np.max(np.abs(to_f64(o) - o_ref)))
+    err_l = float(np.max(np.abs(to_f64(lse) - l_ref)))
+    print(f"growing scores d{d} causal={causal}: O {err_o:.3g} L {err_l:.3g}", flush=True)
+    assert err_o <= O_TOL, err_o
+    assert err_l <= L_TOL, err_l
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_constant_v_gives_ones(causal):
     arrs = gen.make_arrays(1, 1, 257, 128, seed=22)
