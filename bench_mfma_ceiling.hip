@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256) void mfma_loop(const bf16x8* __restrict__ a, c
 
 // One operand per MFMA from memory.  SRC 0: LDS read per MFMA; 1: LDS read per
 // two MFMAs; 2: global load per MFMA (a 64 KiB window per workgroup, L1-resident
-// after the first pass).  Every address is masked into its buffer.
+// after the first pass); 3: two transposing 8-byte LDS reads per MFMA
+// (ds_read_b64_tr_b16, consecutive lanes 8 bytes apart).  Every address is
+// masked into its buffer.
 template <int SRC>
 __global__ void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out, int iters) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[32768];   // 64 KiB
@@ -80,8 +82,18 @@ __global__ void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out
 #pragma unroll
     for (int u = 0; u < 16; u += (SRC == 1 ? 2 : 1)) {
       const uint32_t off = (uint32_t)(lane * 16 + u * 1024 + wave * 4096 + it * 256) & 0xFFF0u;
-      const bf16x8 a = SRC == 2 ? *reinterpret_cast<const bf16x8*>(gbase + off)
-                                : *reinterpret_cast<const bf16x8*>(lbase + off);
+      bf16x8 a;
+      if constexpr (SRC == 3) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const uint32_t o0 = (uint32_t)(lane * 8 + u * 1024 + wave * 4096 + it * 256) & 0xFFF8u;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lbase + o0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lbase + (o0 ^ 512u)));
+        const s16x4 both[2] = {lo, hi};
+        a = __builtin_bit_cast(bf16x8, both);
+      } else {
+        a = SRC == 2 ? *reinterpret_cast<const bf16x8*>(gbase + off) : *reinterpret_cast<const bf16x8*>(lbase + off);
+      }
       acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u & 3], 0, 0, 0);
       if (SRC == 1) acc[(u + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[(u + 1) & 3], 0, 0, 0);
     }
@@ -113,15 +125,17 @@ int run_fed() {
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
   const int iters = 2048;
-  const char* names[3] = {"LDS read per MFMA", "LDS read per 2 MFMAs", "L1 global load per MFMA"};
-  for (int src = 0; src < 3; ++src)
+  const char* names[4] = {"LDS read per MFMA", "LDS read per 2 MFMAs", "L1 global load per MFMA",
+                          "two transposing 8-byte LDS reads per MFMA"};
+  for (int src = 0; src < 4; ++src)
     for (int waves : {4, 8, 16}) {
       float ms = 0.f;
       for (int rep = 0; rep < 3; ++rep) {   // the last of three runs is reported
         CHECK(hipEventRecord(e0));
         if (src == 0) mfma_fed<0><<<256, 64 * waves>>>(g, out, iters);
         else if (src == 1) mfma_fed<1><<<256, 64 * waves>>>(g, out, iters);
-        else mfma_fed<2><<<256, 64 * waves>>>(g, out, iters);
+        else if (src == 2) mfma_fed<2><<<256, 64 * waves>>>(g, out, iters);
+        else mfma_fed<3><<<256, 64 * waves>>>(g, out, iters);
         CHECK(hipEventRecord(e1));
         CHECK(hipEventSynchronize(e1));
         CHECK(hipEventElapsedTime(&ms, e0, e1));

@@ -117,29 +117,30 @@ __device__ __forceinline__ void sched_fence() {
 #endif
 }
 
-template <int SYNC, int N_MFMA, int N_READS, int I, int READS>
+template <int SYNC, int N_MFMA, int N_READS, int RPM, int I, int READS>
 __device__ __forceinline__ void mfma_pipeline_step() {
   if constexpr (I < N_MFMA) {
+    constexpr int more = READS + RPM <= N_READS ? RPM : N_READS - READS;
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);                 // one MFMA
-    if constexpr (READS < N_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, SYNC);  // one read
+    if constexpr (more > 0) __builtin_amdgcn_sched_group_barrier(0x100, more, SYNC);  // its reads
 #endif
-    mfma_pipeline_step<SYNC, N_MFMA, N_READS, I + 1, (READS < N_READS ? READS + 1 : READS)>();
+    mfma_pipeline_step<SYNC, N_MFMA, N_READS, RPM, I + 1, READS + more>();
   }
 }
 
-// Scheduling hint for a run of N_MFMA MFMAs fed by N_READS LDS reads: issue
-// DEPTH reads first, then one more read after each MFMA, so DEPTH operand loads
-// stay in flight and the LDS latency hides behind the matrix cores instead of
-// stalling every MFMA.  Emitted right after the code it describes, in the same
-// basic block; SYNC tells independent hints apart.
-template <int SYNC, int N_MFMA, int N_READS, int DEPTH>
+// Scheduling hint for a run of N_MFMA MFMAs fed by N_READS LDS reads, RPM
+// reads per MFMA: issue DEPTH reads first, then RPM more after each MFMA, so
+// DEPTH operand loads stay in flight and the LDS latency hides behind the
+// matrix cores instead of stalling every MFMA.  Emitted right after the code
+// it describes, in the same basic block; SYNC tells independent hints apart.
+template <int SYNC, int N_MFMA, int N_READS, int DEPTH, int RPM = 1>
 __device__ __forceinline__ void mfma_pipeline_hint() {
   constexpr int first = DEPTH < N_READS ? DEPTH : N_READS;
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_sched_group_barrier(0x100, first, SYNC);
 #endif
-  mfma_pipeline_step<SYNC, N_MFMA, N_READS, 0, first>();
+  mfma_pipeline_step<SYNC, N_MFMA, N_READS, RPM, 0, first>();
 }
 
 // One 16-byte global -> LDS load per lane (global_load_lds_dwordx4 with a
@@ -171,15 +172,16 @@ __device__ __forceinline__ void global_load_lds16(const void* base, uint32_t byt
 }
 
 // Copies ROWS-row tiles of one head (rows R elements apart, D features) into
-// a RowTile in LDS with direct global -> LDS loads, following DmaPlan: the
+// a RowTile (or a TrRowTile: LT) in LDS with direct global -> LDS loads,
+// following DmaPlan (slots the layout keeps constant are skipped): the
 // per-lane source offsets are computed once (init); a full tile then costs
 // one load per chunk and no vector arithmetic.  Rows past n_rows (the ragged
 // last tile) are clamped to the last row: finite data that the caller masks
 // or weights by zero.  issue() returns immediately; wait_vmem() and a
 // workgroup barrier make the tile visible.
-template <int D, int ROWS, int THREADS>
+template <int D, int ROWS, int THREADS, class LT = RowTile<D>>
 struct TileDma {
-  using P = DmaPlan<D, ROWS, THREADS>;
+  using P = DmaPlan<D, ROWS, THREADS, LT>;
   uint32_t off[P::NOFF];
   int lrow[P::NOFF];
   int wave, R;
@@ -204,7 +206,11 @@ struct TileDma {
         uint32_t o;
         const int i = P::off_index(t);
         P::source(off[i], lrow[i], t, row0, n_rows, R, &base_row, &o);
-        global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+        if constexpr (LT::HAS_CONST) {
+          if (off[i] != P::kSkip) global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+        } else {
+          global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+        }
       }
     }
   }
@@ -331,6 +337,19 @@ inline View view(const Strided& t) {
 
 __device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// MFMA operand from two transposed reads of a row-major tile (TrRowTile):
+// p0 and p1 are the lane's addresses of reads 0 and 1 (tokens 4h..4h+3 and
+// 8+4h..8+4h+3 of the chunk, feature lane % 32 of the block).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 lds_read_tr(const uint16_t* p0, const uint16_t* p1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  const u32x4 v = {ua[0], ua[1], ub[0], ub[1]};
+  return v;
 }
 
 // MFMA B operand for 16 tokens (chunk c of a 32-row accumulator pair) from

@@ -31,11 +31,10 @@
 // the product ("FlashAttention-2" summary page, "How It Works" 2) and
 // L = (c m + log2 l) ln 2 is stored.
 //
-// K tiles go global -> LDS directly (no registers); V tiles are transposed on
-// the way (global -> registers -> LDS).  Tiles are staged in stages of one or
-// two tiles, double-buffered: the loads of stage J+1 are issued right after
-// the barrier that opens stage J, and its transposed V tiles are written once
-// stage J's products are issued.
+// K and V tiles go global -> LDS directly (no registers), both row-major; the
+// P V product reads V^T with transposing LDS reads.  Tiles are staged in
+// stages of one or two tiles, double-buffered: the copies of stage J+1 are
+// issued right after the barrier that opens stage J.
 #include <type_traits>
 
 #include "fa2_device.h"
@@ -74,8 +73,18 @@ struct FwdCfg {
   static constexpr int SUB = D == 64 && !CAUSAL ? 2 : 1;
   static constexpr int STAGE = SUB * BC;          // keys per stage
   static constexpr int TILE = RowTile<D>::elems(STAGE);
-  static constexpr int VTILE = TrTile<D, BC>::ELEMS;
-  static constexpr int VSTAGERS = StagePlan<D, BC>::THREADS_USED;   // threads per V tile
+  // V tiles: at D <= 96 copied row-major like K and read transposed by the
+  // P V product (TrRowTile: no register staging, which at four and three
+  // wavefronts per SIMD competes with the softmax for the vector unit:
+  // B4 H32 N4096 d64 causal forward -4 %, B2 H32 N8192 d80 causal and
+  // B2 H24 N8192 d96 causal -2 %); at D = 128 and 256 transposed on the way
+  // through registers (TrTile), which measured 2-4 % faster there
+  // (B1 H16 N16384 d128 causal, B1 H16 N8192 d256 causal).
+  static constexpr bool V_DMA = D <= 96;
+  using VL = TrRowTile<D>;
+  static constexpr int VSUB = TrTile<D, BC>::ELEMS;                // one staged V^T tile
+  static constexpr int VTILE = V_DMA ? VL::elems(STAGE) : SUB * VSUB;
+  static constexpr int VSTAGERS = StagePlan<D, BC>::THREADS_USED;   // threads per staged V tile
   // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint);
   // fewer at D = 96, whose three wavefronts per SIMD have 170 registers each
   static constexpr int READ_AHEAD = D == 96 ? 4 : 6;
@@ -120,6 +129,15 @@ struct FwdWave {
   int key_last;        // causal: last key this lane's query may see (q_lane + Nk - Nq)
   int key_last_wave;   // the same for the wavefront's last query row
   LaneOffsets<D, FwdCfg<D, CAUSAL>::BC> off;
+  int vtr[2][C::NDB];  // V_DMA: TrRowTile offsets of the V^T reads 0 and 1 per feature block
+
+  __device__ __forceinline__ void init_offsets() {
+    off.init(lane);
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+      for (int mb = 0; mb < C::NDB; ++mb) vtr[rd][mb] = C::VL::tr_elem(lane, rd, mb);
+  }
 
   // S^T (64 keys x this wave's 32 queries) of the K tile at kt.
   __device__ __forceinline__ void scores(const uint16_t* kt, f32x16 (&sacc)[C::KB]) const {
@@ -227,18 +245,28 @@ struct FwdWave {
   }
 
   // O^T (d x query) += V^T (d x 16 keys) P^T (16 keys x query) over the 16-key
-  // chunks of score blocks [KB0, KB0 + NKB).
+  // chunks of score blocks [KB0, KB0 + NKB).  V_DMA: V^T by two transposed
+  // reads of the row-major V tile vt per operand; otherwise one read of the
+  // transposed tile vt.
   template <int KB0, int NKB>
   __device__ __forceinline__ void pv(const uint16_t* vt, const uint32_t (&pw)[C::KB][8]) {
 #pragma unroll
     for (int c = 2 * KB0; c < 2 * (KB0 + NKB); ++c) {
       const u32x4 b = acc_chunk(pw[c >> 1], c & 1);
 #pragma unroll
-      for (int mb = 0; mb < C::NDB; ++mb)
-        oacc[mb] = E::mfma(lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D, CAUSAL>::BC>::TR32), b,
-                                oacc[mb]);
+      for (int mb = 0; mb < C::NDB; ++mb) {
+        u32x4 a;
+        if constexpr (C::V_DMA)
+          a = lds_read_tr(vt + vtr[0][mb] + c * C::VL::ROWS16, vt + vtr[1][mb] + c * C::VL::ROWS16);
+        else
+          a = lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D, CAUSAL>::BC>::TR32);
+        oacc[mb] = E::mfma(a, b, oacc[mb]);
+      }
     }
-    mfma_pipeline_hint<2, 2 * NKB * C::NDB, 2 * NKB * C::NDB, C::READ_AHEAD>();
+    if constexpr (C::V_DMA)
+      mfma_pipeline_hint<2, 2 * NKB * C::NDB, 4 * NKB * C::NDB, C::READ_AHEAD, 2>();
+    else
+      mfma_pipeline_hint<2, 2 * NKB * C::NDB, 2 * NKB * C::NDB, C::READ_AHEAD>();
   }
 
   // Softmax and O += V P over score blocks [KB0, KB0 + NKB) of the tile.
@@ -253,16 +281,19 @@ struct FwdWave {
 };
 
 // Stage J (PAR = J % 2, a compile-time constant so that LDS buffers are
-// immediate offsets) holds tiles J*SUB .. J*SUB + SUB - 1: issue the loads of
-// stage J+1, then per tile scores, softmax, the rare rescale and
-// O += V(j) P(j), then the transposed store of this thread's V tile of stage
-// J+1.  Tiles from n_full on are masked.  vsub: the tile of a stage whose V
-// this thread stages (>= SUB: none).
+// immediate offsets) holds tiles J*SUB .. J*SUB + SUB - 1: issue the copies of
+// stage J+1's K (and V_DMA: V) or the register loads of this thread's staged V
+// tile, then per tile scores, softmax, the rare rescale and O += V(j) P(j),
+// then (staged V) the transposed store of that V tile.  Tiles from n_full on
+// are masked.  vsub: the tile of a stage whose V this thread stages (>= SUB:
+// none).
 template <int D, bool CAUSAL, class E, int PAR>
 __device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D, CAUSAL>::BC>& vstage,
                                           const TileDma<D, FwdCfg<D, CAUSAL>::STAGE, FwdCfg<D, CAUSAL>::THREADS>& kdma,
+                                          const TileDma<D, FwdCfg<D, CAUSAL>::STAGE, FwdCfg<D, CAUSAL>::THREADS,
+                                                        TrRowTile<D>>& vdma,
                                           uint16_t (*k_lds)[FwdCfg<D, CAUSAL>::TILE],
-                                          uint16_t (*v_lds)[FwdCfg<D, CAUSAL>::SUB][FwdCfg<D, CAUSAL>::VTILE],
+                                          uint16_t (*v_lds)[FwdCfg<D, CAUSAL>::VTILE],
                                           const uint16_t* Kh, const uint16_t* Vh, int J, int vsub,
                                           int n_tiles, int n_full, int Nk, float scale_log2) {
   using C = FwdCfg<D, CAUSAL>;
@@ -270,11 +301,15 @@ __device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, F
   __syncthreads();   // stage J is in LDS; every wave is done with the other buffer
   const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
   const bool more = J + 1 < n_stages;
-  if (more) kdma.issue(k_lds[PAR ^ 1], Kh, (J + 1) * C::STAGE, Nk);
-  // The V stage is loaded and stored on every stage (the last one re-stages
-  // itself into the idle buffer), so its registers never live across stages.
+  if (more) {
+    kdma.issue(k_lds[PAR ^ 1], Kh, (J + 1) * C::STAGE, Nk);
+    if constexpr (C::V_DMA) vdma.issue(v_lds[PAR ^ 1], Vh, (J + 1) * C::STAGE, Nk);
+  }
+  // A staged V tile is loaded and stored on every stage (the last one
+  // re-stages itself into the idle buffer), so its registers never live
+  // across stages.
   const int jv = (more ? J + 1 : J) * C::SUB + vsub;
-  const bool vdo = vsub < C::SUB && jv < n_tiles;
+  const bool vdo = !C::V_DMA && vsub < C::SUB && jv < n_tiles;
   if (vdo) vstage.load(Vh, jv * C::BC, Nk);
 #pragma unroll
   for (int sub = 0; sub < C::SUB; ++sub) {
@@ -287,14 +322,14 @@ __device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, F
       // With the lazy maximum each 32-key block is a softmax step of its own,
       // so the exponentials of block 1 can run under the products of block 0.
       if constexpr (C::BLOCK_STEPS) {
-        w.template softmax_pv<0, 1>(v_lds[PAR][sub], scale_log2);
-        w.template softmax_pv<1, 1>(v_lds[PAR][sub], scale_log2);
+        w.template softmax_pv<0, 1>(v_lds[PAR] + sub * (C::V_DMA ? (C::BC / 16) * C::VL::ROWS16 : C::VSUB), scale_log2);
+        w.template softmax_pv<1, 1>(v_lds[PAR] + sub * (C::V_DMA ? (C::BC / 16) * C::VL::ROWS16 : C::VSUB), scale_log2);
       } else {
-        w.template softmax_pv<0, C::KB>(v_lds[PAR][sub], scale_log2);
+        w.template softmax_pv<0, C::KB>(v_lds[PAR] + sub * (C::V_DMA ? (C::BC / 16) * C::VL::ROWS16 : C::VSUB), scale_log2);
       }
     }
   }
-  if (vdo) vstage.store(v_lds[PAR ^ 1][vsub]);
+  if (vdo) vstage.store(v_lds[PAR ^ 1] + vsub * C::VSUB);
 }
 
 template <int D, bool CAUSAL, class E>
@@ -302,13 +337,23 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
                                                      float* __restrict__ LSE, int BH, int H, int Nq,
                                                      int Nk, float scale_log2) {
   using C = FwdCfg<D, CAUSAL>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::SUB][C::VTILE];
+  __shared__ __attribute__((aligned(256))) uint16_t k_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(256))) uint16_t v_lds[2][C::VTILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  for (int b = 0; b < 2; ++b)
-    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[b][t], tid, C::THREADS, E::kOne);
+  if constexpr (!C::V_DMA) {
+    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[0] + t * C::VSUB, tid, C::THREADS, E::kOne);
+    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[1] + t * C::VSUB, tid, C::THREADS, E::kOne);
+  } else if constexpr (C::VL::HAS_CONST) {
+    // features 80..95 of every V row: (1, 0, .., 0) and zeros (slots 10, 11)
+    for (int i = tid; i < 2 * C::STAGE; i += C::THREADS) {
+      const u32x4 one = {(uint32_t)E::kOne, 0u, 0u, 0u}, zero = {0u, 0u, 0u, 0u};
+      uint16_t* row = v_lds[i / C::STAGE] + C::VL::elem(i % C::STAGE, 80);
+      *reinterpret_cast<u32x4*>(row) = one;
+      *reinterpret_cast<u32x4*>(row + 8) = zero;
+    }
+  }
 
   // Linear workgroup id -> (row block, batch*head).  Consecutive ids take
   // different heads, so with the round-robin dispatch over the 8 XCDs all row
@@ -337,7 +382,7 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
   w.m_run = -INFINITY;
   w.l_run = 0.f;
   w.lr_run = 0.f;
-  w.off.init(w.lane);
+  w.init_offsets();
 #pragma unroll
   for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
@@ -352,15 +397,21 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
   // tiles [0, n_full) hold only keys that every row of the block may see
   const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
-  // Stage 0 into LDS (K directly, V transposed through registers: thread tid
-  // stages V tile tid / VSTAGERS of each stage).
-  TrStage<D, C::BC> vstage;
+  // Stage 0 into LDS: K by direct copies; V by direct copies (V_DMA) or
+  // transposed through registers (thread tid stages V tile tid / VSTAGERS of
+  // each stage).
   TileDma<D, C::STAGE, C::THREADS> kdma;
-  const int vsub = tid / C::VSTAGERS;
-  vstage.init(vsub < C::SUB ? tid % C::VSTAGERS : C::VSTAGERS, V.sr);
+  TileDma<D, C::STAGE, C::THREADS, typename C::VL> vdma;
+  TrStage<D, C::BC> vstage;
+  const int vsub = C::V_DMA ? C::SUB : tid / C::VSTAGERS;
   kdma.init(tid, K.sr);
+  if constexpr (C::V_DMA) vdma.init(tid, V.sr);
+  else vstage.init(vsub < C::SUB ? tid % C::VSTAGERS : C::VSTAGERS, V.sr);
   const bool v0 = vsub < C::SUB && vsub < n_tiles;
-  if (n_tiles > 0) kdma.issue(k_lds[0], Kh, 0, Nk);
+  if (n_tiles > 0) {
+    kdma.issue(k_lds[0], Kh, 0, Nk);
+    if constexpr (C::V_DMA) vdma.issue(v_lds[0], Vh, 0, Nk);
+  }
   if (v0) vstage.load(Vh, vsub * C::BC, Nk);
   // Q fragments stay in registers for the whole pass (B operand of S^T = K Q^T).
 #pragma unroll
@@ -369,15 +420,15 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
     if (w.q_lane < Nq) z = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
     w.qf[s] = z;
   }
-  if (v0) vstage.store(v_lds[0][vsub]);
+  if (v0) vstage.store(v_lds[0] + vsub * C::VSUB);
 
   // Stage J uses buffer J % 2; unrolled by two so the buffer is an immediate.
   const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
   for (int J = 0; J < n_stages; J += 2) {
-    fwd_stage<D, CAUSAL, E, 0>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, J, vsub, n_tiles, n_full, Nk,
+    fwd_stage<D, CAUSAL, E, 0>(w, vstage, kdma, vdma, k_lds, v_lds, Kh, Vh, J, vsub, n_tiles, n_full, Nk,
                                scale_log2);
     if (J + 1 < n_stages)
-      fwd_stage<D, CAUSAL, E, 1>(w, vstage, kdma, k_lds, v_lds, Kh, Vh, J + 1, vsub, n_tiles, n_full, Nk,
+      fwd_stage<D, CAUSAL, E, 1>(w, vstage, kdma, vdma, k_lds, v_lds, Kh, Vh, J + 1, vsub, n_tiles, n_full, Nk,
                                  scale_log2);
   }
 

@@ -36,6 +36,7 @@ struct RowTile {
   static constexpr int CH = D / 8;
   static constexpr bool PADDED = (CH & (CH - 1)) != 0;
   static constexpr int SLOTS = PADDED ? CH + 1 : CH;
+  static constexpr bool HAS_CONST = false;        // every slot is copied from the tensor
   static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16 || CH == 32), "unsupported head dim");
 
   // XOR key of a row (an involution on the chunk index); depends on row % 16.
@@ -143,6 +144,64 @@ struct TrTile {
 };
 
 // ---------------------------------------------------------------------------
+// Row-major tiles read transposed.
+//
+// ds_read_b64_tr_b16 (gfx950) reads 8 bytes per lane and transposes them
+// within each group of 16 lanes: lane j of a group receives, for e = 0..3,
+// 16-bit element j % 4 of the 8 bytes addressed by lane 4 e + j / 4 of its
+// group.  So when lane 4 e + r of group g addresses row T0(g) + e, columns
+// F0(g) + 4 r .. + 3 of a row-major tile, lane j receives column F0(g) + j of
+// rows T0(g) .. T0(g) + 3.  Two such reads give the 8 tokens of an MFMA
+// operand whose reduction index is the token (V^T, K^T, Q^T, dO^T): for the
+// 16-token chunk c, feature block mb and read rd, group g addresses rows
+// 16 c + 8 rd + 4 (g / 2) + e and columns 32 mb + 16 (g % 2) + 4 r, so lane
+// l = 32 h + i receives feature 32 mb + i of tokens 16 c + 8 rd + 4 h + e:
+// the tokens {4h..4h+3, 8+4h..8+4h+3} of an accumulator's lane half.
+//
+// Layouts, chosen so that each 32-lane half of such a read touches every
+// LDS bank once (checked on the host): at D = 64, 128 and 256 the RowTile
+// itself (its XOR swizzle); at D = 80 and 96 plain 12-slot rows (192 bytes).
+// At D = 80 slots 10 and 11 of every row are not copied from the tensor:
+// they hold features 80..95 of the padded feature blocks, set once to
+// (1, 0, .., 0) and zeros, so that a product with the transposed tile also
+// yields the sum of the other operand over its tokens (feature row 80).
+// ---------------------------------------------------------------------------
+template <int D>
+struct TrRowTile {
+  static constexpr int CH = D / 8;
+  static constexpr bool LINEAR = D == 80 || D == 96;
+  static constexpr bool PADDED = LINEAR;          // not a 16-row XOR period (DmaPlan)
+  static constexpr int SLOTS = LINEAR ? 12 : CH;
+  static constexpr bool HAS_CONST = D == 80;     // slots 10 and 11 are constant
+  static_assert(LINEAR || D == 64 || D == 128 || D == 256, "unsupported head dim");
+
+  static FA2_HD int slot(int row, int chunk) {
+    if constexpr (LINEAR) return row * SLOTS + chunk;
+    else return RowTile<D>::slot(row, chunk);
+  }
+  static FA2_HD int elem(int row, int col) { return slot(row, col >> 3) * 8 + (col & 7); }
+  // Chunk of the tensor row stored in slot s; -1 for a constant slot.
+  static FA2_HD int chunk_of_slot(int s) {
+    if constexpr (LINEAR) {
+      const int c = s % SLOTS;
+      return c < CH ? c : -1;
+    } else {
+      return RowTile<D>::chunk_of_slot(s);
+    }
+  }
+  static constexpr int elems(int rows) { return rows * SLOTS * 8; }
+  // Elements between 16-row groups: the swizzle repeats every 16 rows, so the
+  // token chunk c of a read adds c * ROWS16.
+  static constexpr int ROWS16 = 16 * SLOTS * 8;
+  // Element offset of the 8 bytes that lane `lane` addresses in read rd of
+  // feature block mb, token chunk 0.
+  static FA2_HD int tr_elem(int lane, int rd, int mb) {
+    const int g = (lane >> 4) & 3, e = (lane >> 2) & 3, r = lane & 3;
+    return elem(8 * rd + 4 * (g >> 1) + e, 32 * mb + 16 * (g & 1) + 4 * r);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Direct global -> LDS copy of a RowTile of ROWS rows by THREADS threads.
 //
 // Pass t moves slots [t*THREADS, (t+1)*THREADS); wavefront w's 64 lanes move
@@ -156,9 +215,9 @@ struct TrTile {
 // 128 with 256 or more threads; two at D = 256 with 256 threads, whose passes
 // span 8 rows).
 // ---------------------------------------------------------------------------
-template <int D, int ROWS, int THREADS>
+template <int D, int ROWS, int THREADS, class LT = RowTile<D>>
 struct DmaPlan {
-  using L = RowTile<D>;
+  using L = LT;
   static constexpr int TOTAL = ROWS * L::SLOTS;   // 16-byte slots per tile
   static constexpr int ITER = (TOTAL + THREADS - 1) / THREADS;
   static constexpr int RPP = THREADS / L::SLOTS;  // rows per pass (PERIODIC only)
@@ -176,11 +235,17 @@ struct DmaPlan {
   static FA2_HD int period_start(int t) { return PERIODIC ? t - t % PERIOD : 0; }
 
   // Row (from the first row of the tile) and byte offset of the source chunk
-  // of lane `lane` in pass t, stored once per lane (t < NOFF).
+  // of lane `lane` in pass t, stored once per lane (t < NOFF).  A slot that
+  // the layout keeps constant (chunk -1) is not copied: its offset is kSkip.
+  static constexpr uint32_t kSkip = 0xFFFFFFFFu;
   static FA2_HD int lane_row(int wave, int lane, int t) { return (pass_slot(wave, t) + lane) / L::SLOTS; }
   static FA2_HD uint32_t lane_offset(int wave, int lane, int t, int R) {
     const int s = pass_slot(wave, t) + lane;
-    return (uint32_t)((s / L::SLOTS) * R + L::chunk_of_slot(s) * 8) * 2u;
+    const int c = L::chunk_of_slot(s);
+    if constexpr (L::HAS_CONST) {
+      if (c < 0) return kSkip;
+    }
+    return (uint32_t)((s / L::SLOTS) * R + c * 8) * 2u;
   }
 
   // Source of pass t given the stored offset `off` and row `lrow` (those of

@@ -7,6 +7,8 @@
 // accesses are also checked for bank conflicts, taking 16 lanes per cycle
 // (64 banks of 4 bytes: 16 groups of 4 banks): every group of 16 lanes of a
 // register-stage row store or an operand read must reach 16 distinct groups.
+// Transposed operand reads (ds_read_b64_tr_b16) of TrRowTile tiles are
+// simulated lane by lane and checked for content and banks (check_tr_reads).
 // Prints "ok" and exits 0, or prints the first violation and exits 1.
 #include <cstdio>
 #include <cstdlib>
@@ -32,10 +34,10 @@ static int failures = 0;
 // Rows of the source tensor lie R elements apart (R = D: contiguous rows;
 // R > D: a strided view such as one head of a [B, N, H, D] tensor); the
 // tensor's last byte is that of row n - 1's last feature.
-template <int D, int ROWS, int THREADS>
+template <int D, int ROWS, int THREADS, class LT = RowTile<D>>
 void check_dma(int max_n, int R) {
-  using P = DmaPlan<D, ROWS, THREADS>;
-  using L = RowTile<D>;
+  using P = DmaPlan<D, ROWS, THREADS, LT>;
+  using L = LT;
   const long row_bytes = 2L * R;
   for (int n = 1; n <= max_n; ++n) {
     for (int row0 = 0; row0 < n; row0 += ROWS) {
@@ -48,9 +50,14 @@ void check_dma(int max_n, int R) {
             const int slot = first + lane;
             CHECK(slot < P::TOTAL, "D=%d slot %d", D, slot);
             if (slot >= P::TOTAL) continue;
-            written[slot]++;
             const int ti = P::off_index(t);
             const uint32_t off = P::lane_offset(wave, lane, ti, R);
+            if (L::chunk_of_slot(slot) < 0) {   // a constant slot: never copied
+              CHECK(L::HAS_CONST && off == P::kSkip, "D=%d constant slot %d not skipped", D, slot);
+              continue;
+            }
+            CHECK(off != P::kSkip, "D=%d slot %d skipped", D, slot);
+            written[slot]++;
             int base_row;
             uint32_t o;
             P::source(off, P::lane_row(wave, lane, ti), t, row0, n, R, &base_row, &o);
@@ -72,7 +79,8 @@ void check_dma(int max_n, int R) {
         }
       }
       for (int s = 0; s < P::TOTAL; ++s)
-        CHECK(written[s] == 1, "D=%d THREADS=%d slot %d written %d times", D, THREADS, s, written[s]);
+        CHECK(written[s] == (L::chunk_of_slot(s) < 0 ? 0 : 1), "D=%d THREADS=%d slot %d written %d times", D,
+              THREADS, s, written[s]);
     }
   }
 }
@@ -185,6 +193,58 @@ void check_reads() {
   }
 }
 
+// Transposed reads (ds_read_b64_tr_b16) of a TrRowTile of ROWS rows: lane j
+// of 16-lane group g receives, for e = 0..3, element j % 4 of the 8 bytes
+// that lane 4e + j/4 of its group addresses (the instruction's lane layout on
+// gfx950).  For token chunk c, feature block mb and read rd, lane l = 32h + i
+// must receive feature 32 mb + i of tokens 16c + 8rd + 4h + e (at D = 80,
+// features 80..95 come from the constant slots: 1 for feature 80, else 0);
+// every address must lie in the tile, 8-byte aligned; each 32-lane half must
+// reach each of the 64 banks once.
+template <int D, int ROWS>
+void check_tr_reads() {
+  using L = TrRowTile<D>;
+  const int NDB = (D + 31) / 32;
+  // content of every element: 1000 * (row + 1) + col for tensor data,
+  // -1 / -2 for the constant one / zero elements
+  std::vector<int> tile(L::elems(ROWS), -3);
+  for (int r = 0; r < ROWS; ++r) {
+    for (int col = 0; col < D; ++col) tile[L::elem(r, col)] = 1000 * (r + 1) + col;
+    if (L::HAS_CONST)
+      for (int col = D; col < 96; ++col) tile[L::elem(r, col)] = col == D ? -1 : -2;
+  }
+  for (int c = 0; c < ROWS / 16; ++c)
+    for (int mb = 0; mb < NDB; ++mb)
+      for (int rd = 0; rd < 2; ++rd) {
+        int addr[64];
+        for (int lane = 0; lane < 64; ++lane) {
+          addr[lane] = L::tr_elem(lane, rd, mb) + c * L::ROWS16;
+          CHECK(addr[lane] >= 0 && addr[lane] + 4 <= L::elems(ROWS) && addr[lane] % 4 == 0,
+                "D=%d tr read address of lane %d c=%d mb=%d rd=%d: %d", D, lane, c, mb, rd, addr[lane]);
+        }
+        for (int half = 0; half < 2; ++half) {
+          int banks[64] = {0};
+          for (int lane = 32 * half; lane < 32 * half + 32; ++lane)
+            for (int w = 0; w < 2; ++w) banks[(addr[lane] / 2 + w) % 64]++;
+          for (int b = 0; b < 64; ++b)
+            CHECK(banks[b] <= 1, "D=%d tr read c=%d mb=%d rd=%d half %d: bank %d hit %d times", D, c, mb, rd, half,
+                  b, banks[b]);
+        }
+        for (int lane = 0; lane < 64; ++lane) {
+          const int g = lane >> 4, j = lane & 15, h = lane >> 5, i = lane & 31;
+          for (int e = 0; e < 4; ++e) {
+            const int src = 16 * g + 4 * e + (j >> 2);
+            const int got = tile[addr[src] + (j & 3)];
+            const int row = 16 * c + 8 * rd + 4 * h + e, col = 32 * mb + i;
+            const int want = col < D ? 1000 * (row + 1) + col : (L::HAS_CONST ? (col == D ? -1 : -2) : -4);
+            if (col < D || L::HAS_CONST)
+              CHECK(got == want, "D=%d tr read lane %d c=%d mb=%d rd=%d e=%d: got %d want %d", D, lane, c, mb, rd,
+                    e, got, want);
+          }
+        }
+      }
+}
+
 int main() {
   const int max_n = 3 * 64 + 9;
   // row pitches: contiguous rows, a [B, N, H, D] head (R = H D), the q part of a
@@ -239,6 +299,22 @@ int main() {
     check_stage<256, 64, 512, RowTileW<256>>(max_n, 256 * mult);
   }
   check_dma<256, 32, 256>(max_n, 264);
+  // V tiles of the forward (TrRowTile): the thread counts of its workgroups
+  for (int mult : {1, 2, 3}) {
+    check_dma<64, 64, 512, TrRowTile<64>>(max_n, 64 * mult);
+    check_dma<64, 128, 512, TrRowTile<64>>(max_n, 64 * mult);
+    check_dma<80, 64, 256, TrRowTile<80>>(max_n, 80 * mult);
+    check_dma<96, 64, 768, TrRowTile<96>>(max_n, 96 * mult);
+    check_dma<128, 64, 512, TrRowTile<128>>(max_n, 128 * mult);
+  }
+  check_dma<256, 32, 256, TrRowTile<256>>(max_n, 264);
+  check_dma<80, 64, 256, TrRowTile<80>>(max_n, 88);
+  check_tr_reads<64, 64>();
+  check_tr_reads<64, 128>();
+  check_tr_reads<80, 64>();
+  check_tr_reads<96, 64>();
+  check_tr_reads<128, 64>();
+  check_tr_reads<256, 32>();
   check_stage<256, 64, 512, RowTileW<256>>(max_n, 264);
   check_reads<256, 32>();
   check_reads<256, 64, RowTileW<256>>();
