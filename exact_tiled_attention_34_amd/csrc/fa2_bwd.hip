@@ -14,9 +14,9 @@
 //                 S  = Q K^T          P  = 2^(c S - L log2 e),  c = scale log2 e
 //                 dP = dO V^T         dS = P (dP - delta)
 //                 dV^T += dO^T P      dK^T += Q^T dS
-//               P and dS feed their MFMAs straight from registers; Q and dO go
-//               through registers once per step and are written to LDS twice,
-//               row-major and transposed.
+//               P and dS feed their MFMAs straight from registers; Q and dO are
+//               copied row-major straight into LDS and read there both
+//               row-wise and transposed (ds_read_b64_tr_b16).
 //   dq          one workgroup of 8 wavefronts per (256-query row block, batch*head),
 //               shaped like the forward: Q and dO stay in registers, K/V tiles (and a
 //               transposed copy of K) stream through LDS:
@@ -104,15 +104,19 @@ struct DkdvCfg {
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
   static constexpr int NQB = BQ / 32;
-  // Row-major Q and dO tiles: at D = 80 and 96 rows are laid out as 128-wide
-  // RowTileW rows (10 or 12 of their 16 chunks used).  The padded RowTileW<80>
-  // and RowTileW<96> layouts measured 1.3e8 bank-conflict cycles per launch
-  // at B2 H32 N8192 d80 causal on MI355X; the 128-wide one, like D = 64 and
-  // 128, none.
-  using RowL = std::conditional_t<(D == 80 || D == 96), RowTileW<128>, RowTileW<D>>;
-  static constexpr int TILE = RowL::elems(BQ);
-  static constexpr int TTILE = TrTile<D, 64>::ELEMS;
-  static_assert(BQ == 64, "transposed tiles hold 64 tokens");
+  // Q and dO tiles are copied row-major straight into LDS (direct global ->
+  // LDS loads, no registers) and read twice: row-wise for S and dP, and with
+  // transposing reads (ds_read_b64_tr_b16) as Q^T and dO^T for the dV and dK
+  // products.  RowTile's swizzle suits both kinds of read; D = 80 and 96 use
+  // its 128-feature rows (WideRowTile).  Staging both tiles through
+  // registers and writing them twice, row-major and transposed, measured
+  // 2-4 % slower on MI355X (backward B4 H32 N4096 d64 causal -3.3 %,
+  // B2 H32 N8192 d80 causal -1.4 %, B1 H16 N16384 d128 causal -1.5 %).
+  using TileL = std::conditional_t<(D == 80 || D == 96), WideRowTile<D>, RowTile<D>>;
+  static constexpr int TILE = TileL::elems(BQ);
+  // passes of the copy of one tile (one per MFMA stage)
+  static constexpr int NP = DmaPlan<D, BQ, THREADS, TileL>::ITER;
+  static_assert(BQ == 64, "64 queries per step");
 };
 
 template <int D, bool CAUSAL, class E>
@@ -121,13 +125,22 @@ struct DkdvWave {
   u32x4 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
-  LaneOffsets<D, 64, typename C::RowL> off;
+  LaneOffsets<D, 64, typename C::TileL> off;
+  int tro[2][C::NDB];   // transposed reads 0 and 1 of feature block mb
 
-  // One 64-query step.  qt, dot: row-major Q and dO tiles; qtt, dott: their
-  // transposes; l2s, dls: the step's L log2 e and delta; kq0: the last key
-  // the step's first query may see (causal); Nk: keys.  issue(t) runs at
-  // the end of stage t (the caller's global loads for the next step, spread
-  // out so that they never arrive in one burst).
+  __device__ __forceinline__ void init_offsets() {
+    off.init(lane);
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+      for (int mb = 0; mb < C::NDB; ++mb) tro[rd][mb] = tr_lane_elem<typename C::TileL>(lane, rd, mb);
+  }
+
+  // One 64-query step.  qt, dot: the row-major Q and dO tiles (read row-wise
+  // and transposed); l2s, dls: the step's L log2 e and delta; kq0: the last
+  // key the step's first query may see (causal); Nk: keys.  issue(t) runs at
+  // the end of stage t (the caller's copies for the next step, spread out so
+  // that they never go out in one burst).
   //
   // The step is a fixed sequence of MFMA stages, two MFMAs each:
   //   stage t <  NS:  S and dP of query half qb = t / DK, feature chunk s = t % DK
@@ -137,9 +150,8 @@ struct DkdvWave {
   // under the first dV/dK MFMAs (which only need half 0): with one wavefront
   // per SIMD this is the only way the matrix cores and the vector ALU overlap.
   template <bool MASK, class Issue>
-  __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const uint16_t* qtt,
-                                       const uint16_t* dott, const float* l2s, const float* dls,
-                                       int kq0, int Nk, float scale_log2, Issue&& issue) {
+  __device__ __forceinline__ void step(const uint16_t* qt, const uint16_t* dot, const float* l2s,
+                                       const float* dls, int kq0, int Nk, float scale_log2, Issue&& issue) {
     static_assert(C::NQB == 2, "two 32-query halves per step");
     constexpr int NS = C::NQB * C::DK;
     constexpr int NT = (C::BQ / 16) * C::NDB;
@@ -153,9 +165,10 @@ struct DkdvWave {
         rb[t] = lds_read16(dot + o);
       } else {
         const int u = t - NS;
-        const int o = off.tr + 16 * (u / C::NDB) + (u % C::NDB) * LaneOffsets<D>::TR32;
-        ra[t] = lds_read16(dott + o);
-        rb[t] = lds_read16(qtt + o);
+        const int c = u / C::NDB, mb = u % C::NDB;
+        constexpr int R16 = C::TileL::ROWS16;
+        ra[t] = lds_read_tr(dot + tro[0][mb] + c * R16, dot + tro[1][mb] + c * R16);
+        rb[t] = lds_read_tr(qt + tro[0][mb] + c * R16, qt + tro[1][mb] + c * R16);
       }
     };
 #pragma unroll
@@ -248,15 +261,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   using C = DkdvCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][C::TTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[2][C::TTILE];
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * C::BQ];   // [L log2e | delta]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  for (int b = 0; b < 2; ++b) {
-    tr_zero_pad<D>(qt_lds[b], tid, C::THREADS);
-    tr_zero_pad<D>(dot_lds[b], tid, C::THREADS);
+  if constexpr (C::TileL::HAS_CONST) {
+    // slots of the wide rows that are never copied: zero once
+    for (int s = tid; s < C::BQ * C::TileL::SLOTS; s += C::THREADS)
+      if (C::TileL::chunk_of_slot(s) < 0) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int b = 0; b < 2; ++b) {
+          *reinterpret_cast<u32x4*>(q_lds[b] + 8 * s) = z;
+          *reinterpret_cast<u32x4*>(do_lds[b] + 8 * s) = z;
+        }
+      }
   }
 
   // Linear id -> (key block, batch*head); consecutive ids take different heads
@@ -288,41 +306,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         global_load_lds16(Dh + q0, 16u * (lane - C::BQ / 4), dst);
     }
   };
-  // Q and dO go through registers once and are written twice per step:
-  // row-major and transposed.
-  // (at D = 128 every thread stages its part of both tiles)
-  constexpr bool ALL_STAGE = StagePlan<D>::THREADS_USED == C::THREADS;
-  TrStage<D, 64, ALL_STAGE> qstage, dostage;
-  // A tile stage needs StagePlan<D>::THREADS_USED threads: at D = 64 that is
-  // half the workgroup, so wavefronts 0-1 stage Q and 2-3 stage dO; otherwise
-  // every thread stages its part of both.  (A thread index past the plan
-  // leaves that stage idle.)
-  constexpr int SPLIT = 2 * StagePlan<D>::THREADS_USED <= C::THREADS ? StagePlan<D>::THREADS_USED : 0;
-  constexpr int IDLE = C::THREADS;
-  qstage.init(SPLIT && tid >= SPLIT ? IDLE : tid, Q.sr);
-  dostage.init(SPLIT ? (tid >= SPLIT ? tid - SPLIT : IDLE) : tid, dO.sr);
-  auto load_stage = [&](int i) {
-    qstage.load(Qh, i * C::BQ, Nq);
-    dostage.load(dOh, i * C::BQ, Nq);
-  };
-  // Inside a step the next step's staging loads go out one per MFMA stage
-  // (stages 0..3: Q tokens k = 0..3, stages 4..7: dO; every step has at least
-  // 16 stages): issued as one burst before the step, they held the wavefront
-  // up for longer than the matrix work of its first stages.
+  // Q and dO: direct copies into the idle buffers.  Inside a step the next
+  // step's copies go out one pass per MFMA stage (stages 0..NP-1 Q, then dO;
+  // every step has at least 16 stages): issued as one burst before the step,
+  // they measured slower.
+  TileDma<D, C::BQ, C::THREADS, typename C::TileL> qdma, dodma;
+  qdma.init(tid, Q.sr);
+  dodma.init(tid, dO.sr);
+  int dma_row = -1;   // first row of the next step's tiles (-1: none)
+  uint16_t *dma_q = nullptr, *dma_do = nullptr;
   auto issue = [&](int t) {
-    if (t < 4) qstage.load_k(t);
-    else if (t < 8) dostage.load_k(t - 4);
-  };
-  auto store_step = [&](int buf) {
-    qstage.store(qt_lds[buf]);
-    qstage.template store_rows<typename C::RowL>(q_lds[buf]);
-    dostage.store(dot_lds[buf]);
-    dostage.template store_rows<typename C::RowL>(do_lds[buf]);
+    if (dma_row >= 0) {
+      if (t < C::NP) qdma.issue_pass(t, dma_q, Qh, dma_row, Nq);
+      else if (t < 2 * C::NP) dodma.issue_pass(t - C::NP, dma_do, dOh, dma_row, Nq);
+    }
   };
   if (i_begin < n_qblk) {
     load_ld(ld_lds[0], i_begin * C::BQ);
-    load_stage(i_begin);
-    store_step(0);
+    qdma.issue(q_lds[0], Qh, i_begin * C::BQ, Nq);
+    dodma.issue(do_lds[0], dOh, i_begin * C::BQ, Nq);
   }
 
   DkdvWave<D, CAUSAL, E> w;
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   w.lh = w.lane >> 5;
   w.key_w = key_wg + wave * 32;
   w.key_lane = w.key_w + w.lr;
-  w.off.init(w.lane);
+  w.init_offsets();
   // K, V as B operands (lane: one key, 8 consecutive features per k-step).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
@@ -359,25 +361,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __syncthreads();   // step i is in LDS; every wave is done with the other buffer
     const bool more = i + 1 < n_qblk;
     if (more) load_ld(ld_lds[BUF ^ 1], (i + 1) * C::BQ);
-    // The stages are loaded and stored on every step (the last one re-stages
-    // itself into the idle buffers), so their registers never live across steps.
-    const int inext = more ? i + 1 : i;
-    qstage.begin(Qh, inext * C::BQ, Nq);
-    dostage.begin(dOh, inext * C::BQ, Nq);
+    dma_row = more ? (i + 1) * C::BQ : -1;
+    dma_q = q_lds[BUF ^ 1];
+    dma_do = do_lds[BUF ^ 1];
     // kq0: the key position of the step's first query (its last visible key)
     const int kq0 = i * C::BQ + koff;
     const bool need_mask = (CAUSAL && w.key_w + 31 > kq0) || (w.key_w + 32 > Nk);
     const bool active = !CAUSAL || w.key_w <= kq0 + C::BQ - 1;
     if (!need_mask) {
-      w.template step<false>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
-                             ld_lds[BUF] + C::BQ, kq0, Nk, scale_log2, issue);
+      w.template step<false>(q_lds[BUF], do_lds[BUF], ld_lds[BUF], ld_lds[BUF] + C::BQ, kq0, Nk,
+                             scale_log2, issue);
     } else if (active) {
-      w.template step<true>(q_lds[BUF], do_lds[BUF], qt_lds[BUF], dot_lds[BUF], ld_lds[BUF],
-                            ld_lds[BUF] + C::BQ, kq0, Nk, scale_log2, issue);
+      w.template step<true>(q_lds[BUF], do_lds[BUF], ld_lds[BUF], ld_lds[BUF] + C::BQ, kq0, Nk,
+                            scale_log2, issue);
     } else {
-      load_stage(inext);
+      // a wavefront with no key this step can see still does its share of
+      // copying the next one
+      if (dma_row >= 0) {
+        qdma.issue(dma_q, Qh, dma_row, Nq);
+        dodma.issue(dma_do, dOh, dma_row, Nq);
+      }
     }
-    store_step(BUF ^ 1);
   };
   for (int i = i_begin; i < n_qblk; i += 2) {
     iteration(std::integral_constant<int, 0>{}, i);

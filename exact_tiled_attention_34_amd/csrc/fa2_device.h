@@ -195,24 +195,29 @@ struct TileDma {
       lrow[t] = P::lane_row(wave, tid & 63, t);
     }
   }
+  // Pass t of the copy (t < P::ITER; requires 0 <= row0 < n_rows).  row0 is
+  // the same in every lane (made visibly so: the load takes a scalar base).
+  __device__ __forceinline__ void issue_pass(int t, uint16_t* tile, const uint16_t* head, int row0,
+                                             int n_rows) const {
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    const int first = P::pass_slot(wave, t);   // wavefront-uniform
+    if (first < P::TOTAL) {
+      int base_row;
+      uint32_t o;
+      const int i = P::off_index(t);
+      P::source(off[i], lrow[i], t, row0, n_rows, R, &base_row, &o);
+      if constexpr (LT::HAS_CONST) {
+        if (off[i] != P::kSkip) global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+      } else {
+        global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+      }
+    }
+  }
   // requires 0 <= row0 < n_rows
   __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* head, int row0,
                                         int n_rows) const {
 #pragma unroll
-    for (int t = 0; t < P::ITER; ++t) {
-      const int first = P::pass_slot(wave, t);   // wavefront-uniform
-      if (first < P::TOTAL) {
-        int base_row;
-        uint32_t o;
-        const int i = P::off_index(t);
-        P::source(off[i], lrow[i], t, row0, n_rows, R, &base_row, &o);
-        if constexpr (LT::HAS_CONST) {
-          if (off[i] != P::kSkip) global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
-        } else {
-          global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
-        }
-      }
-    }
+    for (int t = 0; t < P::ITER; ++t) issue_pass(t, tile, head, row0, n_rows);
   }
 };
 

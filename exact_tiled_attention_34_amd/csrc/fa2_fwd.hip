@@ -136,7 +136,7 @@ struct FwdWave {
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-      for (int mb = 0; mb < C::NDB; ++mb) vtr[rd][mb] = C::VL::tr_elem(lane, rd, mb);
+      for (int mb = 0; mb < C::NDB; ++mb) vtr[rd][mb] = tr_lane_elem<typename C::VL>(lane, rd, mb);
   }
 
   // S^T (64 keys x this wave's 32 queries) of the K tile at kt.

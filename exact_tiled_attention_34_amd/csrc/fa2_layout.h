@@ -65,6 +65,8 @@ struct RowTile {
   }
   // bf16 elements to reserve for a tile.
   static constexpr int elems(int rows) { return rows * SLOTS * 8; }
+  // Elements per 16 rows (the period of the swizzle).
+  static constexpr int ROWS16 = 16 * SLOTS * 8;
   // Row lr + 32 b, features 16 s + 8 h: the lane's block-0 offset for step
   // perm(s, b) (= s: the permutation repeats every 16 rows) plus block(b).
   static constexpr int perm(int s, int) { return s; }
@@ -193,12 +195,43 @@ struct TrRowTile {
   // Elements between 16-row groups: the swizzle repeats every 16 rows, so the
   // token chunk c of a read adds c * ROWS16.
   static constexpr int ROWS16 = 16 * SLOTS * 8;
-  // Element offset of the 8 bytes that lane `lane` addresses in read rd of
-  // feature block mb, token chunk 0.
-  static FA2_HD int tr_elem(int lane, int rd, int mb) {
-    const int g = (lane >> 4) & 3, e = (lane >> 2) & 3, r = lane & 3;
-    return elem(8 * rd + 4 * (g >> 1) + e, 32 * mb + 16 * (g & 1) + 4 * r);
+};
+
+// Element offset, in a tile of layout L, of the 8 bytes that lane `lane`
+// addresses in transposed read rd of feature block mb, token chunk 0 (the
+// token chunk c adds c * L::ROWS16).
+template <class L>
+FA2_HD int tr_lane_elem(int lane, int rd, int mb) {
+  const int g = (lane >> 4) & 3, e = (lane >> 2) & 3, r = lane & 3;
+  return L::elem(8 * rd + 4 * (g >> 1) + e, 32 * mb + 16 * (g & 1) + 4 * r);
+}
+
+// ---------------------------------------------------------------------------
+// D = 80 and 96 features in 128-feature rows: the RowTile<128> layout (whose
+// swizzle suits both 16-byte row reads and transposed reads), of which only
+// the first D / 8 chunks of each row are copied from the tensor; the other
+// slots (chunk -1 for the copy plan) are zeroed once by the kernel and feed
+// only padding rows of the feature blocks.
+// ---------------------------------------------------------------------------
+template <int D>
+struct WideRowTile {
+  using W = RowTile<128>;
+  static constexpr int CH = 16;                  // chunk slots per row
+  static constexpr int DCH = D / 8;              // chunks copied from the tensor
+  static constexpr bool PADDED = false;
+  static constexpr int SLOTS = 16;
+  static constexpr bool HAS_CONST = DCH < 16;
+  static_assert(D == 80 || D == 96, "wide rows for D = 80, 96");
+  static FA2_HD int slot(int row, int chunk) { return W::slot(row, chunk); }
+  static FA2_HD int elem(int row, int col) { return W::elem(row, col); }
+  static FA2_HD int chunk_of_slot(int s) {
+    const int c = W::chunk_of_slot(s);
+    return c < DCH ? c : -1;
   }
+  static constexpr int elems(int rows) { return W::elems(rows); }
+  static constexpr int ROWS16 = 16 * SLOTS * 8;
+  static constexpr int perm(int s, int b) { return W::perm(s, b); }
+  static constexpr int block(int b) { return W::block(b); }
 };
 
 // ---------------------------------------------------------------------------

@@ -201,16 +201,16 @@ void check_reads() {
 // features 80..95 come from the constant slots: 1 for feature 80, else 0);
 // every address must lie in the tile, 8-byte aligned; each 32-lane half must
 // reach each of the 64 banks once.
-template <int D, int ROWS>
+template <int D, int ROWS, class L = TrRowTile<D>>
 void check_tr_reads() {
-  using L = TrRowTile<D>;
+  constexpr bool ONES = std::is_same<L, TrRowTile<D>>::value && L::HAS_CONST;   // (1, 0, ..) in features D..
   const int NDB = (D + 31) / 32;
   // content of every element: 1000 * (row + 1) + col for tensor data,
   // -1 / -2 for the constant one / zero elements
   std::vector<int> tile(L::elems(ROWS), -3);
   for (int r = 0; r < ROWS; ++r) {
     for (int col = 0; col < D; ++col) tile[L::elem(r, col)] = 1000 * (r + 1) + col;
-    if (L::HAS_CONST)
+    if (ONES)
       for (int col = D; col < 96; ++col) tile[L::elem(r, col)] = col == D ? -1 : -2;
   }
   for (int c = 0; c < ROWS / 16; ++c)
@@ -218,7 +218,7 @@ void check_tr_reads() {
       for (int rd = 0; rd < 2; ++rd) {
         int addr[64];
         for (int lane = 0; lane < 64; ++lane) {
-          addr[lane] = L::tr_elem(lane, rd, mb) + c * L::ROWS16;
+          addr[lane] = tr_lane_elem<L>(lane, rd, mb) + c * L::ROWS16;
           CHECK(addr[lane] >= 0 && addr[lane] + 4 <= L::elems(ROWS) && addr[lane] % 4 == 0,
                 "D=%d tr read address of lane %d c=%d mb=%d rd=%d: %d", D, lane, c, mb, rd, addr[lane]);
         }
@@ -236,8 +236,8 @@ void check_tr_reads() {
             const int src = 16 * g + 4 * e + (j >> 2);
             const int got = tile[addr[src] + (j & 3)];
             const int row = 16 * c + 8 * rd + 4 * h + e, col = 32 * mb + i;
-            const int want = col < D ? 1000 * (row + 1) + col : (L::HAS_CONST ? (col == D ? -1 : -2) : -4);
-            if (col < D || L::HAS_CONST)
+            const int want = col < D ? 1000 * (row + 1) + col : (ONES ? (col == D ? -1 : -2) : -4);
+            if (col < D || ONES)
               CHECK(got == want, "D=%d tr read lane %d c=%d mb=%d rd=%d e=%d: got %d want %d", D, lane, c, mb, rd,
                     e, got, want);
           }
@@ -315,6 +315,20 @@ int main() {
   check_tr_reads<96, 64>();
   check_tr_reads<128, 64>();
   check_tr_reads<256, 32>();
+  // Q and dO tiles of the dK/dV pass (copied, read row-wise and transposed)
+  for (int mult : {1, 2, 3}) {
+    check_dma<64, 64, 256, RowTile<64>>(max_n, 64 * mult);
+    check_dma<80, 64, 256, WideRowTile<80>>(max_n, 80 * mult);
+    check_dma<96, 64, 256, WideRowTile<96>>(max_n, 96 * mult);
+    check_dma<128, 64, 256, RowTile<128>>(max_n, 128 * mult);
+  }
+  check_dma<80, 64, 256, WideRowTile<80>>(max_n, 88);
+  check_reads<80, 64, WideRowTile<80>>();
+  check_reads<96, 64, WideRowTile<96>>();
+  check_tr_reads<64, 64, RowTile<64>>();
+  check_tr_reads<80, 64, WideRowTile<80>>();
+  check_tr_reads<96, 64, WideRowTile<96>>();
+  check_tr_reads<128, 64, RowTile<128>>();
   check_stage<256, 64, 512, RowTileW<256>>(max_n, 264);
   check_reads<256, 32>();
   check_reads<256, 64, RowTileW<256>>();
