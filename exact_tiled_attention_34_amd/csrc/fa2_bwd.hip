@@ -18,8 +18,8 @@
 //               copied row-major straight into LDS and read there both
 //               row-wise and transposed (ds_read_b64_tr_b16).
 //   dq          one workgroup of 8 wavefronts per (256-query row block, batch*head),
-//               shaped like the forward: Q and dO stay in registers, K/V tiles (and a
-//               transposed copy of K) stream through LDS:
+//               shaped like the forward: Q and dO stay in registers, K/V tiles are
+//               copied into LDS (K is read there both row-wise and transposed):
 //                 S^T = K Q^T   dP^T = V dO^T   dS^T = P^T (dP^T - delta)
 //                 dQ^T += K^T dS^T
 //               This second pass recomputes S and dP instead of adding partial dQ
@@ -713,8 +713,12 @@ struct DqCfg {
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;
-  static constexpr int TILE = RowTile<D>::elems(BC);
-  static constexpr int TTILE = TrTile<D, BC>::ELEMS;
+  // K and V tiles are copied row-major straight into LDS and read row-wise
+  // (S^T, dP^T); K is also read transposed (ds_read_b64_tr_b16) as K^T for
+  // the dQ product.  RowTile's swizzle suits both kinds of read; D = 80 and
+  // 96 use its 128-feature rows (WideRowTile).
+  using TileL = std::conditional_t<(D == 80 || D == 96), WideRowTile<D>, RowTile<D>>;
+  static constexpr int TILE = TileL::elems(BC);
   // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint)
   static constexpr int READ_AHEAD = D == 256 ? 2 : 6;
 };
@@ -727,15 +731,24 @@ struct DqWave {
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
   int key_last;   // causal: last key this lane's query may see (q_lane + Nk - Nq)
-  LaneOffsets<D, DqCfg<D>::BC> off;
+  LaneOffsets<D, DqCfg<D>::BC, typename DqCfg<D>::TileL> off;
+  int tro[2][C::NDB];   // transposed reads 0 and 1 of feature block mb
 
-  // kt, vt: row-major K and V tiles; ktt: transposed K tile.  mask: the tile
+  __device__ __forceinline__ void init_offsets() {
+    off.init(lane);
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+      for (int mb = 0; mb < C::NDB; ++mb) tro[rd][mb] = tr_lane_elem<typename C::TileL>(lane, rd, mb);
+  }
+
+  // kt, vt: row-major K and V tiles (K also read transposed).  mask: the tile
   // may hold keys past the end or above the diagonal for some of this wave's
   // rows.  It is a run-time branch that only sets such scores to -inf (so P
   // = 0): one tile body for every tile, so the dQ accumulators keep one
   // register assignment through the loop.
-  __device__ __forceinline__ void tile(bool mask, const uint16_t* kt, const uint16_t* vt,
-                                       const uint16_t* ktt, int key0, int Nk, float scale_log2) {
+  __device__ __forceinline__ void tile(bool mask, const uint16_t* kt, const uint16_t* vt, int key0, int Nk,
+                                       float scale_log2) {
     f32x16 sacc[C::KB], pacc[C::KB];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
@@ -772,16 +785,17 @@ struct DqWave {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) dsw[kb][i >> 1] = E::pack2(pacc[kb][i], pacc[kb][i + 1]);
     }
-    // dQ^T (d x query) += K^T (d x 16 keys) dS^T (16 keys x query).
+    // dQ^T (d x query) += K^T (d x 16 keys) dS^T (16 keys x query), K^T by two
+    // transposed reads of the K tile.
+    constexpr int R16 = C::TileL::ROWS16;
 #pragma unroll
     for (int c = 0; c < C::BC / 16; ++c) {
       const u32x4 b = acc_chunk(dsw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb)
-        dqacc[mb] = E::mfma(lds_read16(ktt + off.tr + 16 * c + mb * LaneOffsets<D, C::BC>::TR32), b,
-                                 dqacc[mb]);
+        dqacc[mb] = E::mfma(lds_read_tr(kt + tro[0][mb] + c * R16, kt + tro[1][mb] + c * R16), b, dqacc[mb]);
     }
-    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, (C::BC / 16) * C::NDB, C::READ_AHEAD>();
+    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, 2 * (C::BC / 16) * C::NDB, C::READ_AHEAD, 2>();
   }
 };
 
@@ -793,12 +807,20 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[2][C::TTILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  tr_zero_pad<D, C::BC>(kt_lds[0], tid, C::THREADS);
-  tr_zero_pad<D, C::BC>(kt_lds[1], tid, C::THREADS);
+  if constexpr (C::TileL::HAS_CONST) {
+    // slots of the wide rows that are never copied: zero once
+    for (int s = tid; s < C::BC * C::TileL::SLOTS; s += C::THREADS)
+      if (C::TileL::chunk_of_slot(s) < 0) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int b = 0; b < 2; ++b) {
+          *reinterpret_cast<u32x4*>(k_lds[b] + 8 * s) = z;
+          *reinterpret_cast<u32x4*>(v_lds[b] + 8 * s) = z;
+        }
+      }
+  }
   const int nrb = (Nq + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;
@@ -818,7 +840,7 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
   w.q_wave = rb * C::BR + wave * 32;
   w.q_lane = w.q_wave + w.lr;
   w.key_last = w.q_lane + koff;
-  w.off.init(w.lane);
+  w.init_offsets();
 
   const int q_first = rb * C::BR;
   int n_tiles = (Nk + C::BC - 1) / C::BC;
@@ -828,16 +850,14 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
   }
   const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
-  // K goes through registers (written row-major and transposed), V is copied
-  // to LDS directly; both row-major tiles are RowTiles (one set of lane
-  // offsets reads them).
-  TrStage<D, C::BC> kstage;
-  TileDma<D, C::BC, C::THREADS> vdma;
-  kstage.init(tid, K.sr);
+  // K and V are copied to LDS directly, in the same layout (one set of lane
+  // offsets reads both row-wise).
+  TileDma<D, C::BC, C::THREADS, typename C::TileL> kdma, vdma;
+  kdma.init(tid, K.sr);
   vdma.init(tid, V.sr);
   if (n_tiles > 0) {
+    kdma.issue(k_lds[0], Kh, 0, Nk);
     vdma.issue(v_lds[0], Vh, 0, Nk);
-    kstage.load(Kh, 0, Nk);
   }
 
   // Q and dO fragments stay in registers (B operands of K Q^T and V dO^T);
@@ -863,11 +883,10 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
     constexpr int BUF = decltype(buf_tag)::value;
     wait_vmem();
     __syncthreads();
-    const bool more = j + 1 < n_tiles;
-    if (more) vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, Nk);
-    // The K stage is loaded and stored on every tile (the last one re-stages
-    // itself into the idle buffers), so its registers never live across tiles.
-    kstage.load(Kh, (more ? j + 1 : j) * C::BC, Nk);
+    if (j + 1 < n_tiles) {
+      kdma.issue(k_lds[BUF ^ 1], Kh, (j + 1) * C::BC, Nk);
+      vdma.issue(v_lds[BUF ^ 1], Vh, (j + 1) * C::BC, Nk);
+    }
     const int key0 = j * C::BC;
     // tiles from n_full on are masked; a wavefront whose rows all precede the
     // tile's first key has nothing to do.  Without the causal mask every tile
@@ -876,14 +895,8 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
     // compiler otherwise builds needs more than the 512 registers of a lane.
     const bool visit = CAUSAL ? (j < n_full || key0 <= w.q_wave + 31 + koff)
                               : (D != 256 || key0 <= w.q_wave + 31 + koff + Nq + Nk);
-    if (visit) w.tile(j >= n_full, k_lds[BUF], v_lds[BUF], kt_lds[BUF], key0, Nk, scale_log2);
-    kstage.store(kt_lds[BUF ^ 1]);
-    kstage.template store_rows<RowTile<D>>(k_lds[BUF ^ 1]);
+    if (visit) w.tile(j >= n_full, k_lds[BUF], v_lds[BUF], key0, Nk, scale_log2);
   };
-  if (n_tiles > 0) {
-    kstage.store(kt_lds[0]);
-    kstage.template store_rows<RowTile<D>>(k_lds[0]);
-  }
   for (int j = 0; j < n_tiles; j += 2) {
     iteration(std::integral_constant<int, 0>{}, j);
     if (j + 1 < n_tiles) iteration(std::integral_constant<int, 1>{}, j + 1);

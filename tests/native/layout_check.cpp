@@ -323,6 +323,11 @@ int main() {
     check_dma<128, 64, 256, RowTile<128>>(max_n, 128 * mult);
   }
   check_dma<80, 64, 256, WideRowTile<80>>(max_n, 88);
+  // K and V tiles of the dQ pass (eight wavefronts)
+  for (int mult : {1, 2, 3}) {
+    check_dma<80, 64, 512, WideRowTile<80>>(max_n, 80 * mult);
+    check_dma<96, 64, 512, WideRowTile<96>>(max_n, 96 * mult);
+  }
   check_reads<80, 64, WideRowTile<80>>();
   check_reads<96, 64, WideRowTile<96>>();
   check_tr_reads<64, 64, RowTile<64>>();
