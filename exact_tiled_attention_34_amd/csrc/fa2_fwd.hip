@@ -22,9 +22,9 @@
 //                          tile (then every factor is exactly 1), which after
 //                          the first tiles is the common case
 //                          ("FlashAttention-2" summary page, "How It Works" 2:
-//                          scaling kept out of the inner loop).  Except at
-//                          head dim 64 the maximum pass itself is skipped
-//                          while every P against the current m stays <= 2^8.
+//                          scaling kept out of the inner loop).  The maximum
+//                          pass itself is skipped while every P against the
+//                          current m stays <= 2^8.
 //   O^T += V^T P^T         bf16 MFMA; V^T is a transposed LDS tile, P^T comes
 //                          straight from registers
 // After the last tile, O is divided once by the row sum of P as rounded for
@@ -96,17 +96,16 @@ struct FwdCfg {
   static constexpr bool ONES_ROW = DP != D;
   // The softmax step first tries P against the current reference maximum
   // (no maximum pass); the scores stay live until it knows whether the
-  // maximum pass is due.  That fits the registers of every head dimension but
-  // 64, whose four wavefronts per SIMD have 128 registers each (it spills).
-  // Forward time on MI355X: B1 H16 N16384 d128 causal -7 %, B8 H16 N2048 d128
-  // -7 %, B1 H16 N8192 d256 causal -19 %.
-  static constexpr bool LAZY = D != 64;
+  // maximum pass is due.  Forward time on MI355X: B1 H16 N16384 d128 causal
+  // -7 %, B8 H16 N2048 d128 -7 %, B1 H16 N8192 d256 causal -19 %,
+  // B4 H32 N4096 d64 causal -7 %.
+  static constexpr bool LAZY = true;
   // With the lazy maximum, one softmax step per 32-key block instead of one
   // per tile, so that the exponentials of block 1 can run under the products
-  // of block 0: B2 H32 N8192 d80 causal -6 %, B2 H24 N8192 d96 causal -5 %
-  // (and at D = 96 the whole-tile step spills), but B1 H16 N16384 d128
-  // causal +6 %.
-  static constexpr bool BLOCK_STEPS = LAZY && KB == 2 && (D == 80 || D == 96);
+  // of block 0: B2 H32 N8192 d80 causal -6 %, B2 H24 N8192 d96 causal -5 %,
+  // but B1 H16 N16384 d128 causal +6 %.  At D = 64 (four wavefronts per SIMD,
+  // 128 registers) and 96 the whole-tile step spills.
+  static constexpr bool BLOCK_STEPS = LAZY && KB == 2 && (D == 64 || D == 80 || D == 96);
   static constexpr int ONES_REG = 4 * ((D % 32) / 8) + D % 4;
   static constexpr int ONES_HALF = (D % 8) / 4;
 };
