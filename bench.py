@@ -124,13 +124,17 @@ def compulsory_bytes(w, n_pad):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources and of the build script (whose flags shape the code)."""
     import hashlib
-    d = os.path.join(ROOT, "exact_tiled_attention_34_amd", "csrc")
+    pkg = os.path.join(ROOT, "exact_tiled_attention_34_amd")
+    d = os.path.join(pkg, "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(d)):
         if name.endswith((".hip", ".h")):
             with open(os.path.join(d, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(b"build.py\0" + f.read())
     return h.hexdigest()[:16]
 
 

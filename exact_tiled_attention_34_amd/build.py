@@ -17,7 +17,21 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfa2.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["fa2_api.hip", "fa2_fwd.hip", "fa2_bwd.hip"]
+SOURCES = ["fa2_api.hip", "fa2_fwd.hip", "fa2_bwd.hip", "fa2_bwd_dq256.hip"]
+# Kernels that run one wavefront per SIMD may use all 512 registers of a lane,
+# and for those the compiler otherwise writes every MFMA result to the
+# accumulator registers: the S and dP products (and the forward's scores at
+# head dim 256) were then copied to vector registers on every step for the
+# softmax.  With MFMA results in vector registers they are read in place
+# (dK/dV on MI355X: B4 H32 N4096 d64 causal -11 %, B2 H32 N8192 d80 causal
+# -6.5 %; head dim 256 forward -8 %).  Kernels with two or more wavefronts per
+# SIMD compile to the same code either way.  The head-dim-256 dQ kernel, whose
+# accumulators are only ever MFMA operands, measured 21 % slower with it and
+# keeps the default (its own unit).
+SOURCE_FLAGS = {
+    "fa2_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa2_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -42,7 +56,7 @@ def hipcc():
 
 def _compile(src, extra):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature flag; that note is harmless
     noise = "is not a recognized feature for this target"

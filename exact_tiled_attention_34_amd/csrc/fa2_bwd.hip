@@ -34,7 +34,9 @@
 namespace fa2 {
 
 // Multiple of every query block size the backward kernels use (64 and 256).
+#if !FA2_DQ256_UNIT
 int bwd_rows_padded(int N) { return (N + 255) / 256 * 256; }
+#endif
 
 namespace {
 
@@ -344,6 +346,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     w.kf[s] = zk;
     w.vf[s] = zv;
+    // K and V only ever feed MFMAs, which read operands from the accumulator
+    // registers as well: keeping them there leaves the vector registers to
+    // the S and dP products, which the softmax reads.
+    asm volatile("" : "+a"(w.kf[s]));
+    asm volatile("" : "+a"(w.vf[s]));
   }
 #pragma unroll
   for (int mb = 0; mb < C::NDB; ++mb)
@@ -963,6 +970,22 @@ hipError_t launch_dq_t(const Strided& q, const Strided& k, const Strided& v, con
 
 }  // namespace
 
+#if FA2_DQ256_UNIT
+// The dQ kernel at head dimension 256 (one wavefront per SIMD) is compiled in
+// a unit of its own (fa2_bwd_dq256.hip), without the MFMA register form the
+// other backward kernels are built with (build.py): its dQ accumulators are
+// only ever MFMA operands and belong in the accumulator registers.
+hipError_t launch_bwd_dq_d256(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
+                              const float* l2, const float* delta, const Strided& dq, int B, int H,
+                              int Nq, int Nk, float scale, int causal, int dtype, hipStream_t stream) {
+  return dispatch(256, causal, dtype, [&](auto dc, auto cc, auto ec) {
+    if constexpr (decltype(dc)::value == 256)
+      return launch_dq_t<256, decltype(cc)::value, decltype(ec)>(q, k, v, dout, l2, delta, dq, B, H, Nq, Nk,
+                                                               scale, stream);
+    return hipErrorInvalidValue;
+  });
+}
+#else
 hipError_t launch_bwd_preprocess(const Strided& o, const Strided& dout, const float* lse,
                                  float* delta, float* l2, int B, int H, int N, int d, int dtype,
                                  hipStream_t stream) {
@@ -985,9 +1008,12 @@ hipError_t launch_bwd_dq(const Strided& q, const Strided& k, const Strided& v, c
                          const float* l2, const float* delta, const Strided& dq, int B, int H,
                          int Nq, int Nk, int d, float scale, int causal, int dtype,
                          hipStream_t stream) {
+  if (d == 256) return launch_bwd_dq_d256(q, k, v, dout, l2, delta, dq, B, H, Nq, Nk, scale, causal, dtype, stream);
   return dispatch(d, causal, dtype, [&](auto dc, auto cc, auto ec) {
-    return launch_dq_t<decltype(dc)::value, decltype(cc)::value, decltype(ec)>(
-        q, k, v, dout, l2, delta, dq, B, H, Nq, Nk, scale, stream);
+    if constexpr (decltype(dc)::value == 256) return hipErrorInvalidValue;   // launch_bwd_dq_d256
+    else
+      return launch_dq_t<decltype(dc)::value, decltype(cc)::value, decltype(ec)>(
+          q, k, v, dout, l2, delta, dq, B, H, Nq, Nk, scale, stream);
   });
 }
 
@@ -1002,5 +1028,6 @@ void bwd_tiles(int d, int* block_k, int* block_q, int* waves) {
   *block_q = DkdvCfg<128>::BQ;
   *waves = DkdvCfg<128>::WAVES;
 }
+#endif
 
 }  // namespace fa2

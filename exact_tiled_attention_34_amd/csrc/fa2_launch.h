@@ -39,6 +39,11 @@ hipError_t launch_bwd_dq(const Strided& q, const Strided& k, const Strided& v, c
                          int Nq, int Nk, int d, float scale, int causal, int dtype,
                          hipStream_t stream);
 
+// launch_bwd_dq at head dimension 256 (its own compilation unit)
+hipError_t launch_bwd_dq_d256(const Strided& q, const Strided& k, const Strided& v, const Strided& dout,
+                              const float* lse_log2, const float* delta, const Strided& dq, int B, int H,
+                              int Nq, int Nk, float scale, int causal, int dtype, hipStream_t stream);
+
 void fwd_tiles(int d, int* block_q, int* block_k, int* waves);
 void bwd_tiles(int d, int* block_k, int* block_q, int* waves);
 

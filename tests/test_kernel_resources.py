@@ -19,7 +19,7 @@ KERNEL_SOURCES = [s for s in B.SOURCES if s != "fa2_api.hip"]
 
 
 def resource_report(src):
-    cmd = [HIPCC, *B.COMMON_FLAGS, "--cuda-device-only", "-c", os.path.join(B.CSRC, src),
+    cmd = [HIPCC, *B.COMMON_FLAGS, *B.SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-c", os.path.join(B.CSRC, src),
            "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -46,6 +46,13 @@ def test_every_kernel_reported(reports):
     names = [k for rep in reports.values() for k in rep]
     for kind in ("fwd_kernel", "bwd_preprocess_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
         assert any(kind in n for n in names), kind
+
+
+def test_head_dim_256_dq_in_its_own_unit(reports):
+    # the dQ kernel at head dim 256 is built only by its own unit (other flags)
+    assert any("bwd_dq_kernelILi256" in k for k in reports["fa2_bwd_dq256.hip"])
+    assert not any("bwd_dq_kernelILi256" in k for k in reports["fa2_bwd.hip"])
+    assert not any("dkdv" in k or "fwd_kernel" in k for k in reports["fa2_bwd_dq256.hip"])
 
 
 def test_no_scratch(reports):
