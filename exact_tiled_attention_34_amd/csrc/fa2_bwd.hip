@@ -158,7 +158,10 @@ struct DkdvWave {
     constexpr int NS = C::NQB * C::DK;
     constexpr int NT = (C::BQ / 16) * C::NDB;
     constexpr int NALL = NS + NT;
-    constexpr int PF = 3;
+    // operand reads in flight: 2 stages at D = 128, whose registers are
+    // the tightest (fewer spills to the accumulator registers: B1 H16 N16384
+    // d128 causal dK/dV -0.8 %), else 3
+    constexpr int PF = D == 128 ? 2 : 3;
     u32x4 ra[NALL], rb[NALL];
     auto fetch = [&](int t) {
       if (t < NS) {
