@@ -434,11 +434,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 //   phase 2  member h accumulates dV^T += dO^T P and dK^T += Q^T dS for its
 //            feature half over all 64 queries (its own half's P and dS from
 //            registers, the partner's from LDS).
-// One wavefront per SIMD (4 wavefronts, 64 keys per workgroup), and every tile
-// single-buffered to fit LDS: the row-major Q and dO tiles of step i + 1 are
-// written after the phase barrier of step i (phase 1 no longer reads them),
-// their transposed tiles at the start of step i + 1 (phase 2 of step i is
-// done), both from registers loaded during phase 1 of step i.
+// One wavefront per SIMD (4 wavefronts, 64 keys per workgroup).  Q and dO are
+// copied row-major straight into double-buffered LDS tiles (the copies of
+// step i + 1 go out one pass per phase-1 MFMA stage of step i) and read
+// row-wise in phase 1 and transposed (ds_read_b64_tr_b16) in phase 2.
 template <int D>
 struct DkdvSplitCfg {
   static constexpr int PAIRS = 2;
@@ -449,15 +448,12 @@ struct DkdvSplitCfg {
   static constexpr int NDB = D / 32;              // 32-feature blocks
   static constexpr int NBH = NDB / 2;             // feature blocks per member
   static constexpr int DK = D / 16;               // k-steps of S and dP
-  using RowL = RowTileW<D>;
-  static constexpr int TILE = RowL::elems(BQ);
-  static constexpr int TTILE = TrTile<D, 64>::ELEMS;
+  using TileL = RowTile<D>;                       // read row-wise and transposed
+  static constexpr int TILE = TileL::elems(BQ);
   static constexpr int XV = 2 * 2 * 64;           // u32x4 per member: [P | dS][word quad][lane]
-  // register stages per thread: the Q and dO tiles need
-  // StagePlan<D>::THREADS_USED stagers each
-  static constexpr int NSTAGE = 2 * StagePlan<D>::THREADS_USED / THREADS;
+  static constexpr int NP = DmaPlan<D, BQ, THREADS, TileL>::ITER;   // copy passes per tile
   static_assert(D % 64 == 0, "feature halves made of whole 32-feature blocks");
-  static_assert(2 * StagePlan<D>::THREADS_USED % THREADS == 0, "whole stages per thread");
+  static_assert(2 * NP <= 2 * DK, "one copy pass per phase-1 stage");
 };
 
 template <int D, bool CAUSAL, class E>
@@ -466,15 +462,22 @@ struct DkdvSplitWave {
   u32x4 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NBH], dvacc[C::NBH];
   int lane, lr, lh, h, key_w, key_lane;
-  int qrow[C::DK];          // row-major tiles: features 16 s + 8 lh of query 32 h + lr
-  int tr_own, tr_partner;   // transposed tiles: the member's first feature block, own / partner's query half
+  int qrow[C::DK];          // row reads: features 16 s + 8 lh of query 32 h + lr
+  // transposed reads rd of the member's feature block j, first 16-query chunk
+  // of the own (o = 0) and the partner's (o = 1) query half
+  int tro[2][2][C::NBH];
 
   __device__ __forceinline__ void init_offsets() {
+    using L = typename C::TileL;
 #pragma unroll
-    for (int s = 0; s < C::DK; ++s) qrow[s] = C::RowL::elem(32 * h + lr, 16 * s + 8 * lh);
-    const int base = lr * TrTile<D, 64>::ROW + 8 * lh + h * C::NBH * LaneOffsets<D>::TR32;
-    tr_own = base + 32 * h;
-    tr_partner = base + 32 * (1 - h);
+    for (int s = 0; s < C::DK; ++s) qrow[s] = L::elem(32 * h + lr, 16 * s + 8 * lh);
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+        for (int j = 0; j < C::NBH; ++j)
+          tro[o][rd][j] = tr_lane_elem<L>(lane, rd, h * C::NBH + j) + 2 * (o ? 1 - h : h) * L::ROWS16;
   }
 
   // S and dP for query half h (row-major tiles qt, dot), then P (packed to the
@@ -483,9 +486,12 @@ struct DkdvSplitWave {
   // kq0: the key position of the step's first query.  mask: some keys of the
   // block lie past the end or above the diagonal for some of the half's
   // queries (a run-time branch, so that one body serves every step).
+  // issue(t) runs after stage t (the copies of the next step).
+  template <class Issue>
   __device__ __forceinline__ void phase1(bool mask, const uint16_t* qt, const uint16_t* dot,
                                          const float* l2s, const float* dls, int kq0, int Nk,
-                                         float scale_log2, uint32_t (&pw)[8], uint32_t (&dsw)[8]) {
+                                         float scale_log2, uint32_t (&pw)[8], uint32_t (&dsw)[8],
+                                         Issue&& issue) {
     constexpr int NS = 2 * C::DK;   // S (t < DK), then dP
     constexpr int PF = 3;
     u32x4 ra[NS];
@@ -506,6 +512,7 @@ struct DkdvSplitWave {
       if (t < C::DK) sacc = E::mfma(ra[t], kf[t], sacc);
       else pacc = E::mfma(ra[t], vf[t - C::DK], pacc);
       if (t + PF < NS) fetch(t + PF);
+      issue(t);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (t == C::DK + g * C::DK / 4) {
@@ -535,8 +542,9 @@ struct DkdvSplitWave {
 
   // dV^T += dO^T P and dK^T += Q^T dS for the member's feature blocks over the
   // step's four 16-query chunks: the own half's two (B operands pw, dsw), then
-  // the partner's two (px: its P and dS words in LDS).
-  __device__ __forceinline__ void phase2(const uint16_t* qtt, const uint16_t* dott, const u32x4* px,
+  // the partner's two (px: its P and dS words in LDS).  qt, dot: the row-major
+  // Q and dO tiles, read transposed.
+  __device__ __forceinline__ void phase2(const uint16_t* qt, const uint16_t* dot, const u32x4* px,
                                          const uint32_t (&pw)[8], const uint32_t (&dsw)[8]) {
     u32x4 xp[2], xd[2];
 #pragma unroll
@@ -549,9 +557,10 @@ struct DkdvSplitWave {
     u32x4 ra[NT], rb[NT];
     auto fetch = [&](int u) {
       const int k = u / C::NBH, j = u % C::NBH;
-      const int o = (k < 2 ? tr_own : tr_partner) + 16 * (k % 2) + j * LaneOffsets<D>::TR32;
-      ra[u] = lds_read16(dott + o);
-      rb[u] = lds_read16(qtt + o);
+      const int o = k < 2 ? 0 : 1;
+      const int c = (k % 2) * C::TileL::ROWS16;
+      ra[u] = lds_read_tr(dot + tro[o][0][j] + c, dot + tro[o][1][j] + c);
+      rb[u] = lds_read_tr(qt + tro[o][0][j] + c, qt + tro[o][1][j] + c);
     };
 #pragma unroll
     for (int u = 0; u < PF; ++u) fetch(u);
@@ -573,10 +582,8 @@ __global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_ke
     const float* __restrict__ Delta, View dK, View dV, int BH, int H, int Nq, int Nk, int Npad,
     float scale, float scale_log2) {
   using C = DkdvSplitCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[C::TTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[C::TTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][C::TILE];
   __shared__ __attribute__((aligned(16))) u32x4 x_lds[C::WAVES][C::XV];
   __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * C::BQ];   // [L log2e | delta]
 
@@ -601,34 +608,25 @@ __global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_ke
         global_load_lds16(Dh + q0, 16u * (lane - C::BQ / 4), dst);
     }
   };
-  // Register stages: stage k of thread tid is stager (tid + k THREADS) % S of
-  // Q (first S stagers) or dO (the next S), S = StagePlan<D>::THREADS_USED.
-  constexpr int S = StagePlan<D>::THREADS_USED;
   const uint16_t* Qh = Q.head(bh / H, bh % H);
   const uint16_t* dOh = dO.head(bh / H, bh % H);
-  TrStage<D, 64, true> st[C::NSTAGE];
-#pragma unroll
-  for (int k = 0; k < C::NSTAGE; ++k) {
-    const int g = tid + k * C::THREADS;
-    st[k].init(g % S, g < S ? Q.sr : dO.sr);
-  }
-  auto load_stages = [&](int i) {
-#pragma unroll
-    for (int k = 0; k < C::NSTAGE; ++k) st[k].load((tid + k * C::THREADS) < S ? Qh : dOh, i * C::BQ, Nq);
-  };
-  auto store_tr = [&]() {
-#pragma unroll
-    for (int k = 0; k < C::NSTAGE; ++k) st[k].store((tid + k * C::THREADS) < S ? qt_lds : dot_lds);
-  };
-  auto store_rows = [&]() {
-#pragma unroll
-    for (int k = 0; k < C::NSTAGE; ++k)
-      st[k].template store_rows<typename C::RowL>((tid + k * C::THREADS) < S ? q_lds : do_lds);
+  // Q and dO: direct copies into the idle buffers, one pass per phase-1 stage
+  // (Q passes first, then dO).
+  TileDma<D, C::BQ, C::THREADS, typename C::TileL> qdma, dodma;
+  qdma.init(tid, Q.sr);
+  dodma.init(tid, dO.sr);
+  int dma_row = -1;   // first row of the next step's tiles (-1: none)
+  uint16_t *dma_q = nullptr, *dma_do = nullptr;
+  auto issue = [&](int t) {
+    if (dma_row >= 0) {
+      if (t < C::NP) qdma.issue_pass(t, dma_q, Qh, dma_row, Nq);
+      else if (t < 2 * C::NP) dodma.issue_pass(t - C::NP, dma_do, dOh, dma_row, Nq);
+    }
   };
   if (i_begin < n_qblk) {
     load_ld(ld_lds[0], i_begin * C::BQ);
-    load_stages(i_begin);
-    store_rows();
+    qdma.issue(q_lds[0], Qh, i_begin * C::BQ, Nq);
+    dodma.issue(do_lds[0], dOh, i_begin * C::BQ, Nq);
   }
 
   DkdvSplitWave<D, CAUSAL, E> w;
@@ -659,32 +657,32 @@ __global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_ke
   u32x4* x_own = x_lds[wave];
   const u32x4* x_partner = x_lds[(wave + C::PAIRS) % C::WAVES];
   wait_vmem();
-  __syncthreads();   // the first step's row tiles and statistics are in LDS
+  __syncthreads();   // the first step's tiles and statistics are in LDS
 
   for (int i = i_begin; i < n_qblk; ++i) {
-    const int buf = (i - i_begin) & 1;   // statistics buffer of step i
-    store_tr();   // transposed tiles of step i (phase 2 of step i - 1 is done with them)
+    const int buf = (i - i_begin) & 1;   // tile and statistics buffer of step i
     const bool more = i + 1 < n_qblk;
-    // staged on every step (the last re-stages itself)
-    load_stages(more ? i + 1 : i);
     if (more) load_ld(ld_lds[buf ^ 1], (i + 1) * C::BQ);
+    dma_row = more ? (i + 1) * C::BQ : -1;
+    dma_q = q_lds[buf ^ 1];
+    dma_do = do_lds[buf ^ 1];
     const int kq0 = i * C::BQ + koff;   // key position of the step's first query
     // Every pair runs every step of the workgroup: a block whose keys all lie
     // above a step's queries (at most the first step of the second pair) is
     // masked to P = 0 rather than skipped, which keeps one straight-line body.
     const bool need_mask = (CAUSAL && w.key_w + 31 > kq0 + 32 * w.h) || (w.key_w + 32 > Nk);
     uint32_t pw[8], dsw[8];
-    w.phase1(need_mask, q_lds, do_lds, ld_lds[buf], ld_lds[buf] + C::BQ, kq0, Nk, scale_log2, pw, dsw);
+    w.phase1(need_mask, q_lds[buf], do_lds[buf], ld_lds[buf], ld_lds[buf] + C::BQ, kq0, Nk, scale_log2, pw, dsw,
+             issue);
 #pragma unroll
     for (int q4 = 0; q4 < 2; ++q4) {
       x_own[q4 * 64 + w.lane] = acc_chunk(pw, q4);
       x_own[(2 + q4) * 64 + w.lane] = acc_chunk(dsw, q4);
     }
-    __syncthreads();   // P, dS and the transposed tiles visible; the row tiles are free
-    store_rows();      // row tiles of step i + 1
-    w.phase2(qt_lds, dot_lds, x_partner, pw, dsw);
+    __syncthreads();   // both members' P and dS visible
+    w.phase2(q_lds[buf], do_lds[buf], x_partner, pw, dsw);
     wait_vmem();
-    __syncthreads();   // row tiles and statistics of step i + 1 in LDS; X and the transposed tiles free
+    __syncthreads();   // tiles and statistics of step i + 1 in LDS; X and this step's tiles free
   }
 
   // Epilogue: dK = scale * dS^T Q, dV = P^T dO (bf16), the member's features.

@@ -334,6 +334,12 @@ int main() {
   check_tr_reads<80, 64, WideRowTile<80>>();
   check_tr_reads<96, 64, WideRowTile<96>>();
   check_tr_reads<128, 64, RowTile<128>>();
+  // Q and dO tiles of the head-dim-256 dK/dV pass (64 rows, four wavefronts)
+  check_dma<256, 64, 256, RowTile<256>>(max_n, 256);
+  check_dma<256, 64, 256, RowTile<256>>(max_n, 264);
+  check_dma<256, 64, 256, RowTile<256>>(max_n, 768);
+  check_reads<256, 64, RowTile<256>>();
+  check_tr_reads<256, 64, RowTile<256>>();
   check_stage<256, 64, 512, RowTileW<256>>(max_n, 264);
   check_reads<256, 32>();
   check_reads<256, 64, RowTileW<256>>();
