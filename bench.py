@@ -77,31 +77,30 @@ def parse():
 # plain copy of known size (bench.py --calibrate-copy).  Valid only for the
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
-    # (kernel source hash, workload, kernel): HBM bytes read + written per launch
-    ("c670850b0f8c2893", "c1", "bwd_dkdv"): 127358,
-    ("c670850b0f8c2893", "c1", "bwd_dq"): 101886,
-    ("c670850b0f8c2893", "c1", "bwd_preprocess"): 89598,
-    ("c670850b0f8c2893", "c1", "fwd"): 88318,
-    ("c670850b0f8c2893", "c2", "bwd_dkdv"): 1359289906,
-    ("c670850b0f8c2893", "c2", "bwd_dq"): 740476444,
-    ("c670850b0f8c2893", "c2", "bwd_preprocess"): 137428318,
-    ("c670850b0f8c2893", "c2", "fwd"): 672325245,
-    ("c670850b0f8c2893", "c3", "bwd_dkdv"): 1420485359,
-    ("c670850b0f8c2893", "c3", "bwd_dq"): 809646939,
-    ("c670850b0f8c2893", "c3", "bwd_preprocess"): 140568798,
-    ("c670850b0f8c2893", "c3", "fwd"): 762922139,
-    ("c670850b0f8c2893", "c4", "bwd_dkdv"): 869348112,
-    ("c670850b0f8c2893", "c4", "bwd_dq"): 701174150,
-    ("c670850b0f8c2893", "c4", "bwd_preprocess"): 137429086,
-    ("c670850b0f8c2893", "c4", "fwd"): 541150701,
-    ("c670850b0f8c2893", "c5", "bwd_dkdv"): 1782705580,
-    ("c670850b0f8c2893", "c5", "bwd_dq"): 1016431597,
-    ("c670850b0f8c2893", "c5", "bwd_preprocess"): 174125902,
-    ("c670850b0f8c2893", "c5", "fwd"): 1617790744,
-    ("c670850b0f8c2893", "d256", "bwd_dkdv"): 866515644,
-    ("c670850b0f8c2893", "d256", "bwd_dq"): 671293837,
-    ("c670850b0f8c2893", "d256", "bwd_preprocess"): 135866630,
-    ("c670850b0f8c2893", "d256", "fwd"): 500551011,
+    ("c46d5a72a1d82efe", "c1", "bwd_dkdv"): 125054,
+    ("c46d5a72a1d82efe", "c1", "bwd_dq"): 100734,
+    ("c46d5a72a1d82efe", "c1", "bwd_preprocess"): 93694,
+    ("c46d5a72a1d82efe", "c1", "fwd"): 93694,
+    ("c46d5a72a1d82efe", "c2", "bwd_dkdv"): 1359927653,
+    ("c46d5a72a1d82efe", "c2", "bwd_dq"): 740467052,
+    ("c46d5a72a1d82efe", "c2", "bwd_preprocess"): 137429921,
+    ("c46d5a72a1d82efe", "c2", "fwd"): 672351339,
+    ("c46d5a72a1d82efe", "c3", "bwd_dkdv"): 1421118916,
+    ("c46d5a72a1d82efe", "c3", "bwd_dq"): 809629933,
+    ("c46d5a72a1d82efe", "c3", "bwd_preprocess"): 140569697,
+    ("c46d5a72a1d82efe", "c3", "fwd"): 756944074,
+    ("c46d5a72a1d82efe", "c4", "bwd_dkdv"): 868129972,
+    ("c46d5a72a1d82efe", "c4", "bwd_dq"): 740209520,
+    ("c46d5a72a1d82efe", "c4", "bwd_preprocess"): 137430481,
+    ("c46d5a72a1d82efe", "c4", "fwd"): 596178615,
+    ("c46d5a72a1d82efe", "c5", "bwd_dkdv"): 1783468200,
+    ("c46d5a72a1d82efe", "c5", "bwd_dq"): 1013533745,
+    ("c46d5a72a1d82efe", "c5", "bwd_preprocess"): 174112610,
+    ("c46d5a72a1d82efe", "c5", "fwd"): 1647702822,
+    ("c46d5a72a1d82efe", "d256", "bwd_dkdv"): 868148340,
+    ("c46d5a72a1d82efe", "d256", "bwd_dq"): 713771087,
+    ("c46d5a72a1d82efe", "d256", "bwd_preprocess"): 135868649,
+    ("c46d5a72a1d82efe", "d256", "fwd"): 625023306,
 }
 
 
