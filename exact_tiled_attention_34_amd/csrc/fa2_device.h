@@ -225,7 +225,7 @@ struct TileDma {
 // elements apart: begin() and the four load_k() issue the global loads (all
 // at once with load(), or spread over the compute that hides them), store()
 // (once the values are needed, typically after the current tile's compute)
-// writes the transposed tile, store_rows<L>() the same tokens as a row-major tile.
+// writes the transposed tile.
 // Rows past n_rows are clamped to the last row.  ALL: every thread of the
 // workgroup stages (known at compile time, so no thread tests its `act`).
 template <int D, int TOK = 64, bool ALL = false>
@@ -271,28 +271,8 @@ struct TrStage {
       *reinterpret_cast<u32x2*>(dst + e * TrTile<D, TOK>::ROW) = out;
     }
   }
-  // The same tokens as rows 4g..4g+3 of a row-major tile of layout L
-  // (RowTileW: conflict-free stores; RowTile: the layout of a tile that is
-  // read together with a DMA-filled one).  Pad slots are left as they are: no
-  // operand read reaches them.
-  template <class L>
-  __device__ __forceinline__ void store_rows(uint16_t* tile) const {
-    if (!ALL && !act) return;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<u32x4*>(tile + L::elem(4 * g + k, 8 * c)) = r[k];
-  }
 };
 
-// Fill the padding feature rows [D, DP) of a transposed tile (once; staging
-// never writes them): zero, or with first_row = the storage type's 1.0, the
-// first padding row holds ones (a product with it sums over the tokens).
-template <int D, int TOK = 64>
-__device__ __forceinline__ void tr_zero_pad(uint16_t* t, int tid, int nthreads, uint16_t first_row = 0) {
-  using T = TrTile<D, TOK>;
-  if constexpr (T::DP != D)
-    for (int i = tid; i < (T::DP - D) * T::ROW; i += nthreads) t[D * T::ROW + i] = i < T::ROW ? first_row : 0;
-}
 
 // One bf16 [B, H, N, D] tensor addressed through element strides (the last
 // dimension contiguous): element (b, h, n, i) is at p + b sb + h sh + n sr + i.

@@ -341,10 +341,8 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  if constexpr (!C::V_DMA) {
-    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[0] + t * C::VSUB, tid, C::THREADS, E::kOne);
-    for (int t = 0; t < C::SUB; ++t) tr_zero_pad<D, C::BC>(v_lds[1] + t * C::VSUB, tid, C::THREADS, E::kOne);
-  } else if constexpr (C::VL::HAS_CONST) {
+  static_assert(C::V_DMA || TrTile<D, C::BC>::DP == D, "staged V^T tiles have no padding feature rows");
+  if constexpr (C::VL::HAS_CONST) {
     // features 80..95 of every V row: (1, 0, .., 0) and zeros (slots 10, 11)
     for (int i = tid; i < 2 * C::STAGE; i += C::THREADS) {
       const u32x4 one = {(uint32_t)E::kOne, 0u, 0u, 0u}, zero = {0u, 0u, 0u, 0u};

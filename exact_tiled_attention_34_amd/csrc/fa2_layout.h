@@ -74,50 +74,6 @@ struct RowTile {
 };
 
 // ---------------------------------------------------------------------------
-// Row-major tiles written from registers in 4-row groups.
-//
-// A register stage (StagePlan below) writes one chunk of rows 4g + k for the
-// 16 values of g in one store pass: under the RowTile permutation, which
-// depends on row % 16 only, those 16 rows share 4 chunk positions (a 4-way
-// bank conflict on every write).  These tiles keep the read pattern of a
-// RowTile (16 consecutive rows of one chunk on 16 distinct 4-bank groups) and
-// also spread rows 4 apart:
-//   D = 128:     the XOR key also takes rows 16..63 of each 64-row period
-//                into account (row bits 4-5 flip key bits 2-3); D = 256
-//                applies the same key to the low four chunk bits;
-//   D = 64:      a spare slot after every 4 rows, and row bit 1 flips chunk
-//                bit 2;
-//   D = 80, 96:  the RowTile row padding plus a spare slot after every 16 rows.
-// Lane offsets computed for rows 0..31 serve every 32-row block: for D = 128
-// an odd block flips chunk bit 3 (feature step s ^ 4 of the same lane),
-// otherwise a block adds a constant.
-// ---------------------------------------------------------------------------
-template <int D>
-struct RowTileW {
-  static constexpr int CH = D / 8;
-  static constexpr bool PADDED = (CH & (CH - 1)) != 0;
-  static constexpr int SLOTS = PADDED ? CH + 1 : CH;
-  static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16 || CH == 32), "unsupported head dim");
-  // 16-byte slots per 32 rows
-  static constexpr int SLOTS32 = PADDED ? 32 * SLOTS + 2 : CH >= 16 ? 32 * CH : 32 * 8 + 8;
-
-  static FA2_HD int slot(int row, int chunk) {
-    if constexpr (PADDED) {
-      return row * SLOTS + (row >> 4) + chunk;
-    } else if constexpr (CH >= 16) {
-      return row * CH + (chunk ^ ((4 * ((row & 3) ^ ((row >> 4) & 3))) | ((row >> 2) & 3)));
-    } else {
-      return row * 8 + (row >> 2) + (chunk ^ (4 * ((row >> 1) & 1)));
-    }
-  }
-  static FA2_HD int elem(int row, int col) { return slot(row, col >> 3) * 8 + (col & 7); }
-  // bf16 elements to reserve for a tile of `rows` rows (a multiple of 32).
-  static constexpr int elems(int rows) { return rows / 32 * SLOTS32 * 8; }
-  static constexpr int perm(int s, int b) { return CH >= 16 ? (s ^ (4 * (b & 1))) : s; }
-  static constexpr int block(int b) { return b * SLOTS32 * 8; }
-};
-
-// ---------------------------------------------------------------------------
 // Transposed tiles in LDS.
 //
 // Operands whose reduction index is the token (V^T, K^T, Q^T, dO^T) need 8

@@ -85,9 +85,11 @@ void check_dma(int max_n, int R) {
   }
 }
 
-// L: the row-major layout the stage's row stores write (RowTileW for the
-// dK/dV pass's Q and dO tiles, RowTile for the dQ pass's K tile).
-template <int D, int TOK, int THREADS, class L>
+// Register stage of a V tile (the forward at D = 128 and 256): every global
+// address inside the tensor and fetching the (token, chunk) its thread owns,
+// every (token, chunk) of the tile fetched once, every transposed-tile element
+// written once.
+template <int D, int TOK, int THREADS>
 void check_stage(int max_n, int R) {
   using P = StagePlan<D, TOK>;
   using T = TrTile<D, TOK>;
@@ -96,7 +98,7 @@ void check_stage(int max_n, int R) {
   for (int n = 1; n <= max_n; ++n) {
     for (int tok0 = 0; tok0 < n; tok0 += TOK) {
       std::vector<int> cover(TOK * P::CH, 0);
-      std::vector<int> tr_written(T::ELEMS, 0), row_written(L::elems(TOK), 0);
+      std::vector<int> tr_written(T::ELEMS, 0);
       for (int tid = 0; tid < THREADS; ++tid) {
         if (!P::active(tid)) continue;
         const uint32_t off = P::lane_offset(tid, R);
@@ -112,10 +114,6 @@ void check_stage(int max_n, int R) {
           CHECK(addr / row_bytes == want && (addr % row_bytes) / 16 == ch, "D=%d n=%d tid=%d k=%d row %ld want %d",
                 D, n, tid, k, addr / row_bytes, want);
           cover[(4 * g + k) * P::CH + ch]++;
-          // store_rows: 16 bytes at RowTileW elem(4g + k, 8ch)
-          const int re = L::elem(4 * g + k, 8 * ch);
-          CHECK(re >= 0 && re + 8 <= L::elems(TOK), "D=%d row store out of tile", D);
-          for (int e = 0; e < 8 && re >= 0 && re + 8 <= L::elems(TOK); ++e) row_written[re + e]++;
         }
         // store: feature rows 8ch + e, tokens 4g..4g+3 (8 bytes each)
         for (int e = 0; e < 8; ++e) {
@@ -132,23 +130,8 @@ void check_stage(int max_n, int R) {
         for (int tok = 0; tok < TOK; ++tok)
           CHECK(tr_written[T::elem(f, tok)] == 1, "D=%d transposed (%d, %d) written %d times", D, f, tok,
                 tr_written[T::elem(f, tok)]);
-      for (int r = 0; r < TOK; ++r)
-        for (int c = 0; c < D; ++c)
-          CHECK(row_written[L::elem(r, c)] == 1, "D=%d row tile (%d, %d) written %d times", D, r, c,
-                row_written[L::elem(r, c)]);
     }
   }
-  // RowTileW row stores: store k of 16 consecutive active threads reaches 16
-  // distinct bank groups
-  for (int t0 = 0; (std::is_same<L, RowTileW<D>>::value || std::is_same<L, RowTileW<128>>::value) &&
-                  t0 < P::THREADS_USED; t0 += 16)
-    for (int k = 0; k < 4; ++k) {
-      int seen[16] = {0};
-      for (int tid = t0; tid < t0 + 16; ++tid) seen[(L::elem(4 * P::grp(tid) + k, 8 * P::chunk(tid)) / 8) % 16]++;
-      for (int q = 0; q < 16; ++q)
-        CHECK(seen[q] <= 1, "D=%d TOK=%d row store threads %d.. k=%d: bank group %d hit %d times", D, TOK, t0, k, q,
-              seen[q]);
-    }
 }
 
 // Operand reads: row-major tiles of TOK rows are read at row[s] + 2*b*ROW16
@@ -265,40 +248,26 @@ int main() {
     check_dma<80, 64, 768>(max_n, 80 * mult);
     check_dma<96, 64, 768>(max_n, 96 * mult);
     check_dma<128, 64, 768>(max_n, 128 * mult);
-    check_stage<64, 64, 256, RowTileW<64>>(max_n, 64 * mult);
-    check_stage<80, 64, 256, RowTileW<80>>(max_n, 80 * mult);
-    check_stage<96, 64, 256, RowTileW<96>>(max_n, 96 * mult);
-    check_stage<128, 64, 256, RowTileW<128>>(max_n, 128 * mult);
-    check_stage<64, 64, 512, RowTile<64>>(max_n, 64 * mult);
-    check_stage<80, 64, 512, RowTile<80>>(max_n, 80 * mult);
-    check_stage<96, 64, 512, RowTile<96>>(max_n, 96 * mult);
-    check_stage<128, 64, 512, RowTile<128>>(max_n, 128 * mult);
   }
   check_dma<128, 64, 256>(max_n, 136);
   check_dma<80, 64, 512>(max_n, 88);
-  check_stage<128, 64, 256, RowTileW<128>>(max_n, 136);
-  check_stage<80, 64, 256, RowTileW<80>>(max_n, 88);
-  // the dK/dV pass stores D = 80 and 96 rows in 128-wide rows
-  for (int mult : {1, 2, 3}) {
-    check_stage<80, 64, 256, RowTileW<128>>(max_n, 80 * mult);
-    check_stage<96, 64, 256, RowTileW<128>>(max_n, 96 * mult);
-  }
-  check_stage<80, 64, 256, RowTileW<128>>(max_n, 88);
   // 32-row tiles (the dQ kernel's key tile can be 32 keys for D = 64 and 128)
   for (int mult : {1, 3}) {
     check_dma<64, 32, 512>(max_n, 64 * mult);
     check_dma<128, 32, 512>(max_n, 128 * mult);
-    check_stage<64, 32, 512, RowTile<64>>(max_n, 64 * mult);
-    check_stage<128, 32, 512, RowTile<128>>(max_n, 128 * mult);
   }
-  // head dim 256: 32-key tiles of the forward and dQ kernels (256 threads),
-  // 64-query tiles of the dK/dV kernel staged by 256 threads in two halves
+  // head dim 256: 32-key tiles of the forward and dQ kernels (256 threads)
   for (int mult : {1, 2, 3}) {
     check_dma<256, 32, 256>(max_n, 256 * mult);
-    check_stage<256, 32, 256, RowTile<256>>(max_n, 256 * mult);
-    check_stage<256, 64, 512, RowTileW<256>>(max_n, 256 * mult);
   }
   check_dma<256, 32, 256>(max_n, 264);
+  // V tiles the forward stages through registers (D = 128, 256)
+  for (int mult : {1, 2, 3}) {
+    check_stage<128, 64, 512>(max_n, 128 * mult);
+    check_stage<256, 32, 256>(max_n, 256 * mult);
+  }
+  check_stage<128, 64, 512>(max_n, 136);
+  check_stage<256, 32, 256>(max_n, 264);
   // V tiles of the forward (TrRowTile): the thread counts of its workgroups
   for (int mult : {1, 2, 3}) {
     check_dma<64, 64, 512, TrRowTile<64>>(max_n, 64 * mult);
@@ -340,21 +309,13 @@ int main() {
   check_dma<256, 64, 256, RowTile<256>>(max_n, 768);
   check_reads<256, 64, RowTile<256>>();
   check_tr_reads<256, 64, RowTile<256>>();
-  check_stage<256, 64, 512, RowTileW<256>>(max_n, 264);
   check_reads<256, 32>();
-  check_reads<256, 64, RowTileW<256>>();
   check_reads<64, 32>();
   check_reads<128, 32>();
   check_reads<64>();
   check_reads<80>();
   check_reads<96>();
   check_reads<128>();
-  check_reads<64, 64, RowTileW<64>>();
-  check_reads<80, 64, RowTileW<80>>();
-  check_reads<96, 64, RowTileW<96>>();
-  check_reads<128, 64, RowTileW<128>>();
-  check_reads<80, 64, RowTileW<128>>();
-  check_reads<96, 64, RowTileW<128>>();
   if (failures) {
     std::printf("%d violations\n", failures);
     return 1;
