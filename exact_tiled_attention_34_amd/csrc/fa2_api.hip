@@ -72,8 +72,9 @@ fa2::Strided dense(const void* p, int H, int N, int d) { return fa2::contiguous(
 
 // A strided bf16 [B, H, N, d] tensor (s == NULL: contiguous).  Checks: 16-byte
 // aligned base; strides >= 0 and multiples of 8 elements (every row starts on
-// 16 bytes); one head's rows within 2^30 elements (the kernels' 32-bit
-// offsets).  For an output, the element map must be one-to-one: ordered by
+// 16 bytes); one head's rows within 2^30 elements and a row stride of at most
+// 2^20 elements (the kernels' 32-bit offsets: a 128-row tile stays below
+// 2^31 bytes).  For an output, the element map must be one-to-one: ordered by
 // stride, every dimension must step over everything inside it (the last
 // dimension, d elements at stride 1, innermost).  On success *span is the
 // byte range the tensor touches.
@@ -89,7 +90,7 @@ bool strided_view(const void* p, const fa2_strides* s, int B, int H, int N, int 
   const long long ext[3] = {B, H, N};
   for (int i = 0; i < 3; ++i)
     if (st[i] < 0 || st[i] % 8 != 0) return false;
-  if ((long long)(N - 1) * t->row + d > (1LL << 30)) return false;
+  if ((long long)(N - 1) * t->row + d > (1LL << 30) || t->row > (1LL << 20)) return false;
   const long long last = (B - 1) * t->batch + (long long)(H - 1) * t->head + (long long)(N - 1) * t->row + d;
   if (last > (1LL << 40)) return false;
   if (output) {

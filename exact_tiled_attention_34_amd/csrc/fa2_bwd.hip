@@ -270,17 +270,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  if constexpr (C::TileL::HAS_CONST) {
-    // slots of the wide rows that are never copied: zero once
-    for (int s = tid; s < C::BQ * C::TileL::SLOTS; s += C::THREADS)
-      if (C::TileL::chunk_of_slot(s) < 0) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int b = 0; b < 2; ++b) {
-          *reinterpret_cast<u32x4*>(q_lds[b] + 8 * s) = z;
-          *reinterpret_cast<u32x4*>(do_lds[b] + 8 * s) = z;
-        }
-      }
-  }
+  // the constant slots of wide rows are zeros, which every copy stores
+  static_assert(!C::TileL::HAS_CONST || C::TileL::CONST_ZERO, "copies store the constant slots");
 
   // Linear id -> (key block, batch*head); consecutive ids take different heads
   // (XCD round-robin keeps one head's blocks on one XCD).  Key block 0 sees the
@@ -314,17 +305,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // Q and dO: direct copies into the idle buffers.  Inside a step the next
   // step's copies go out one pass per MFMA stage (stages 0..NP-1 Q, then dO;
   // every step has at least 16 stages): issued as one burst before the step,
-  // they measured slower.
+  // they measured slower.  After the last step the tiles have no rows: the
+  // copies then only store zeros into buffers nobody reads again.
   TileDma<D, C::BQ, C::THREADS, typename C::TileL> qdma, dodma;
   qdma.init(tid, Q.sr);
   dodma.init(tid, dO.sr);
-  int dma_row = -1;   // first row of the next step's tiles (-1: none)
-  uint16_t *dma_q = nullptr, *dma_do = nullptr;
+  i32x4 rq, rdo;   // the next step's tiles
+  uint32_t dma_q = 0, dma_do = 0;   // LDS addresses of the idle buffers
   auto issue = [&](int t) {
-    if (dma_row >= 0) {
-      if (t < C::NP) qdma.issue_pass(t, dma_q, Qh, dma_row, Nq);
-      else if (t < 2 * C::NP) dodma.issue_pass(t - C::NP, dma_do, dOh, dma_row, Nq);
-    }
+    if (t < C::NP) qdma.issue_pass(t, dma_q, rq);
+    else if (t < 2 * C::NP) dodma.issue_pass(t - C::NP, dma_do, rdo);
   };
   if (i_begin < n_qblk) {
     load_ld(ld_lds[0], i_begin * C::BQ);
@@ -369,11 +359,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     constexpr int BUF = decltype(buf_tag)::value;
     wait_vmem();
     __syncthreads();   // step i is in LDS; every wave is done with the other buffer
-    const bool more = i + 1 < n_qblk;
-    if (more) load_ld(ld_lds[BUF ^ 1], (i + 1) * C::BQ);
-    dma_row = more ? (i + 1) * C::BQ : -1;
-    dma_q = q_lds[BUF ^ 1];
-    dma_do = do_lds[BUF ^ 1];
+    if (i + 1 < n_qblk) load_ld(ld_lds[BUF ^ 1], (i + 1) * C::BQ);
+    rq = qdma.tile(Qh, (i + 1) * C::BQ, Nq);
+    rdo = dodma.tile(dOh, (i + 1) * C::BQ, Nq);
+    dma_q = lds_address(q_lds[BUF ^ 1]);
+    dma_do = lds_address(do_lds[BUF ^ 1]);
     // kq0: the key position of the step's first query (its last visible key)
     const int kq0 = i * C::BQ + koff;
     const bool need_mask = (CAUSAL && w.key_w + 31 > kq0) || (w.key_w + 32 > Nk);
@@ -387,16 +377,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     } else {
       // a wavefront with no key this step can see still does its share of
       // copying the next one
-      if (dma_row >= 0) {
-        qdma.issue(dma_q, Qh, dma_row, Nq);
-        dodma.issue(dma_do, dOh, dma_row, Nq);
-      }
+#pragma unroll
+      for (int t = 0; t < 2 * C::NP; ++t) issue(t);
     }
   };
   for (int i = i_begin; i < n_qblk; i += 2) {
     iteration(std::integral_constant<int, 0>{}, i);
     if (i + 1 < n_qblk) iteration(std::integral_constant<int, 1>{}, i + 1);
   }
+  wait_vmem();   // the last step's copies: LDS must not be released under them
 
   // Epilogue: dK = scale * dS^T Q, dV = P^T dO (bf16).
   if (w.key_lane < Nk) {
@@ -611,17 +600,16 @@ __global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_ke
   const uint16_t* Qh = Q.head(bh / H, bh % H);
   const uint16_t* dOh = dO.head(bh / H, bh % H);
   // Q and dO: direct copies into the idle buffers, one pass per phase-1 stage
-  // (Q passes first, then dO).
+  // (Q passes first, then dO).  After the last step the tiles have no rows:
+  // the copies then only store zeros into buffers nobody reads again.
   TileDma<D, C::BQ, C::THREADS, typename C::TileL> qdma, dodma;
   qdma.init(tid, Q.sr);
   dodma.init(tid, dO.sr);
-  int dma_row = -1;   // first row of the next step's tiles (-1: none)
-  uint16_t *dma_q = nullptr, *dma_do = nullptr;
+  i32x4 rq, rdo;   // the next step's tiles
+  uint32_t dma_q = 0, dma_do = 0;   // LDS addresses of the idle buffers
   auto issue = [&](int t) {
-    if (dma_row >= 0) {
-      if (t < C::NP) qdma.issue_pass(t, dma_q, Qh, dma_row, Nq);
-      else if (t < 2 * C::NP) dodma.issue_pass(t - C::NP, dma_do, dOh, dma_row, Nq);
-    }
+    if (t < C::NP) qdma.issue_pass(t, dma_q, rq);
+    else if (t < 2 * C::NP) dodma.issue_pass(t - C::NP, dma_do, rdo);
   };
   if (i_begin < n_qblk) {
     load_ld(ld_lds[0], i_begin * C::BQ);
@@ -661,11 +649,11 @@ __global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_ke
 
   for (int i = i_begin; i < n_qblk; ++i) {
     const int buf = (i - i_begin) & 1;   // tile and statistics buffer of step i
-    const bool more = i + 1 < n_qblk;
-    if (more) load_ld(ld_lds[buf ^ 1], (i + 1) * C::BQ);
-    dma_row = more ? (i + 1) * C::BQ : -1;
-    dma_q = q_lds[buf ^ 1];
-    dma_do = do_lds[buf ^ 1];
+    if (i + 1 < n_qblk) load_ld(ld_lds[buf ^ 1], (i + 1) * C::BQ);
+    rq = qdma.tile(Qh, (i + 1) * C::BQ, Nq);
+    rdo = dodma.tile(dOh, (i + 1) * C::BQ, Nq);
+    dma_q = lds_address(q_lds[buf ^ 1]);
+    dma_do = lds_address(do_lds[buf ^ 1]);
     const int kq0 = i * C::BQ + koff;   // key position of the step's first query
     // Every pair runs every step of the workgroup: a block whose keys all lie
     // above a step's queries (at most the first step of the second pair) is
@@ -818,17 +806,8 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  if constexpr (C::TileL::HAS_CONST) {
-    // slots of the wide rows that are never copied: zero once
-    for (int s = tid; s < C::BC * C::TileL::SLOTS; s += C::THREADS)
-      if (C::TileL::chunk_of_slot(s) < 0) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int b = 0; b < 2; ++b) {
-          *reinterpret_cast<u32x4*>(k_lds[b] + 8 * s) = z;
-          *reinterpret_cast<u32x4*>(v_lds[b] + 8 * s) = z;
-        }
-      }
-  }
+  // the constant slots of wide rows are zeros, which every copy stores
+  static_assert(!C::TileL::HAS_CONST || C::TileL::CONST_ZERO, "copies store the constant slots");
   const int nrb = (Nq + C::BR - 1) / C::BR;
   const int bh = blockIdx.x % BH;
   int rb = blockIdx.x / BH;

@@ -26,6 +26,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -171,53 +172,96 @@ __device__ __forceinline__ void global_load_lds16(const void* base, uint32_t byt
 #endif
 }
 
+// Resource descriptor of an untyped byte range [base, base + num_bytes) for
+// the buffer loads below: a load whose byte offset (the per-lane offset plus
+// the scalar one) reaches num_bytes is out of range and returns zeros, and
+// into LDS it stores zeros (measured on MI355X).  Word 3 selects the 32-bit
+// data format with no stride, swizzle or index: plain byte addressing.
+__device__ __forceinline__ i32x4 raw_buffer(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)num_bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// The LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// One 16-byte buffer -> LDS load per lane (buffer_load_dwordx4 ... lds) from
+// byte voff + soff of the range `rsrc`; lane l's 16 bytes land at LDS byte
+// address lds + 16*l, zeros when the offset is out of range.  Inline assembly
+// for the reason given at global_load_lds16.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(m0)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+#endif
+}
+
 // Copies ROWS-row tiles of one head (rows R elements apart, D features) into
-// a RowTile (or a TrRowTile: LT) in LDS with direct global -> LDS loads,
-// following DmaPlan (slots the layout keeps constant are skipped): the
-// per-lane source offsets are computed once (init); a full tile then costs
-// one load per chunk and no vector arithmetic.  Rows past n_rows (the ragged
-// last tile) are clamped to the last row: finite data that the caller masks
-// or weights by zero.  issue() returns immediately; wait_vmem() and a
-// workgroup barrier make the tile visible.
+// a RowTile (or a TrRowTile / WideRowTile: LT) in LDS with buffer -> LDS
+// loads, following DmaPlan.  The per-lane byte offsets within a tile are
+// computed once (init); a tile's resource (tile()) covers only its rows that
+// exist, so the rows of a ragged last tile, and every row of a tile that
+// starts at or past the end, arrive as zeros with no test in the kernel.  A
+// pass then costs one scalar offset, the LDS address and the load.  Slots
+// that the layout keeps at zero are loaded out of range (zeros again); slots
+// holding other constants are left out by lane.  issue() returns at once;
+// wait_vmem() and a workgroup barrier make the tile visible.
+//
+// Offsets stay below 2^31: the row pitch is at most 2^20 elements (checked by
+// the API), so a tile spans at most 128 * 2^21 bytes.
 template <int D, int ROWS, int THREADS, class LT = RowTile<D>>
 struct TileDma {
   using P = DmaPlan<D, ROWS, THREADS, LT>;
   uint32_t off[P::NOFF];
-  int lrow[P::NOFF];
   int wave, R;
 
   __device__ __forceinline__ void init(int tid, int row_pitch) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     R = row_pitch;
 #pragma unroll
-    for (int t = 0; t < P::NOFF; ++t) {
-      off[t] = P::lane_offset(wave, tid & 63, t, R);
-      lrow[t] = P::lane_row(wave, tid & 63, t);
-    }
+    for (int t = 0; t < P::NOFF; ++t) off[t] = P::stored_offset(wave, tid & 63, t, row_pitch);
   }
-  // Pass t of the copy (t < P::ITER; requires 0 <= row0 < n_rows).  row0 is
-  // the same in every lane (made visibly so: the load takes a scalar base).
-  __device__ __forceinline__ void issue_pass(int t, uint16_t* tile, const uint16_t* head, int row0,
-                                             int n_rows) const {
+  // The resource of the tile whose first row is row0 (row0 >= 0): rows
+  // row0 .. n_rows - 1 of it, none when row0 >= n_rows.
+  __device__ __forceinline__ i32x4 tile(const uint16_t* head, int row0, int n_rows) const {
     row0 = __builtin_amdgcn_readfirstlane(row0);
+    const int rows = n_rows - row0;
+    return raw_buffer(head + (size_t)row0 * R, P::tile_bytes(rows < ROWS ? rows : ROWS, R));
+  }
+  // Pass t of the copy of the tile `rs` into the tile at LDS byte address `tile`.
+  __device__ __forceinline__ void issue_pass(int t, uint32_t tile, i32x4 rs) const {
     const int first = P::pass_slot(wave, t);   // wavefront-uniform
-    if (first < P::TOTAL) {
-      int base_row;
-      uint32_t o;
-      const int i = P::off_index(t);
-      P::source(off[i], lrow[i], t, row0, n_rows, R, &base_row, &o);
-      if constexpr (LT::HAS_CONST) {
-        if (off[i] != P::kSkip) global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+    if (P::TOTAL % THREADS == 0 || first < P::TOTAL) {
+      const uint32_t o = off[P::off_index(t)];
+      const uint32_t soff = P::pass_offset(t, R);
+      const uint32_t dst = tile + (uint32_t)first * 16u;
+      if constexpr (P::SKIP_BY_LANE) {
+        if (o != P::kSkip) buffer_load_lds16(rs, o, soff, dst);
       } else {
-        global_load_lds16(head + (size_t)base_row * R, o, tile + first * 8);
+        buffer_load_lds16(rs, o, soff, dst);
       }
     }
   }
-  // requires 0 <= row0 < n_rows
+  // The whole tile at row0 (row0 >= 0; rows at or past n_rows arrive as zeros).
   __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* head, int row0,
                                         int n_rows) const {
+    const i32x4 rs = this->tile(head, row0, n_rows);
+    const uint32_t dst = lds_address(tile);
 #pragma unroll
-    for (int t = 0; t < P::ITER; ++t) issue_pass(t, tile, head, row0, n_rows);
+    for (int t = 0; t < P::ITER; ++t) issue_pass(t, dst, rs);
   }
 };
 

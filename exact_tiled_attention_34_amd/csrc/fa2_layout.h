@@ -37,6 +37,7 @@ struct RowTile {
   static constexpr bool PADDED = (CH & (CH - 1)) != 0;
   static constexpr int SLOTS = PADDED ? CH + 1 : CH;
   static constexpr bool HAS_CONST = false;        // every slot is copied from the tensor
+  static constexpr bool CONST_ZERO = false;
   static_assert(D % 16 == 0 && (PADDED || CH == 8 || CH == 16 || CH == 32), "unsupported head dim");
 
   // XOR key of a row (an involution on the chunk index); depends on row % 16.
@@ -131,6 +132,7 @@ struct TrRowTile {
   static constexpr bool PADDED = LINEAR;          // not a 16-row XOR period (DmaPlan)
   static constexpr int SLOTS = LINEAR ? 12 : CH;
   static constexpr bool HAS_CONST = D == 80;     // slots 10 and 11 are constant
+  static constexpr bool CONST_ZERO = false;      // slot 10 is not zero
   static_assert(LINEAR || D == 64 || D == 128 || D == 256, "unsupported head dim");
 
   static FA2_HD int slot(int row, int chunk) {
@@ -166,8 +168,8 @@ FA2_HD int tr_lane_elem(int lane, int rd, int mb) {
 // D = 80 and 96 features in 128-feature rows: the RowTile<128> layout (whose
 // swizzle suits both 16-byte row reads and transposed reads), of which only
 // the first D / 8 chunks of each row are copied from the tensor; the other
-// slots (chunk -1 for the copy plan) are zeroed once by the kernel and feed
-// only padding rows of the feature blocks.
+// slots (chunk -1 for the copy plan) hold zeros, which every copy stores
+// (DmaPlan::stored_offset), and feed only padding rows of the feature blocks.
 // ---------------------------------------------------------------------------
 template <int D>
 struct WideRowTile {
@@ -177,6 +179,7 @@ struct WideRowTile {
   static constexpr bool PADDED = false;
   static constexpr int SLOTS = 16;
   static constexpr bool HAS_CONST = DCH < 16;
+  static constexpr bool CONST_ZERO = true;       // the constant slots hold zeros
   static_assert(D == 80 || D == 96, "wide rows for D = 80, 96");
   static FA2_HD int slot(int row, int chunk) { return W::slot(row, chunk); }
   static FA2_HD int elem(int row, int col) { return W::elem(row, col); }
@@ -194,7 +197,7 @@ struct WideRowTile {
 // Direct global -> LDS copy of a RowTile of ROWS rows by THREADS threads.
 //
 // Pass t moves slots [t*THREADS, (t+1)*THREADS); wavefront w's 64 lanes move
-// the 64 consecutive slots starting at w*64 + t*THREADS (a global_load_lds
+// the 64 consecutive slots starting at w*64 + t*THREADS (a load into LDS
 // writes lane l's 16 bytes at its wavefront base + 16 l).  Rows of the source
 // tensor lie R elements apart (R >= D, a multiple of 8: the row pitch, D for a
 // contiguous [.., N, D] tensor).  The chunk swizzle repeats every 16 rows, so
@@ -237,26 +240,27 @@ struct DmaPlan {
     return (uint32_t)((s / L::SLOTS) * R + c * 8) * 2u;
   }
 
-  // Source of pass t given the stored offset `off` and row `lrow` (those of
-  // pass off_index(t)): the load reads the 16 bytes at
-  //   head + base_row * R elements + byte_off bytes.
-  // Rows at or past n_rows are clamped to n_rows - 1.  Requires
-  // 0 <= row0 < n_rows; then base_row <= row0 (it never points past the
-  // tensor) and byte_off is a non-negative offset into it.
-  static FA2_HD void source(uint32_t off, int lrow, int t, int row0, int n_rows, int R, int* base_row,
-                            uint32_t* byte_off) {
-    const int shift = period_start(t) * RPP;   // rows between the stored pass and pass t
-    if (row0 + ROWS <= n_rows) {
-      // full tile: for PERIODIC the pass moves the scalar base instead
-      *base_row = row0 + (PERIODIC ? shift : 0);
-      *byte_off = off;
-      return;
-    }
-    const int rt = lrow + (PERIODIC ? shift : 0);   // row of the chunk within the tile
-    const int last = n_rows - 1 - row0;
-    const int rc = rt < last ? rt : last;
-    *base_row = row0;
-    *byte_off = (uint32_t)((int)off + (rc - lrow) * 2 * R);
+  // The offset a copy stores for lane `lane` of pass t (t < NOFF): that of
+  // its chunk, or for a constant slot kOutOfRange (past any tile, so the slot
+  // is stored as zeros) when the layout's constants are zeros, else kSkip
+  // (the lane does not load).
+  static constexpr uint32_t kOutOfRange = 0x80000000u;
+  static constexpr bool SKIP_BY_LANE = L::HAS_CONST && !L::CONST_ZERO;
+  static FA2_HD uint32_t stored_offset(int wave, int lane, int t, int R) {
+    const uint32_t o = lane_offset(wave, lane, t, R);
+    return (o == kSkip && !SKIP_BY_LANE) ? kOutOfRange : o;
+  }
+  // The copy of a tile reads a byte range that starts at the tile's first
+  // row: pass t of a lane reads the 16 bytes at lane_offset(off_index(t)) +
+  // pass_offset(t) of it, and a read at or past tile_bytes() returns zeros.
+  // Bytes between the stored pass off_index(t) and pass t:
+  static FA2_HD uint32_t pass_offset(int t, int R) {
+    return PERIODIC ? (uint32_t)(period_start(t) * RPP) * (uint32_t)R * 2u : 0u;
+  }
+  // Bytes of the range of a tile of which `rows` rows exist (0 .. ROWS): up
+  // to the last feature of its last row.
+  static FA2_HD uint32_t tile_bytes(int rows, int R) {
+    return rows <= 0 ? 0u : (uint32_t)(rows - 1) * (uint32_t)R * 2u + (uint32_t)D * 2u;
   }
 };
 

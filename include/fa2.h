@@ -83,7 +83,7 @@ typedef enum fa2_status {
  * base + j*H*d with {N*3*H*d, d, 3*H*d}.
  * Requirements (else FA2_ERR_INVALID_ARG): the base 16-byte aligned; every
  * stride >= 0 and a multiple of 8 (the stride of a dimension of extent 1 is
- * ignored); (N-1)*row + d <= 2^30.  An output tensor
+ * ignored); (N-1)*row + d <= 2^30 and row <= 2^20.  An output tensor
  * must also map its elements one to one: ordered by stride, every dimension
  * steps over everything inside it (the d contiguous elements innermost).
  */

@@ -11,6 +11,7 @@
 // simulated lane by lane and checked for content and banks (check_tr_reads).
 // Prints "ok" and exits 0, or prints the first violation and exits 1.
 #include <cstdio>
+#include <cstdint>
 #include <cstdlib>
 #include <type_traits>
 #include <vector>
@@ -33,54 +34,72 @@ static int failures = 0;
 
 // Rows of the source tensor lie R elements apart (R = D: contiguous rows;
 // R > D: a strided view such as one head of a [B, N, H, D] tensor); the
-// tensor's last byte is that of row n - 1's last feature.
+// tensor's last byte is that of row n - 1's last feature.  A tile copy reads
+// a byte range that starts at the tile's first row and ends tile_bytes()
+// later; a lane's read at or past that end stores zeros (the buffer range
+// check).  So: every chunk of a row that exists must be read in range, from
+// that row and chunk, inside the tensor; every slot of a row past the end,
+// and every zero-constant slot, must be read out of range; slots of other
+// constants must be left out by lane; no offset may wrap 32 bits.  Tiles
+// starting at or past the end (the copies after a last step) are covered.
 template <int D, int ROWS, int THREADS, class LT = RowTile<D>>
 void check_dma(int max_n, int R) {
   using P = DmaPlan<D, ROWS, THREADS, LT>;
   using L = LT;
   const long row_bytes = 2L * R;
   for (int n = 1; n <= max_n; ++n) {
-    for (int row0 = 0; row0 < n; row0 += ROWS) {
+    for (int row0 = 0; row0 < n + ROWS; row0 += ROWS) {
+      const int rows = n - row0;
+      const uint64_t bytes = P::tile_bytes(rows < ROWS ? rows : ROWS, R);
+      CHECK(bytes < (1ull << 31) && bytes % 16 == 0, "D=%d R=%d range %llu", D, R, (unsigned long long)bytes);
       std::vector<int> written(P::TOTAL, 0);
       for (int wave = 0; wave < THREADS / 64; ++wave) {
         for (int t = 0; t < P::ITER; ++t) {
           const int first = P::pass_slot(wave, t);
+          CHECK(P::TOTAL % THREADS != 0 || first < P::TOTAL, "D=%d full plan with a missing pass", D);
           if (first >= P::TOTAL) continue;
           for (int lane = 0; lane < 64; ++lane) {
             const int slot = first + lane;
             CHECK(slot < P::TOTAL, "D=%d slot %d", D, slot);
             if (slot >= P::TOTAL) continue;
-            const int ti = P::off_index(t);
-            const uint32_t off = P::lane_offset(wave, lane, ti, R);
-            if (L::chunk_of_slot(slot) < 0) {   // a constant slot: never copied
-              CHECK(L::HAS_CONST && off == P::kSkip, "D=%d constant slot %d not skipped", D, slot);
+            const uint32_t off = P::stored_offset(wave, lane, P::off_index(t), R);
+            const int c = L::chunk_of_slot(slot);
+            if (off == P::kSkip) {   // left out by lane
+              CHECK(P::SKIP_BY_LANE && c < 0, "D=%d slot %d skipped", D, slot);
               continue;
             }
-            CHECK(off != P::kSkip, "D=%d slot %d skipped", D, slot);
             written[slot]++;
-            int base_row;
-            uint32_t o;
-            P::source(off, P::lane_row(wave, lane, ti), t, row0, n, R, &base_row, &o);
-            CHECK(base_row >= 0 && base_row <= n - 1, "D=%d n=%d row0=%d base_row=%d", D, n, row0, base_row);
-            CHECK(o < (1u << 31), "D=%d n=%d row0=%d t=%d offset wraps: %u", D, n, row0, t, o);
-            const long addr = base_row * row_bytes + (long)o;
+            const uint64_t total = (uint64_t)off + P::pass_offset(t, R);
+            CHECK(total < (1ull << 32) && total % 16 == 0, "D=%d R=%d t=%d offset %llu", D, R, t,
+                  (unsigned long long)total);
+            const bool in_range = total < bytes;
+            const int row = row0 + slot / L::SLOTS;
+            if (c < 0) {
+              CHECK(L::CONST_ZERO && !in_range, "D=%d n=%d row0=%d constant slot %d read in range", D, n, row0,
+                    slot);
+              continue;
+            }
+            if (row >= n) {
+              CHECK(!in_range, "D=%d R=%d n=%d row0=%d slot %d (row %d past the end) read in range", D, R, n,
+                    row0, slot, row);
+              continue;
+            }
+            CHECK(in_range, "D=%d R=%d THREADS=%d n=%d row0=%d t=%d slot %d out of range", D, R, THREADS, n,
+                  row0, t, slot);
+            const long addr = (long)row0 * row_bytes + (long)total;
             const long end = (n - 1) * row_bytes + 2L * D;
-            CHECK(addr >= 0 && addr + 16 <= end && addr % 16 == 0 && addr % row_bytes + 16 <= 2L * D,
-                  "D=%d R=%d THREADS=%d n=%d row0=%d t=%d wave=%d lane=%d addr=%ld of %ld", D, R, THREADS, n,
-                  row0, t, wave, lane, addr, end);
-            const long row = addr / row_bytes;
-            const int chunk = (int)((addr % row_bytes) / 16);
-            int want_row = row0 + slot / L::SLOTS;
-            if (want_row > n - 1) want_row = n - 1;
-            CHECK(row == want_row && chunk == L::chunk_of_slot(slot),
-                  "D=%d n=%d row0=%d slot=%d: row %ld chunk %d, want %d %d", D, n, row0, slot, row, chunk,
-                  want_row, L::chunk_of_slot(slot));
+            CHECK(addr + 16 <= end && addr % row_bytes + 16 <= 2L * D,
+                  "D=%d R=%d n=%d row0=%d t=%d wave=%d lane=%d addr=%ld of %ld", D, R, n, row0, t, wave, lane,
+                  addr, end);
+            CHECK(addr / row_bytes == row && (int)((addr % row_bytes) / 16) == c,
+                  "D=%d n=%d row0=%d slot=%d: row %ld chunk %ld, want %d %d", D, n, row0, slot, addr / row_bytes,
+                  (addr % row_bytes) / 16, row, c);
           }
         }
       }
       for (int s = 0; s < P::TOTAL; ++s)
-        CHECK(written[s] == (L::chunk_of_slot(s) < 0 ? 0 : 1), "D=%d THREADS=%d slot %d written %d times", D,
-              THREADS, s, written[s]);
+        CHECK(written[s] == (P::SKIP_BY_LANE && L::chunk_of_slot(s) < 0 ? 0 : 1),
+              "D=%d THREADS=%d slot %d written %d times", D, THREADS, s, written[s]);
     }
   }
 }
@@ -307,6 +326,11 @@ int main() {
   check_dma<256, 64, 256, RowTile<256>>(max_n, 256);
   check_dma<256, 64, 256, RowTile<256>>(max_n, 264);
   check_dma<256, 64, 256, RowTile<256>>(max_n, 768);
+  // the largest row pitch the API accepts (2^20 elements): no offset wraps
+  check_dma<128, 64, 256>(70, 1 << 20);
+  check_dma<64, 128, 512>(140, 1 << 20);
+  check_dma<96, 64, 256, WideRowTile<96>>(70, 1 << 20);
+  check_dma<256, 64, 256, RowTile<256>>(70, 1 << 20);
   check_reads<256, 64, RowTile<256>>();
   check_tr_reads<256, 64, RowTile<256>>();
   check_reads<256, 32>();

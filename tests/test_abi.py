@@ -167,6 +167,7 @@ def test_strided_entry_points_reject(lib):
     assert fwd_s(sq=S(H * N * d, N * d, d + 4), dtype=1) == INVALID
     assert fwd_s(dtype=2) == INVALID                              # unknown 16-bit type
     assert fwd_s(sq=S(0, 0, 1 << 24)) == INVALID                  # rows beyond 2^30 elements
+    assert fwd_s(sq=S(H * N * d, N * d, (1 << 20) + 8)) == INVALID   # row stride beyond 2^20 elements
     # backward: an output inside an input, the workspace inside an output
     need = lib.fa2_bwd_workspace_bytes(B, H, N, d)
     args = [P[0], None, P[1], None, P[2], None, P[3], None, P[4], P[5], None,
