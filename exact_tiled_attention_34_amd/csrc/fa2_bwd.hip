@@ -127,7 +127,7 @@ struct DkdvWave {
   u32x4 kf[C::DK], vf[C::DK];
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
-  LaneOffsets<D, 64, typename C::TileL> off;
+  LaneOffsets<D, typename C::TileL> off;
   int tro[2][C::NDB];   // transposed reads 0 and 1 of feature block mb
 
   __device__ __forceinline__ void init_offsets() {
@@ -727,7 +727,7 @@ struct DqWave {
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
   int key_last;   // causal: last key this lane's query may see (q_lane + Nk - Nq)
-  LaneOffsets<D, DqCfg<D>::BC, typename DqCfg<D>::TileL> off;
+  LaneOffsets<D, typename DqCfg<D>::TileL> off;
   int tro[2][C::NDB];   // transposed reads 0 and 1 of feature block mb
 
   __device__ __forceinline__ void init_offsets() {

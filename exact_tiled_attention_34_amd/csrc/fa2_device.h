@@ -265,59 +265,6 @@ struct TileDma {
   }
 };
 
-// Stager of one tile of TOK tokens through registers (StagePlan), rows R
-// elements apart: begin() and the four load_k() issue the global loads (all
-// at once with load(), or spread over the compute that hides them), store()
-// (once the values are needed, typically after the current tile's compute)
-// writes the transposed tile.
-// Rows past n_rows are clamped to the last row.  ALL: every thread of the
-// workgroup stages (known at compile time, so no thread tests its `act`).
-template <int D, int TOK = 64, bool ALL = false>
-struct TrStage {
-  using P = StagePlan<D, TOK>;
-  u32x4 r[4];
-  uint32_t off;
-  int g, c, R;
-  bool act;
-  const char* src;
-  int lastk;
-  __device__ __forceinline__ void init(int tid, int row_pitch) {
-    act = P::active(tid);
-    g = P::grp(tid);
-    c = P::chunk(tid);
-    R = row_pitch;
-    off = P::lane_offset(tid, R);
-  }
-  // requires 0 <= tok0 < n_rows
-  __device__ __forceinline__ void begin(const uint16_t* head, int tok0, int n_rows) {
-    src = reinterpret_cast<const char*>(head + (size_t)tok0 * R);
-    lastk = P::last_k(g, tok0, n_rows);
-  }
-  __device__ __forceinline__ void load_k(int k) {
-    if (ALL || act) r[k] = ld_global16(src + (uint32_t)P::source_k(off, k, lastk, R));
-  }
-  __device__ __forceinline__ void load(const uint16_t* head, int tok0, int n_rows) {
-    begin(head, tok0, n_rows);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) load_k(k);
-  }
-  __device__ __forceinline__ void store(uint16_t* tile) const {
-    if (!ALL && !act) return;
-    uint16_t* dst = tile + TrTile<D, TOK>::elem(8 * c, 4 * g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      // feature 8 c + e of tokens 4g..4g+3: low or high halves of word w
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 out;
-      out[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
-      out[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
-      *reinterpret_cast<u32x2*>(dst + e * TrTile<D, TOK>::ROW) = out;
-    }
-  }
-};
-
-
 // One bf16 [B, H, N, D] tensor addressed through element strides (the last
 // dimension contiguous): element (b, h, n, i) is at p + b sb + h sh + n sr + i.
 // sr is the row pitch R of the tile copies and stages.

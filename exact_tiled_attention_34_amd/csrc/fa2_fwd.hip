@@ -64,27 +64,22 @@ struct FwdCfg {
   static constexpr int DP = (D + 31) / 32 * 32;   // O^T rows padded to whole 32-row MFMA blocks
   static constexpr int NDB = DP / 32;
   static constexpr int DK = D / 16;               // k-steps of K Q^T
-  // Tiles per stage: a stage of SUB tiles is staged together and opened by one
-  // workgroup barrier (half the barriers at SUB = 2, and the V tiles of a stage
-  // are staged by twice as many threads).  Two at D = 64, where it also keeps
+  // Tiles per stage: a stage of SUB tiles is copied together and opened by one
+  // workgroup barrier (half the barriers at SUB = 2).  Two at D = 64, where it also keeps
   // the non-causal kernel within 128 VGPRs (B8 H16 N2048 d64: -12 %; B4 H32
   // N4096 d64 causal: -1 %); at D = 96 and 128 it measured even or slower
   // (B1 H16 N16384 d128 causal: +1.5 %).
   static constexpr int SUB = D == 64 && !CAUSAL ? 2 : 1;
   static constexpr int STAGE = SUB * BC;          // keys per stage
   static constexpr int TILE = RowTile<D>::elems(STAGE);
-  // V tiles: at D <= 96 copied row-major like K and read transposed by the
-  // P V product (TrRowTile: no register staging, which at four and three
-  // wavefronts per SIMD competes with the softmax for the vector unit:
-  // B4 H32 N4096 d64 causal forward -4 %, B2 H32 N8192 d80 causal and
-  // B2 H24 N8192 d96 causal -2 %); at D = 128 and 256 transposed on the way
-  // through registers (TrTile), which measured 2-4 % faster there
-  // (B1 H16 N16384 d128 causal, B1 H16 N8192 d256 causal).
-  static constexpr bool V_DMA = D <= 96;
+  // V tiles: copied row-major like K and read transposed by the P V product
+  // (TrRowTile).  Against staging them transposed through registers, which
+  // competes with the softmax for the vector unit: forward B4 H32 N4096 d64
+  // causal -4 %, B2 H32 N8192 d80 causal and B2 H24 N8192 d96 causal -2 %,
+  // B1 H16 N16384 d128 causal -1.6 %, B8 H16 N2048 d128 -2.5 %, B1 H16 N8192
+  // d256 causal -3 % (MI355X).
   using VL = TrRowTile<D>;
-  static constexpr int VSUB = TrTile<D, BC>::ELEMS;                // one staged V^T tile
-  static constexpr int VTILE = V_DMA ? VL::elems(STAGE) : SUB * VSUB;
-  static constexpr int VSTAGERS = StagePlan<D, BC>::THREADS_USED;   // threads per staged V tile
+  static constexpr int VTILE = VL::elems(STAGE);
   // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint);
   // fewer at D = 96, whose three wavefronts per SIMD have 170 registers each
   static constexpr int READ_AHEAD = D == 96 ? 4 : 6;
@@ -127,8 +122,8 @@ struct FwdWave {
   int lane, lr, lh, q_wave, q_lane;
   int key_last;        // causal: last key this lane's query may see (q_lane + Nk - Nq)
   int key_last_wave;   // the same for the wavefront's last query row
-  LaneOffsets<D, FwdCfg<D, CAUSAL>::BC> off;
-  int vtr[2][C::NDB];  // V_DMA: TrRowTile offsets of the V^T reads 0 and 1 per feature block
+  LaneOffsets<D> off;
+  int vtr[2][C::NDB];  // TrRowTile offsets of the V^T reads 0 and 1 per feature block
 
   __device__ __forceinline__ void init_offsets() {
     off.init(lane);
@@ -244,9 +239,8 @@ struct FwdWave {
   }
 
   // O^T (d x query) += V^T (d x 16 keys) P^T (16 keys x query) over the 16-key
-  // chunks of score blocks [KB0, KB0 + NKB).  V_DMA: V^T by two transposed
-  // reads of the row-major V tile vt per operand; otherwise one read of the
-  // transposed tile vt.
+  // chunks of score blocks [KB0, KB0 + NKB): V^T by two transposed reads of
+  // the row-major V tile vt per operand.
   template <int KB0, int NKB>
   __device__ __forceinline__ void pv(const uint16_t* vt, const uint32_t (&pw)[C::KB][8]) {
 #pragma unroll
@@ -254,18 +248,11 @@ struct FwdWave {
       const u32x4 b = acc_chunk(pw[c >> 1], c & 1);
 #pragma unroll
       for (int mb = 0; mb < C::NDB; ++mb) {
-        u32x4 a;
-        if constexpr (C::V_DMA)
-          a = lds_read_tr(vt + vtr[0][mb] + c * C::VL::ROWS16, vt + vtr[1][mb] + c * C::VL::ROWS16);
-        else
-          a = lds_read16(vt + off.tr + 16 * c + mb * LaneOffsets<D, FwdCfg<D, CAUSAL>::BC>::TR32);
+        const u32x4 a = lds_read_tr(vt + vtr[0][mb] + c * C::VL::ROWS16, vt + vtr[1][mb] + c * C::VL::ROWS16);
         oacc[mb] = E::mfma(a, b, oacc[mb]);
       }
     }
-    if constexpr (C::V_DMA)
-      mfma_pipeline_hint<2, 2 * NKB * C::NDB, 4 * NKB * C::NDB, C::READ_AHEAD, 2>();
-    else
-      mfma_pipeline_hint<2, 2 * NKB * C::NDB, 2 * NKB * C::NDB, C::READ_AHEAD>();
+    mfma_pipeline_hint<2, 2 * NKB * C::NDB, 4 * NKB * C::NDB, C::READ_AHEAD, 2>();
   }
 
   // Softmax and O += V P over score blocks [KB0, KB0 + NKB) of the tile.
@@ -281,35 +268,25 @@ struct FwdWave {
 
 // Stage J (PAR = J % 2, a compile-time constant so that LDS buffers are
 // immediate offsets) holds tiles J*SUB .. J*SUB + SUB - 1: issue the copies of
-// stage J+1's K (and V_DMA: V) or the register loads of this thread's staged V
-// tile, then per tile scores, softmax, the rare rescale and O += V(j) P(j),
-// then (staged V) the transposed store of that V tile.  Tiles from n_full on
-// are masked.  vsub: the tile of a stage whose V this thread stages (>= SUB:
-// none).
+// stage J+1's K and V, then per tile scores, softmax, the rare rescale and
+// O += V(j) P(j).  Tiles from n_full on are masked.
 template <int D, bool CAUSAL, class E, int PAR>
-__device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, FwdCfg<D, CAUSAL>::BC>& vstage,
+__device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w,
                                           const TileDma<D, FwdCfg<D, CAUSAL>::STAGE, FwdCfg<D, CAUSAL>::THREADS>& kdma,
                                           const TileDma<D, FwdCfg<D, CAUSAL>::STAGE, FwdCfg<D, CAUSAL>::THREADS,
                                                         TrRowTile<D>>& vdma,
                                           uint16_t (*k_lds)[FwdCfg<D, CAUSAL>::TILE],
                                           uint16_t (*v_lds)[FwdCfg<D, CAUSAL>::VTILE],
-                                          const uint16_t* Kh, const uint16_t* Vh, int J, int vsub,
+                                          const uint16_t* Kh, const uint16_t* Vh, int J,
                                           int n_tiles, int n_full, int Nk, float scale_log2) {
   using C = FwdCfg<D, CAUSAL>;
   wait_vmem();
   __syncthreads();   // stage J is in LDS; every wave is done with the other buffer
   const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
-  const bool more = J + 1 < n_stages;
-  if (more) {
+  if (J + 1 < n_stages) {
     kdma.issue(k_lds[PAR ^ 1], Kh, (J + 1) * C::STAGE, Nk);
-    if constexpr (C::V_DMA) vdma.issue(v_lds[PAR ^ 1], Vh, (J + 1) * C::STAGE, Nk);
+    vdma.issue(v_lds[PAR ^ 1], Vh, (J + 1) * C::STAGE, Nk);
   }
-  // A staged V tile is loaded and stored on every stage (the last one
-  // re-stages itself into the idle buffer), so its registers never live
-  // across stages.
-  const int jv = (more ? J + 1 : J) * C::SUB + vsub;
-  const bool vdo = !C::V_DMA && vsub < C::SUB && jv < n_tiles;
-  if (vdo) vstage.load(Vh, jv * C::BC, Nk);
 #pragma unroll
   for (int sub = 0; sub < C::SUB; ++sub) {
     const int j = J * C::SUB + sub;
@@ -318,17 +295,17 @@ __device__ __forceinline__ void fwd_stage(FwdWave<D, CAUSAL, E>& w, TrStage<D, F
     if (j < n_tiles && (!mask || !CAUSAL || j * C::BC <= w.key_last_wave)) {
       w.scores(k_lds[PAR] + sub * RowTile<D>::block(C::KB), w.sc[0]);
       if (mask) w.apply_mask(w.sc[0], j * C::BC, Nk);
+      const uint16_t* vt = v_lds[PAR] + sub * (C::BC / 16) * C::VL::ROWS16;
       // With the lazy maximum each 32-key block is a softmax step of its own,
       // so the exponentials of block 1 can run under the products of block 0.
       if constexpr (C::BLOCK_STEPS) {
-        w.template softmax_pv<0, 1>(v_lds[PAR] + sub * (C::V_DMA ? (C::BC / 16) * C::VL::ROWS16 : C::VSUB), scale_log2);
-        w.template softmax_pv<1, 1>(v_lds[PAR] + sub * (C::V_DMA ? (C::BC / 16) * C::VL::ROWS16 : C::VSUB), scale_log2);
+        w.template softmax_pv<0, 1>(vt, scale_log2);
+        w.template softmax_pv<1, 1>(vt, scale_log2);
       } else {
-        w.template softmax_pv<0, C::KB>(v_lds[PAR] + sub * (C::V_DMA ? (C::BC / 16) * C::VL::ROWS16 : C::VSUB), scale_log2);
+        w.template softmax_pv<0, C::KB>(vt, scale_log2);
       }
     }
   }
-  if (vdo) vstage.store(v_lds[PAR ^ 1] + vsub * C::VSUB);
 }
 
 template <int D, bool CAUSAL, class E>
@@ -341,7 +318,6 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  static_assert(C::V_DMA || TrTile<D, C::BC>::DP == D, "staged V^T tiles have no padding feature rows");
   if constexpr (C::VL::HAS_CONST) {
     // features 80..95 of every V row: (1, 0, .., 0) and zeros (slots 10, 11)
     for (int i = tid; i < 2 * C::STAGE; i += C::THREADS) {
@@ -394,22 +370,15 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
   // tiles [0, n_full) hold only keys that every row of the block may see
   const int n_full = min(n_tiles, (CAUSAL ? max(0, min(q_first + koff + 1, Nk)) : Nk) / C::BC);
 
-  // Stage 0 into LDS: K by direct copies; V by direct copies (V_DMA) or
-  // transposed through registers (thread tid stages V tile tid / VSTAGERS of
-  // each stage).
+  // Stage 0 into LDS: K and V by direct copies.
   TileDma<D, C::STAGE, C::THREADS> kdma;
   TileDma<D, C::STAGE, C::THREADS, typename C::VL> vdma;
-  TrStage<D, C::BC> vstage;
-  const int vsub = C::V_DMA ? C::SUB : tid / C::VSTAGERS;
   kdma.init(tid, K.sr);
-  if constexpr (C::V_DMA) vdma.init(tid, V.sr);
-  else vstage.init(vsub < C::SUB ? tid % C::VSTAGERS : C::VSTAGERS, V.sr);
-  const bool v0 = vsub < C::SUB && vsub < n_tiles;
+  vdma.init(tid, V.sr);
   if (n_tiles > 0) {
     kdma.issue(k_lds[0], Kh, 0, Nk);
-    if constexpr (C::V_DMA) vdma.issue(v_lds[0], Vh, 0, Nk);
+    vdma.issue(v_lds[0], Vh, 0, Nk);
   }
-  if (v0) vstage.load(Vh, vsub * C::BC, Nk);
   // Q fragments stay in registers for the whole pass (B operand of S^T = K Q^T).
 #pragma unroll
   for (int s = 0; s < C::DK; ++s) {
@@ -417,16 +386,13 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
     if (w.q_lane < Nq) z = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
     w.qf[s] = z;
   }
-  if (v0) vstage.store(v_lds[0] + vsub * C::VSUB);
 
   // Stage J uses buffer J % 2; unrolled by two so the buffer is an immediate.
   const int n_stages = (n_tiles + C::SUB - 1) / C::SUB;
   for (int J = 0; J < n_stages; J += 2) {
-    fwd_stage<D, CAUSAL, E, 0>(w, vstage, kdma, vdma, k_lds, v_lds, Kh, Vh, J, vsub, n_tiles, n_full, Nk,
-                               scale_log2);
+    fwd_stage<D, CAUSAL, E, 0>(w, kdma, vdma, k_lds, v_lds, Kh, Vh, J, n_tiles, n_full, Nk, scale_log2);
     if (J + 1 < n_stages)
-      fwd_stage<D, CAUSAL, E, 1>(w, vstage, kdma, vdma, k_lds, v_lds, Kh, Vh, J + 1, vsub, n_tiles, n_full, Nk,
-                                 scale_log2);
+      fwd_stage<D, CAUSAL, E, 1>(w, kdma, vdma, k_lds, v_lds, Kh, Vh, J + 1, n_tiles, n_full, Nk, scale_log2);
   }
 
   // Epilogue: one division by the row sum of the rounded P, then O (bf16) and

@@ -75,34 +75,6 @@ struct RowTile {
 };
 
 // ---------------------------------------------------------------------------
-// Transposed tiles in LDS.
-//
-// Operands whose reduction index is the token (V^T, K^T, Q^T, dO^T) need 8
-// consecutive tokens per lane, i.e. a column of the row-major tile.  These
-// tiles are transposed once, while being staged: each thread loads a
-// 4-token x 8-feature block into registers, permutes it with v_perm into 8
-// feature rows of 4 tokens and writes those (8 bytes each).  Feature rows hold
-// TOK tokens (+ 8 elements of padding: rows 144 bytes apart for TOK = 64, so
-// 16 consecutive rows cover all 64 banks).  Inside each group of 16 tokens the
-// middle two groups of four are swapped: an MFMA accumulator holds, in lane
-// half h, the tokens {4h..4h+3, 8+4h..8+4h+3}, which then lie side by side, so
-// the operand is one 16-byte read and P or dS feeds the other operand
-// directly.  Feature rows at or past D (the 80 -> 96 padding) stay zero.
-// ---------------------------------------------------------------------------
-template <int D, int TOK = 64>
-struct TrTile {
-  static_assert(TOK == 32 || TOK == 64, "tokens per transposed tile");
-  static constexpr int DP = (D + 31) / 32 * 32;
-  static constexpr int ROW = TOK + 8;                // bf16 per feature row
-  static constexpr int ELEMS = DP * ROW;
-  static FA2_HD int pos(int tok) {   // swap groups 1 and 2 of each 16
-    const int g = (tok >> 2) & 3;
-    return (tok & ~15) | ((g == 1 ? 2 : g == 2 ? 1 : g) << 2) | (tok & 3);
-  }
-  static FA2_HD int elem(int row, int tok) { return row * ROW + pos(tok); }
-};
-
-// ---------------------------------------------------------------------------
 // Row-major tiles read transposed.
 //
 // ds_read_b64_tr_b16 (gfx950) reads 8 bytes per lane and transposes them
@@ -264,60 +236,23 @@ struct DmaPlan {
   }
 };
 
-// ---------------------------------------------------------------------------
-// Register staging of a tile of TOK tokens by the first G*CH threads
-// (G = TOK/4 token groups x CH = D/8 feature chunks): thread i handles tokens
-// 4(i%G)..+3 and features 8(i/G)..+7, reading rows R elements apart.
-// ---------------------------------------------------------------------------
-template <int D, int TOK = 64>
-struct StagePlan {
-  static constexpr int CH = D / 8;
-  static constexpr int G = TOK / 4;
-  static constexpr int THREADS_USED = G * CH;
-  static FA2_HD bool active(int tid) { return tid < THREADS_USED; }
-  static FA2_HD int grp(int tid) { return tid % G; }
-  static FA2_HD int chunk(int tid) { return tid / G; }
-  // byte offset of (token 4g, feature 8ch) from the tile's first row
-  static FA2_HD uint32_t lane_offset(int tid, int R) {
-    return (uint32_t)(4 * grp(tid) * R + 8 * chunk(tid)) * 2u;
-  }
-  // Last token k (0..3) of group g that lies before row n_rows, for a tile
-  // starting at row tok0 < n_rows; 3 for every group of a full tile,
-  // negative for a group entirely past the end.
-  static FA2_HD int last_k(int g, int tok0, int n_rows) {
-    const int m = n_rows - 1 - tok0 - 4 * g;
-    return m < 3 ? m : 3;
-  }
-  // Byte offset, from the tile's first row, of the k-th token of the lane's
-  // group, clamped to the last row (lastk = last_k(...)); never negative.
-  static FA2_HD int64_t source_k(uint32_t off, int k, int lastk, int R) {
-    return (int64_t)off + (int64_t)(k < lastk ? k : lastk) * 2 * R;
-  }
-  static FA2_HD int64_t source(uint32_t off, int g, int k, int tok0, int n_rows, int R) {
-    return source_k(off, k, last_k(g, tok0, n_rows), R);
-  }
-};
-
-// Per-lane LDS element offsets of the two operand reads, computed once per
-// kernel for the lane's row (or feature row) in the first 32-row block; the
-// reads of other blocks and chunks (L::perm, L::block, TR32) differ by
-// compile-time constants: every read in the hot loops is one precomputed
-// register plus an immediate offset.
-template <int D, int TOK = 64, class L = RowTile<D>>
+// Per-lane LDS element offsets of the row-major operand reads, computed once
+// per kernel for the lane's row in the first 32-row block; the reads of other
+// blocks and feature steps (L::perm, L::block) differ by compile-time
+// constants: every such read in the hot loops is one precomputed register
+// plus an immediate offset.
+template <int D, class L = RowTile<D>>
 struct LaneOffsets {
   static constexpr int DK = D / 16;
   static constexpr int NDB = (D + 31) / 32;
-  static constexpr int TR32 = 32 * TrTile<D, TOK>::ROW;     // elements per 32 feature rows
   // feature steps of the layout's rows (more than DK when D features are
   // stored in wider rows: L::perm may then name a step past DK)
   static constexpr int NROW = L::CH / 2;
   int row[NROW];   // row-major tile: features 16 s + 8 h .. +7 of row lane % 32
-  int tr;        // transposed tile: tokens {4h..4h+3, 8+4h..8+4h+3} of feature row lane % 32
   FA2_HD void init(int lane) {
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int s = 0; s < NROW; ++s) row[s] = L::elem(lr, s * 16 + 8 * lh);
-    tr = lr * TrTile<D, TOK>::ROW + 8 * lh;   // + 16 c (token chunk) + TR32 mb (feature block)
   }
   // row-major read of 32-row block b, feature step s
   FA2_HD int rd(int s, int b) const { return row[L::perm(s, b)] + L::block(b); }

@@ -1,14 +1,14 @@
 // Host check of the kernels' index arithmetic (fa2_layout.h), compiled with
 // the system C++ compiler: for every lane, pass, tile and sequence length of
-// small cases, every global address a tile copy or register stage computes
-// must lie inside its tensor and fetch the chunk the LDS layout assigns to
-// the slot it lands in; every slot of a tile must be written exactly once;
-// every MFMA operand read must stay inside its LDS tile.  16-byte LDS
-// accesses are also checked for bank conflicts, taking 16 lanes per cycle
-// (64 banks of 4 bytes: 16 groups of 4 banks): every group of 16 lanes of a
-// register-stage row store or an operand read must reach 16 distinct groups.
-// Transposed operand reads (ds_read_b64_tr_b16) of TrRowTile tiles are
-// simulated lane by lane and checked for content and banks (check_tr_reads).
+// small cases, every read a tile copy makes in range must lie inside its
+// tensor and fetch the chunk the LDS layout assigns to the slot it lands in,
+// and every slot that must hold zeros must be read out of range (check_dma);
+// every slot of a tile must be written exactly once; every MFMA operand read
+// must stay inside its LDS tile.  16-byte LDS reads are also checked for bank
+// conflicts, taking 16 lanes per cycle (64 banks of 4 bytes: 16 groups of 4
+// banks): every group of 16 lanes of an operand read must reach 16 distinct
+// groups.  Transposed operand reads (ds_read_b64_tr_b16) are simulated lane
+// by lane and checked for content and banks (check_tr_reads).
 // Prints "ok" and exits 0, or prints the first violation and exits 1.
 #include <cstdio>
 #include <cstdint>
@@ -104,63 +104,13 @@ void check_dma(int max_n, int R) {
   }
 }
 
-// Register stage of a V tile (the forward at D = 128 and 256): every global
-// address inside the tensor and fetching the (token, chunk) its thread owns,
-// every (token, chunk) of the tile fetched once, every transposed-tile element
-// written once.
-template <int D, int TOK, int THREADS>
-void check_stage(int max_n, int R) {
-  using P = StagePlan<D, TOK>;
-  using T = TrTile<D, TOK>;
-  static_assert(P::THREADS_USED <= THREADS, "stage needs more threads than the workgroup has");
-  const long row_bytes = 2L * R;
-  for (int n = 1; n <= max_n; ++n) {
-    for (int tok0 = 0; tok0 < n; tok0 += TOK) {
-      std::vector<int> cover(TOK * P::CH, 0);
-      std::vector<int> tr_written(T::ELEMS, 0);
-      for (int tid = 0; tid < THREADS; ++tid) {
-        if (!P::active(tid)) continue;
-        const uint32_t off = P::lane_offset(tid, R);
-        const int g = tid % P::G, ch = tid / P::G;
-        CHECK(P::grp(tid) == g && P::chunk(tid) == ch, "D=%d tid=%d grp/chunk", D, tid);
-        for (int k = 0; k < 4; ++k) {
-          const long addr = (long)tok0 * row_bytes + P::source(off, g, k, tok0, n, R);
-          const long end = (n - 1) * row_bytes + 2L * D;
-          CHECK(addr >= 0 && addr + 16 <= end && addr % 16 == 0 && addr % row_bytes + 16 <= 2L * D,
-                "D=%d R=%d n=%d tok0=%d tid=%d k=%d addr=%ld", D, R, n, tok0, tid, k, addr);
-          int want = tok0 + 4 * g + k;
-          if (want > n - 1) want = n - 1;
-          CHECK(addr / row_bytes == want && (addr % row_bytes) / 16 == ch, "D=%d n=%d tid=%d k=%d row %ld want %d",
-                D, n, tid, k, addr / row_bytes, want);
-          cover[(4 * g + k) * P::CH + ch]++;
-        }
-        // store: feature rows 8ch + e, tokens 4g..4g+3 (8 bytes each)
-        for (int e = 0; e < 8; ++e) {
-          const int te = T::elem(8 * ch + e, 4 * g);
-          CHECK(te >= 0 && te + 4 <= T::ELEMS, "D=%d transposed store out of tile", D);
-          for (int j = 0; j < 4 && te >= 0 && te + 4 <= T::ELEMS; ++j) {
-            CHECK(T::elem(8 * ch + e, 4 * g + j) == te + j, "D=%d token group not contiguous", D);
-            tr_written[te + j]++;
-          }
-        }
-      }
-      for (int i = 0; i < TOK * P::CH; ++i) CHECK(cover[i] == 1, "D=%d (token, chunk) %d covered %d times", D, i, cover[i]);
-      for (int f = 0; f < D; ++f)
-        for (int tok = 0; tok < TOK; ++tok)
-          CHECK(tr_written[T::elem(f, tok)] == 1, "D=%d transposed (%d, %d) written %d times", D, f, tok,
-                tr_written[T::elem(f, tok)]);
-    }
-  }
-}
-
 // Operand reads: row-major tiles of TOK rows are read at row[s] + 2*b*ROW16
-// (b = 32-row block, s = 16-feature chunk), 8 elements; transposed tiles at
-// tr + 16c + mb*TR32 (c = 16-token chunk, mb = 32-feature block), 8 elements.  Each read must stay inside its tile and fetch the
-// features / tokens the MFMA lane layout expects.
+// (b = 32-row block, s = 16-feature chunk), 8 elements.  Each read must stay
+// inside its tile and fetch the features the MFMA lane layout expects, and
+// each 16 lanes must reach 16 distinct bank groups.
 template <int D, int TOK = 64, class L = RowTile<D>>
 void check_reads() {
-  using O = LaneOffsets<D, TOK, L>;
-  using T = TrTile<D, TOK>;
+  using O = LaneOffsets<D, L>;
   O lanes[64];
   for (int lane = 0; lane < 64; ++lane) lanes[lane].init(lane);
   // row-major reads: bank groups of each 16 lanes
@@ -181,16 +131,6 @@ void check_reads() {
         const int e = o.rd(s, b);
         CHECK(e >= 0 && e + 8 <= L::elems(TOK), "D=%d row read out of tile", D);
         CHECK(e == L::elem(32 * b + lr, 16 * s + 8 * lh), "D=%d row read of lane %d b=%d s=%d", D, lane, b, s);
-      }
-    for (int c = 0; c < TOK / 16; ++c)
-      for (int mb = 0; mb < O::NDB; ++mb) {
-        const int e = o.tr + 16 * c + mb * O::TR32;
-        CHECK(e >= 0 && e + 8 <= T::ELEMS, "D=%d transposed read out of tile", D);
-        // 8 consecutive elements: tokens 16c + {4lh..4lh+3, 8+4lh..8+4lh+3} of feature 32mb + lr
-        for (int j = 0; j < 8; ++j) {
-          const int tok = 16 * c + (j < 4 ? 4 * lh + j : 8 + 4 * lh + j - 4);
-          CHECK(T::elem(32 * mb + lr, tok) == e + j, "D=%d tr read lane %d c=%d mb=%d j=%d", D, lane, c, mb, j);
-        }
       }
   }
 }
@@ -280,13 +220,6 @@ int main() {
     check_dma<256, 32, 256>(max_n, 256 * mult);
   }
   check_dma<256, 32, 256>(max_n, 264);
-  // V tiles the forward stages through registers (D = 128, 256)
-  for (int mult : {1, 2, 3}) {
-    check_stage<128, 64, 512>(max_n, 128 * mult);
-    check_stage<256, 32, 256>(max_n, 256 * mult);
-  }
-  check_stage<128, 64, 512>(max_n, 136);
-  check_stage<256, 32, 256>(max_n, 264);
   // V tiles of the forward (TrRowTile): the thread counts of its workgroups
   for (int mult : {1, 2, 3}) {
     check_dma<64, 64, 512, TrRowTile<64>>(max_n, 64 * mult);
@@ -294,6 +227,7 @@ int main() {
     check_dma<80, 64, 256, TrRowTile<80>>(max_n, 80 * mult);
     check_dma<96, 64, 768, TrRowTile<96>>(max_n, 96 * mult);
     check_dma<128, 64, 512, TrRowTile<128>>(max_n, 128 * mult);
+    check_dma<256, 32, 256, TrRowTile<256>>(max_n, 256 * mult);
   }
   check_dma<256, 32, 256, TrRowTile<256>>(max_n, 264);
   check_dma<80, 64, 256, TrRowTile<80>>(max_n, 88);
