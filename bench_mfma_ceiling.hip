@@ -59,13 +59,37 @@ __global__ __launch_bounds__(256) void mfma_loop(const bf16x8* __restrict__ a, c
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// One operand per MFMA from memory.  SRC 0: LDS read per MFMA; 1: LDS read per
-// two MFMAs; 2: global load per MFMA (a 64 KiB window per workgroup, L1-resident
-// after the first pass); 3: two transposing 8-byte LDS reads per MFMA
-// (ds_read_b64_tr_b16, consecutive lanes 8 bytes apart).  Every address is
-// masked into its buffer.
-template <int SRC>
-__global__ void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out, int iters) {
+// One operand per MFMA from memory.  SRC 0: one 16-byte LDS read per MFMA;
+// 1: one 16-byte LDS read per two MFMAs; 2: a 16-byte global load per MFMA (a
+// 64 KiB window per workgroup, L1-resident after the first pass); 3: two
+// transposing 8-byte LDS reads per MFMA (ds_read_b64_tr_b16, consecutive
+// lanes 8 bytes apart).  Every address is masked into its buffer.
+//
+// PF = 0: the compiler schedules the reads (it issues a loop iteration's
+// reads ahead of its MFMAs, so each iteration starts by waiting for a read).
+// PF > 0: software-pipelined as the attention kernels do it: the operand of
+// MFMA k is read right after MFMA k - PF is issued, into a ring of PF
+// registers, across loop iterations, and a scheduling barrier after every
+// MFMA keeps that order.
+template <int SRC, int PF>
+__device__ __forceinline__ bf16x8 fed_read(const char* lbase, const char* gbase, int lane, int wave, int k) {
+  const int u = k & 15, it = k >> 4;
+  if constexpr (SRC == 3) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint32_t o0 = (uint32_t)(lane * 8 + u * 1024 + wave * 4096 + it * 256) & 0xFFF8u;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lbase + o0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lbase + (o0 ^ 512u)));
+    const s16x4 both[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, both);
+  } else {
+    const uint32_t off = (uint32_t)(lane * 16 + u * 1024 + wave * 4096 + it * 256) & 0xFFF0u;
+    return SRC == 2 ? *reinterpret_cast<const bf16x8*>(gbase + off) : *reinterpret_cast<const bf16x8*>(lbase + off);
+  }
+}
+
+template <int SRC, int PF>
+__global__ __launch_bounds__(1024) void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out, int iters) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[32768];   // 64 KiB
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < 32768; i += blockDim.x) lds[i] = g[i];
@@ -78,25 +102,33 @@ __global__ void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out
     for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
   const char* lbase = reinterpret_cast<const char*>(lds);
   const char* gbase = reinterpret_cast<const char*>(g) + (size_t)(blockIdx.x % 64) * 65536;
-  for (int it = 0; it < iters; ++it) {
+  constexpr int STEP = SRC == 1 ? 2 : 1;   // MFMAs per read
+  if constexpr (PF == 0) {
+    for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int u = 0; u < 16; u += (SRC == 1 ? 2 : 1)) {
-      const uint32_t off = (uint32_t)(lane * 16 + u * 1024 + wave * 4096 + it * 256) & 0xFFF0u;
-      bf16x8 a;
-      if constexpr (SRC == 3) {
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const uint32_t o0 = (uint32_t)(lane * 8 + u * 1024 + wave * 4096 + it * 256) & 0xFFF8u;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lbase + o0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lbase + (o0 ^ 512u)));
-        const s16x4 both[2] = {lo, hi};
-        a = __builtin_bit_cast(bf16x8, both);
-      } else {
-        a = SRC == 2 ? *reinterpret_cast<const bf16x8*>(gbase + off) : *reinterpret_cast<const bf16x8*>(lbase + off);
+      for (int u = 0; u < 16; u += STEP) {
+        const bf16x8 a = fed_read<SRC, PF>(lbase, gbase, lane, wave, it * 16 + u);
+        acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u & 3], 0, 0, 0);
+        if (SRC == 1) acc[(u + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[(u + 1) & 3], 0, 0, 0);
       }
-      acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u & 3], 0, 0, 0);
-      if (SRC == 1) acc[(u + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[(u + 1) & 3], 0, 0, 0);
     }
+  } else {
+    bf16x8 ring[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) ring[p] = fed_read<SRC, PF>(lbase, gbase, lane, wave, p * STEP);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 16; u += STEP) {
+        const int slot = (u / STEP) % PF;
+        acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[slot], b, acc[u & 3], 0, 0, 0);
+        if (SRC == 1)
+          acc[(u + 1) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, ring[slot], acc[(u + 1) & 3], 0, 0, 0);
+        ring[slot] = fed_read<SRC, PF>(lbase, gbase, lane, wave, it * 16 + u + PF * STEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) acc[0][p] += (float)ring[p][0];
   }
   float s = 0.f;
 #pragma unroll
@@ -105,6 +137,27 @@ __global__ void mfma_fed(const uint16_t* __restrict__ g, float* __restrict__ out
 }
 
 // rates of mfma_fed: 256 workgroups (one per CU) of 4, 8 or 16 wavefronts
+template <int SRC, int PF>
+int run_fed_one(const char* name, const uint16_t* g, float* out, hipEvent_t e0, hipEvent_t e1) {
+  const int iters = 2048;
+  for (int waves : {4, 8, 16}) {
+    float ms = 0.f;
+    for (int rep = 0; rep < 3; ++rep) {   // the last of three runs is reported
+      CHECK(hipEventRecord(e0));
+      mfma_fed<SRC, PF><<<256, 64 * waves>>>(g, out, iters);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+    }
+    const double flops = 256.0 * waves * iters * 16 * (2.0 * 32 * 32 * 16);
+    std::printf("{\"operand_source\": \"%s\", \"reads_ahead\": %d, \"wavefronts_per_simd\": %d, \"ms\": %.3f, "
+                "\"tflops\": %.1f}\n",
+                name, PF, waves / 4, ms, flops / (ms * 1e-3) / 1e12);
+    std::fflush(stdout);
+  }
+  return 0;
+}
+
 int run_fed() {
   const size_t n = (size_t)64 * 65536 / 2;   // bf16 elements: 64 windows of 64 KiB
   std::vector<uint16_t> h(n);
@@ -124,26 +177,16 @@ int run_fed() {
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
-  const int iters = 2048;
-  const char* names[4] = {"LDS read per MFMA", "LDS read per 2 MFMAs", "L1 global load per MFMA",
-                          "two transposing 8-byte LDS reads per MFMA"};
-  for (int src = 0; src < 4; ++src)
-    for (int waves : {4, 8, 16}) {
-      float ms = 0.f;
-      for (int rep = 0; rep < 3; ++rep) {   // the last of three runs is reported
-        CHECK(hipEventRecord(e0));
-        if (src == 0) mfma_fed<0><<<256, 64 * waves>>>(g, out, iters);
-        else if (src == 1) mfma_fed<1><<<256, 64 * waves>>>(g, out, iters);
-        else if (src == 2) mfma_fed<2><<<256, 64 * waves>>>(g, out, iters);
-        else mfma_fed<3><<<256, 64 * waves>>>(g, out, iters);
-        CHECK(hipEventRecord(e1));
-        CHECK(hipEventSynchronize(e1));
-        CHECK(hipEventElapsedTime(&ms, e0, e1));
-      }
-      const double flops = 256.0 * waves * iters * 16 * (2.0 * 32 * 32 * 16);
-      std::printf("{\"operand_source\": \"%s\", \"wavefronts_per_simd\": %d, \"ms\": %.3f, \"tflops\": %.1f}\n",
-                  names[src], waves / 4, ms, flops / (ms * 1e-3) / 1e12);
-    }
+  const char* lds1 = "LDS read per MFMA";
+  const char* lds2 = "LDS read per 2 MFMAs";
+  const char* l1 = "L1 global load per MFMA";
+  const char* tr = "two transposing 8-byte LDS reads per MFMA";
+  if (run_fed_one<0, 0>(lds1, g, out, e0, e1) || run_fed_one<1, 0>(lds2, g, out, e0, e1) ||
+      run_fed_one<2, 0>(l1, g, out, e0, e1) || run_fed_one<3, 0>(tr, g, out, e0, e1) ||
+      run_fed_one<0, 2>(lds1, g, out, e0, e1) || run_fed_one<0, 4>(lds1, g, out, e0, e1) ||
+      run_fed_one<1, 2>(lds2, g, out, e0, e1) || run_fed_one<3, 2>(tr, g, out, e0, e1) ||
+      run_fed_one<3, 4>(tr, g, out, e0, e1))
+    return 1;
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
   return 0;
