@@ -76,33 +76,31 @@ def parse():
 # (FETCH_SIZE, then WRITE_SIZE) divided by what the same counters read for a
 # plain copy of known size (bench.py --calibrate-copy).  Valid only for the
 # kernel sources it was measured on: keyed by their hash, else reported null.
-# Counted on sources of hash c46d5a72a1d82efe; the sources of the key below
-# (unused layout helpers removed) build a byte-identical libfa2.so.
 MEASURED_TRAFFIC = {
-    ("d7d455e4c52d8d87", "c1", "bwd_dkdv"): 125054,
-    ("d7d455e4c52d8d87", "c1", "bwd_dq"): 100734,
-    ("d7d455e4c52d8d87", "c1", "bwd_preprocess"): 93694,
-    ("d7d455e4c52d8d87", "c1", "fwd"): 93694,
-    ("d7d455e4c52d8d87", "c2", "bwd_dkdv"): 1359927653,
-    ("d7d455e4c52d8d87", "c2", "bwd_dq"): 740467052,
-    ("d7d455e4c52d8d87", "c2", "bwd_preprocess"): 137429921,
-    ("d7d455e4c52d8d87", "c2", "fwd"): 672351339,
-    ("d7d455e4c52d8d87", "c3", "bwd_dkdv"): 1421118916,
-    ("d7d455e4c52d8d87", "c3", "bwd_dq"): 809629933,
-    ("d7d455e4c52d8d87", "c3", "bwd_preprocess"): 140569697,
-    ("d7d455e4c52d8d87", "c3", "fwd"): 756944074,
-    ("d7d455e4c52d8d87", "c4", "bwd_dkdv"): 868129972,
-    ("d7d455e4c52d8d87", "c4", "bwd_dq"): 740209520,
-    ("d7d455e4c52d8d87", "c4", "bwd_preprocess"): 137430481,
-    ("d7d455e4c52d8d87", "c4", "fwd"): 596178615,
-    ("d7d455e4c52d8d87", "c5", "bwd_dkdv"): 1783468200,
-    ("d7d455e4c52d8d87", "c5", "bwd_dq"): 1013533745,
-    ("d7d455e4c52d8d87", "c5", "bwd_preprocess"): 174112610,
-    ("d7d455e4c52d8d87", "c5", "fwd"): 1647702822,
-    ("d7d455e4c52d8d87", "d256", "bwd_dkdv"): 868148340,
-    ("d7d455e4c52d8d87", "d256", "bwd_dq"): 713771087,
-    ("d7d455e4c52d8d87", "d256", "bwd_preprocess"): 135868649,
-    ("d7d455e4c52d8d87", "d256", "fwd"): 625023306,
+    ("5a7b5dc80ebe7a5d", "c1", "bwd_dkdv"): 121342,
+    ("5a7b5dc80ebe7a5d", "c1", "bwd_dq"): 99838,
+    ("5a7b5dc80ebe7a5d", "c1", "bwd_preprocess"): 93694,
+    ("5a7b5dc80ebe7a5d", "c1", "fwd"): 92158,
+    ("5a7b5dc80ebe7a5d", "c2", "bwd_dkdv"): 1359548947,
+    ("5a7b5dc80ebe7a5d", "c2", "bwd_dq"): 740458140,
+    ("5a7b5dc80ebe7a5d", "c2", "bwd_preprocess"): 137429531,
+    ("5a7b5dc80ebe7a5d", "c2", "fwd"): 672340950,
+    ("5a7b5dc80ebe7a5d", "c3", "bwd_dkdv"): 1421221406,
+    ("5a7b5dc80ebe7a5d", "c3", "bwd_dq"): 809625250,
+    ("5a7b5dc80ebe7a5d", "c3", "bwd_preprocess"): 140569899,
+    ("5a7b5dc80ebe7a5d", "c3", "fwd"): 762524916,
+    ("5a7b5dc80ebe7a5d", "c4", "bwd_dkdv"): 869118201,
+    ("5a7b5dc80ebe7a5d", "c4", "bwd_dq"): 699904694,
+    ("5a7b5dc80ebe7a5d", "c4", "bwd_preprocess"): 137429659,
+    ("5a7b5dc80ebe7a5d", "c4", "fwd"): 592299194,
+    ("5a7b5dc80ebe7a5d", "c5", "bwd_dkdv"): 1784715239,
+    ("5a7b5dc80ebe7a5d", "c5", "bwd_dq"): 1016433446,
+    ("5a7b5dc80ebe7a5d", "c5", "bwd_preprocess"): 174112926,
+    ("5a7b5dc80ebe7a5d", "c5", "fwd"): 1661722171,
+    ("5a7b5dc80ebe7a5d", "d256", "bwd_dkdv"): 880847538,
+    ("5a7b5dc80ebe7a5d", "d256", "bwd_dq"): 693496940,
+    ("5a7b5dc80ebe7a5d", "d256", "bwd_preprocess"): 135867987,
+    ("5a7b5dc80ebe7a5d", "d256", "fwd"): 616756900,
 }
 
 
