@@ -124,7 +124,7 @@ struct DkdvCfg {
 template <int D, bool CAUSAL, class E>
 struct DkdvWave {
   using C = DkdvCfg<D>;
-  u32x4 kf[C::DK], vf[C::DK];
+  u32x4 kf[C::DK], vf[C::DK];   // K and -V (B operands of S and of delta - dP)
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
   int lane, lr, lh, key_w, key_lane;
   LaneOffsets<D, typename C::TileL> off;
@@ -176,16 +176,13 @@ struct DkdvWave {
         rb[t] = lds_read_tr(qt + tro[0][mb] + c * R16, qt + tro[1][mb] + c * R16);
       }
     };
-#pragma unroll
-    for (int t = 0; t < PF; ++t) fetch(t);
-
     // Row statistics of group (qb, g): lane (lr, lh) needs queries
     // qb*32 + 8g + 4lh + r.  sm_stage(qb, g) is the stage whose end runs the
-    // group's softmax; its statistics are read LEAD stages earlier (from stage
-    // 0 on).  LDS reads complete in order, so a statistics read issued just
+    // group's softmax; its L log2 e is read LEAD stages earlier (from stage 0
+    // on).  LDS reads complete in order, so a statistics read issued just
     // before its use would make the softmax also wait for the operand reads
     // prefetched ahead of it.
-    f32x4 lv[C::NQB][4], dv[C::NQB][4];
+    f32x4 lv[C::NQB][4];
     auto sm_stage = [](int qb, int g) {
       return qb == 0 ? C::DK + 1 + g * (C::DK - 1) / 4 : NS + 1 + g * (2 * C::NDB - 1) / 4;
     };
@@ -193,17 +190,27 @@ struct DkdvWave {
     auto stats_stage = [&](int qb, int g) { return max(0, sm_stage(qb, g) - LEAD); };
     auto load_stats = [&](int qb, int g) {
       lv[qb][g] = *reinterpret_cast<const f32x4*>(l2s + qb * 32 + 8 * g + 4 * lh);
-      dv[qb][g] = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * g + 4 * lh);
     };
 
+    // The dP accumulators start from delta: with V negated (the caller's
+    // vf) the MFMAs leave delta - dP in them, so dS = -(P acc) takes one
+    // multiply.  Half 0's delta is read before the step's operand reads,
+    // half 1's LEAD stages before its first dP product.
     f32x16 sacc[C::NQB], pacc[C::NQB];
+    auto load_delta = [&](int qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d = *reinterpret_cast<const f32x4*>(dls + qb * 32 + 8 * g + 4 * lh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pacc[qb][4 * g + r] = d[r];
+      }
+    };
+    constexpr int DELTA1_STAGE = C::DK > LEAD ? C::DK - LEAD : 0;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        sacc[qb][t] = 0.f;
-        pacc[qb][t] = 0.f;
-      }
+      for (int t = 0; t < 16; ++t) sacc[qb][t] = 0.f;
+    load_delta(0);
     uint32_t pw[C::NQB][8], dsw[C::NQB][8];
     // P = 2^(c S - L log2 e) and dS = P (dP - delta) for 4 of a half's 16
     // registers (queries qb*32 + 8g + 4lh + r), packed to bf16.
@@ -215,7 +222,7 @@ struct DkdvWave {
         float x = exp2_fast(__builtin_fmaf(sacc[qb][t], scale_log2, -lv[qb][g][r]));
         if (MASK && (key_lane >= Nk || (CAUSAL && key_lane > kq0 + qb * 32 + 8 * g + 4 * lh + r))) x = 0.f;
         p[r] = x;
-        ds[r] = x * (pacc[qb][t] - dv[qb][g][r]);
+        ds[r] = -(x * pacc[qb][t]);
       }
       pw[qb][2 * g] = E::pack2(p[0], p[1]);
       pw[qb][2 * g + 1] = E::pack2(p[2], p[3]);
@@ -223,13 +230,18 @@ struct DkdvWave {
       dsw[qb][2 * g + 1] = E::pack2(ds[2], ds[3]);
     };
 
-    // S = Q K^T, dP = dO V^T; softmax of half 0 from stage DK + 1 on.
+#pragma unroll
+    for (int t = 0; t < PF; ++t) fetch(t);
+
+    // S = Q K^T, delta - dP = delta + dO (-V)^T; softmax of half 0 from stage
+    // DK + 1 on.
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       const int qb = t / C::DK, s = t % C::DK;
       sacc[qb] = E::mfma(ra[t], kf[s], sacc[qb]);
       pacc[qb] = E::mfma(rb[t], vf[s], pacc[qb]);
       if (t + PF < NALL) fetch(t + PF);
+      if (t == DELTA1_STAGE) load_delta(1);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (t == stats_stage(0, g)) load_stats(0, g);
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       zv = ld_global16(V.head(bh / H, bh % H) + (size_t)w.key_lane * V.sr + s * 16 + 8 * w.lh);
     }
     w.kf[s] = zk;
-    w.vf[s] = zv;
+    w.vf[s] = zv ^ 0x80008000u;   // -V: the dP products accumulate onto delta (DkdvWave::step)
     // K and V only ever feed MFMAs, which read operands from the accumulator
     // registers as well: keeping them there leaves the vector registers to
     // the S and dP products, which the softmax reads.
