@@ -729,13 +729,18 @@ struct DqCfg {
   static constexpr int TILE = TileL::elems(BC);
   // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint)
   static constexpr int READ_AHEAD = D == 256 ? 2 : 6;
+  // Where registers allow, the dP^T products start from delta (16 registers
+  // holding this lane's delta) with dO negated, leaving delta - dP^T: dS^T =
+  // -(P^T acc) then takes one multiply instead of a subtraction and one.
+  static constexpr bool DELTA_INIT = D <= 96;
 };
 
 template <int D, bool CAUSAL, class E>
 struct DqWave {
   using C = DqCfg<D>;
-  u32x4 qf[C::DK], dof[C::DK];
+  u32x4 qf[C::DK], dof[C::DK];   // Q and dO (DELTA_INIT: -dO)
   f32x16 dqacc[C::NDB];
+  f32x16 dl16;   // DELTA_INIT: dl in every register
   float l2, dl;
   int lane, lr, lh, q_wave, q_lane;
   int key_last;   // causal: last key this lane's query may see (q_lane + Nk - Nq)
@@ -763,7 +768,7 @@ struct DqWave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sacc[kb][i] = 0.f;
-        pacc[kb][i] = 0.f;
+        pacc[kb][i] = C::DELTA_INIT ? dl16[i] : 0.f;
       }
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
@@ -788,7 +793,7 @@ struct DqWave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = exp2_fast(__builtin_fmaf(sacc[kb][i], scale_log2, -l2));
-        pacc[kb][i] = p * (pacc[kb][i] - dl);
+        pacc[kb][i] = C::DELTA_INIT ? -(p * pacc[kb][i]) : p * (pacc[kb][i] - dl);
       }
 #pragma unroll
       for (int i = 0; i < 16; i += 2) dsw[kb][i >> 1] = E::pack2(pacc[kb][i], pacc[kb][i + 1]);
@@ -869,10 +874,12 @@ __global__ __launch_bounds__(DqCfg<D>::THREADS, 1) void bwd_dq_kernel(
       zd = ld_global16(dOh + (size_t)w.q_lane * dO.sr + s * 16 + 8 * w.lh);
     }
     w.qf[s] = zq;
-    w.dof[s] = zd;
+    w.dof[s] = C::DELTA_INIT ? zd ^ 0x80008000u : zd;
   }
   w.l2 = L2[(size_t)bh * Npad + w.q_lane];
   w.dl = Delta[(size_t)bh * Npad + w.q_lane];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w.dl16[i] = w.dl;
 #pragma unroll
   for (int mb = 0; mb < C::NDB; ++mb)
 #pragma unroll
