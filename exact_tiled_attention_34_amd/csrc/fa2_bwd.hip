@@ -731,8 +731,9 @@ struct DqCfg {
   static constexpr int READ_AHEAD = D == 256 ? 2 : 6;
   // Where registers allow, the dP^T products start from delta (16 registers
   // holding this lane's delta) with dO negated, leaving delta - dP^T: dS^T =
-  // -(P^T acc) then takes one multiply instead of a subtraction and one.
-  static constexpr bool DELTA_INIT = D <= 96;
+  // -(P^T acc) then takes one multiply instead of a subtraction and one.  The
+  // D = 128 kernel has no 16 registers to spare (252 of 256).
+  static constexpr bool DELTA_INIT = D != 128;
 };
 
 template <int D, bool CAUSAL, class E>
