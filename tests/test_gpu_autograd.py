@@ -144,6 +144,29 @@ def test_strided_views_match_oracle(B, H, Nq, Nk, d, causal):
         assert rel(f64(t), r) <= G_TOL
 
 
+@pytest.mark.parametrize("d,causal", [(128, True), (80, False)])
+def test_largest_row_pitch(d, causal):
+    """Rows 2^20 elements apart (the largest pitch the API accepts), a ragged 70-row sequence: the
+    tile copies' byte ranges are largest here.  Results equal the contiguous call's bit for bit."""
+    B, H, N = 1, 2, 70
+    pitch = 1 << 20
+    arrs = gen.make_arrays(B, H, N, d, seed=7100 + d)
+    q, k, v, do = (to_dev(arrs[n]) for n in ("q", "k", "v", "do"))
+    wide = [padded_rows(t, pitch - d) for t in (q, k, v, do)]
+    assert all(t.stride(2) == pitch for t in wide)
+    o, lse = fa2.fwd(*wide[:3], causal=causal)
+    dq, dk, dv = fa2.bwd(*wide[:3], o, lse, wide[3], causal=causal)
+    torch.cuda.synchronize()
+    o_c, lse_c = fa2.fwd(q, k, v, causal=causal)
+    g_c = fa2.bwd(q, k, v, o_c, lse_c, do, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_c) and torch.equal(lse, lse_c)
+    for a, b in zip((dq, dk, dv), g_c):
+        assert torch.equal(a, b)
+    with pytest.raises(Exception):
+        fa2.fwd(padded_rows(q, pitch + 8 - d), k, v, causal=causal)
+
+
 @pytest.mark.parametrize("B,S,H,d,causal,dtype", [(2, 150, 2, 80, True, "bf16"), (1, 257, 3, 128, False, "bf16"),
                                                    (2, 64, 4, 64, True, "bf16"), (2, 150, 2, 80, True, "fp16"),
                                                    (1, 130, 2, 256, True, "bf16")])
