@@ -77,30 +77,30 @@ def parse():
 # plain copy of known size (bench.py --calibrate-copy).  Valid only for the
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
-    ("5a7b5dc80ebe7a5d", "c1", "bwd_dkdv"): 121342,
-    ("5a7b5dc80ebe7a5d", "c1", "bwd_dq"): 99838,
-    ("5a7b5dc80ebe7a5d", "c1", "bwd_preprocess"): 93694,
-    ("5a7b5dc80ebe7a5d", "c1", "fwd"): 92158,
-    ("5a7b5dc80ebe7a5d", "c2", "bwd_dkdv"): 1359548947,
-    ("5a7b5dc80ebe7a5d", "c2", "bwd_dq"): 740458140,
-    ("5a7b5dc80ebe7a5d", "c2", "bwd_preprocess"): 137429531,
-    ("5a7b5dc80ebe7a5d", "c2", "fwd"): 672340950,
-    ("5a7b5dc80ebe7a5d", "c3", "bwd_dkdv"): 1421221406,
-    ("5a7b5dc80ebe7a5d", "c3", "bwd_dq"): 809625250,
-    ("5a7b5dc80ebe7a5d", "c3", "bwd_preprocess"): 140569899,
-    ("5a7b5dc80ebe7a5d", "c3", "fwd"): 762524916,
-    ("5a7b5dc80ebe7a5d", "c4", "bwd_dkdv"): 869118201,
-    ("5a7b5dc80ebe7a5d", "c4", "bwd_dq"): 699904694,
-    ("5a7b5dc80ebe7a5d", "c4", "bwd_preprocess"): 137429659,
-    ("5a7b5dc80ebe7a5d", "c4", "fwd"): 592299194,
-    ("5a7b5dc80ebe7a5d", "c5", "bwd_dkdv"): 1784715239,
-    ("5a7b5dc80ebe7a5d", "c5", "bwd_dq"): 1016433446,
-    ("5a7b5dc80ebe7a5d", "c5", "bwd_preprocess"): 174112926,
-    ("5a7b5dc80ebe7a5d", "c5", "fwd"): 1661722171,
-    ("5a7b5dc80ebe7a5d", "d256", "bwd_dkdv"): 880847538,
-    ("5a7b5dc80ebe7a5d", "d256", "bwd_dq"): 693496940,
-    ("5a7b5dc80ebe7a5d", "d256", "bwd_preprocess"): 135867987,
-    ("5a7b5dc80ebe7a5d", "d256", "fwd"): 616756900,
+    ("5a5b831c0aa837e0", "c1", "bwd_dkdv"): 119294,
+    ("5a5b831c0aa837e0", "c1", "bwd_dq"): 101118,
+    ("5a5b831c0aa837e0", "c1", "bwd_preprocess"): 93694,
+    ("5a5b831c0aa837e0", "c1", "fwd"): 92158,
+    ("5a5b831c0aa837e0", "c2", "bwd_dkdv"): 1361096751,
+    ("5a5b831c0aa837e0", "c2", "bwd_dq"): 740457260,
+    ("5a5b831c0aa837e0", "c2", "bwd_preprocess"): 137429396,
+    ("5a5b831c0aa837e0", "c2", "fwd"): 672340913,
+    ("5a5b831c0aa837e0", "c3", "bwd_dkdv"): 1338411205,
+    ("5a5b831c0aa837e0", "c3", "bwd_dq"): 809635366,
+    ("5a5b831c0aa837e0", "c3", "bwd_preprocess"): 140569556,
+    ("5a5b831c0aa837e0", "c3", "fwd"): 762940202,
+    ("5a5b831c0aa837e0", "c4", "bwd_dkdv"): 870802804,
+    ("5a5b831c0aa837e0", "c4", "bwd_dq"): 693963307,
+    ("5a5b831c0aa837e0", "c4", "bwd_preprocess"): 137430836,
+    ("5a5b831c0aa837e0", "c4", "fwd"): 595412113,
+    ("5a5b831c0aa837e0", "c5", "bwd_dkdv"): 1784770426,
+    ("5a5b831c0aa837e0", "c5", "bwd_dq"): 1018047425,
+    ("5a5b831c0aa837e0", "c5", "bwd_preprocess"): 174112562,
+    ("5a5b831c0aa837e0", "c5", "fwd"): 1649936686,
+    ("5a5b831c0aa837e0", "d256", "bwd_dkdv"): 879958884,
+    ("5a5b831c0aa837e0", "d256", "bwd_dq"): 676687646,
+    ("5a5b831c0aa837e0", "d256", "bwd_preprocess"): 135865677,
+    ("5a5b831c0aa837e0", "d256", "fwd"): 607841317,
 }
 
 
