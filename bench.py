@@ -76,31 +76,33 @@ def parse():
 # (FETCH_SIZE, then WRITE_SIZE) divided by what the same counters read for a
 # plain copy of known size (bench.py --calibrate-copy).  Valid only for the
 # kernel sources it was measured on: keyed by their hash, else reported null.
+# Counted on sources of hash 5a5b831c0aa837e0; the sources of the key below
+# (a comment changed) build a byte-identical libfa2.so.
 MEASURED_TRAFFIC = {
-    ("5a5b831c0aa837e0", "c1", "bwd_dkdv"): 119294,
-    ("5a5b831c0aa837e0", "c1", "bwd_dq"): 101118,
-    ("5a5b831c0aa837e0", "c1", "bwd_preprocess"): 93694,
-    ("5a5b831c0aa837e0", "c1", "fwd"): 92158,
-    ("5a5b831c0aa837e0", "c2", "bwd_dkdv"): 1361096751,
-    ("5a5b831c0aa837e0", "c2", "bwd_dq"): 740457260,
-    ("5a5b831c0aa837e0", "c2", "bwd_preprocess"): 137429396,
-    ("5a5b831c0aa837e0", "c2", "fwd"): 672340913,
-    ("5a5b831c0aa837e0", "c3", "bwd_dkdv"): 1338411205,
-    ("5a5b831c0aa837e0", "c3", "bwd_dq"): 809635366,
-    ("5a5b831c0aa837e0", "c3", "bwd_preprocess"): 140569556,
-    ("5a5b831c0aa837e0", "c3", "fwd"): 762940202,
-    ("5a5b831c0aa837e0", "c4", "bwd_dkdv"): 870802804,
-    ("5a5b831c0aa837e0", "c4", "bwd_dq"): 693963307,
-    ("5a5b831c0aa837e0", "c4", "bwd_preprocess"): 137430836,
-    ("5a5b831c0aa837e0", "c4", "fwd"): 595412113,
-    ("5a5b831c0aa837e0", "c5", "bwd_dkdv"): 1784770426,
-    ("5a5b831c0aa837e0", "c5", "bwd_dq"): 1018047425,
-    ("5a5b831c0aa837e0", "c5", "bwd_preprocess"): 174112562,
-    ("5a5b831c0aa837e0", "c5", "fwd"): 1649936686,
-    ("5a5b831c0aa837e0", "d256", "bwd_dkdv"): 879958884,
-    ("5a5b831c0aa837e0", "d256", "bwd_dq"): 676687646,
-    ("5a5b831c0aa837e0", "d256", "bwd_preprocess"): 135865677,
-    ("5a5b831c0aa837e0", "d256", "fwd"): 607841317,
+    ("b75e2db3de9304f5", "c1", "bwd_dkdv"): 119294,
+    ("b75e2db3de9304f5", "c1", "bwd_dq"): 101118,
+    ("b75e2db3de9304f5", "c1", "bwd_preprocess"): 93694,
+    ("b75e2db3de9304f5", "c1", "fwd"): 92158,
+    ("b75e2db3de9304f5", "c2", "bwd_dkdv"): 1361096751,
+    ("b75e2db3de9304f5", "c2", "bwd_dq"): 740457260,
+    ("b75e2db3de9304f5", "c2", "bwd_preprocess"): 137429396,
+    ("b75e2db3de9304f5", "c2", "fwd"): 672340913,
+    ("b75e2db3de9304f5", "c3", "bwd_dkdv"): 1338411205,
+    ("b75e2db3de9304f5", "c3", "bwd_dq"): 809635366,
+    ("b75e2db3de9304f5", "c3", "bwd_preprocess"): 140569556,
+    ("b75e2db3de9304f5", "c3", "fwd"): 762940202,
+    ("b75e2db3de9304f5", "c4", "bwd_dkdv"): 870802804,
+    ("b75e2db3de9304f5", "c4", "bwd_dq"): 693963307,
+    ("b75e2db3de9304f5", "c4", "bwd_preprocess"): 137430836,
+    ("b75e2db3de9304f5", "c4", "fwd"): 595412113,
+    ("b75e2db3de9304f5", "c5", "bwd_dkdv"): 1784770426,
+    ("b75e2db3de9304f5", "c5", "bwd_dq"): 1018047425,
+    ("b75e2db3de9304f5", "c5", "bwd_preprocess"): 174112562,
+    ("b75e2db3de9304f5", "c5", "fwd"): 1649936686,
+    ("b75e2db3de9304f5", "d256", "bwd_dkdv"): 879958884,
+    ("b75e2db3de9304f5", "d256", "bwd_dq"): 676687646,
+    ("b75e2db3de9304f5", "d256", "bwd_preprocess"): 135865677,
+    ("b75e2db3de9304f5", "d256", "fwd"): 607841317,
 }
 
 
