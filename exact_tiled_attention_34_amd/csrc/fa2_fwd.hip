@@ -80,9 +80,16 @@ struct FwdCfg {
   // d256 causal -3 % (MI355X).
   using VL = TrRowTile<D>;
   static constexpr int VTILE = VL::elems(STAGE);
-  // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint);
-  // fewer at D = 96, whose three wavefronts per SIMD have 170 registers each
+  // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint
+  // of the P V products); fewer at D = 96, whose three wavefronts per SIMD
+  // have 170 registers each
   static constexpr int READ_AHEAD = D == 96 ? 4 : 6;
+  // stages of the S^T products whose K operands are read ahead (scores())
+  static constexpr int SCORE_PF = 2;
+  // D = 256: the Q operands (64 registers) sit in accumulator registers, as
+  // MFMA B operands may, which leaves the vector registers room for operand
+  // reads in flight (one wavefront per SIMD: nothing else hides them)
+  static constexpr bool Q_IN_AGPR = D == 256;
   // When V^T is padded to whole 32-feature blocks (D = 80), its first padding
   // row holds ones: O^T row D then accumulates the row sum of the rounded P
   // (scaled with O by every rescale), at no cost, instead of a sum in the
@@ -133,18 +140,31 @@ struct FwdWave {
       for (int mb = 0; mb < C::NDB; ++mb) vtr[rd][mb] = tr_lane_elem<typename C::VL>(lane, rd, mb);
   }
 
-  // S^T (64 keys x this wave's 32 queries) of the K tile at kt.
+  // S^T (64 keys x this wave's 32 queries) of the K tile at kt: a fixed list
+  // of DK stages, one k-step of every 32-key block each (the blocks' MFMA
+  // chains interleaved), each stage's K operands read SCORE_PF stages ahead.
+  // Left to the scheduler, the reads went out one at a time, each waited for
+  // right before its MFMA, and the blocks' chains ran one after the other.
   __device__ __forceinline__ void scores(const uint16_t* kt, f32x16 (&sacc)[C::KB]) const {
+    constexpr int PF = C::SCORE_PF;
+    u32x4 rk[C::DK][C::KB];
+    auto fetch = [&](int s) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
+      for (int kb = 0; kb < C::KB; ++kb) rk[s][kb] = lds_read16(kt + off.rd(s, kb));
+    };
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < C::DK; ++s)
-        sacc[kb] = E::mfma(lds_read16(kt + off.rd(s, kb)), qf[s],
-                                sacc[kb]);
+    for (int s = 0; s < PF; ++s) fetch(s);
+#pragma unroll
+    for (int s = 0; s < C::DK; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) sacc[kb] = E::mfma(rk[s][kb], qf[s], sacc[kb]);
+      if (s + PF < C::DK) fetch(s + PF);
+      sched_fence();
     }
-    mfma_pipeline_hint<1, C::KB * C::DK, C::KB * C::DK, C::READ_AHEAD>();
   }
 
   // P = 2^(c S - mc) for score blocks [KB0, KB0 + NKB), packed to the storage
@@ -385,6 +405,7 @@ __global__ __launch_bounds__((FwdCfg<D, CAUSAL>::THREADS), (FwdCfg<D, CAUSAL>::W
     u32x4 z = {0u, 0u, 0u, 0u};
     if (w.q_lane < Nq) z = ld_global16(Qh + (size_t)w.q_lane * Q.sr + s * 16 + 8 * w.lh);
     w.qf[s] = z;
+    if constexpr (C::Q_IN_AGPR) asm volatile("" : "+a"(w.qf[s]));
   }
 
   // Stage J uses buffer J % 2; unrolled by two so the buffer is an immediate.
