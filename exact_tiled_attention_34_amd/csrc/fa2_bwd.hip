@@ -727,8 +727,6 @@ struct DqCfg {
   // 96 use its 128-feature rows (WideRowTile).
   using TileL = std::conditional_t<(D == 80 || D == 96), WideRowTile<D>, RowTile<D>>;
   static constexpr int TILE = TileL::elems(BC);
-  // LDS operand reads kept in flight ahead of the MFMAs (the scheduling hint)
-  static constexpr int READ_AHEAD = D == 256 ? 2 : 6;
   // Where registers allow, the dP^T products start from delta (16 registers
   // holding this lane's delta) with dO negated, leaving delta - dP^T: dS^T =
   // -(P^T acc) then takes one multiply instead of a subtraction and one
@@ -736,6 +734,18 @@ struct DqCfg {
   // MI355X).  At D = 128 it measured even (B1 H16 N16384 d128 causal) or 1 %
   // slower (B8 H16 N2048 d128).
   static constexpr bool DELTA_INIT = D != 128;
+  // With one wavefront per SIMD (D = 256) nothing hides an LDS read's
+  // latency, and left to the scheduler the products waited for their reads
+  // (a third of the MFMAs behind a full wait): there tile() issues them as
+  // explicit stage lists, the S^T and dP^T operands SCORE_PF k-steps ahead
+  // and the K^T operands of the dQ products DQ_PF products ahead (B1 H16
+  // N8192 d256 causal dQ -3.6 % on MI355X).  With two wavefronts per SIMD the
+  // same lists measured even or up to 3 % slower than the scheduled loops,
+  // whose LDS reads a scheduling hint keeps READ_AHEAD deep.
+  static constexpr bool STAGED = D == 256;
+  static constexpr int SCORE_PF = 2;
+  static constexpr int DQ_PF = 2;
+  static constexpr int READ_AHEAD = 6;
 };
 
 template <int D, bool CAUSAL, class E>
@@ -767,20 +777,59 @@ struct DqWave {
                                        float scale_log2) {
     f32x16 sacc[C::KB], pacc[C::KB];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sacc[kb][i] = 0.f;
         pacc[kb][i] = C::DELTA_INIT ? dl16[i] : 0.f;
       }
+    if constexpr (C::STAGED) {
+      // DK stages, one k-step of every S^T and dP^T chain each
+      constexpr int PF = C::SCORE_PF;
+      u32x4 rk[C::DK][C::KB], rv[C::DK][C::KB];
+      auto fetch = [&](int s) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          rk[s][kb] = lds_read16(kt + off.rd(s, kb));
+          rv[s][kb] = lds_read16(vt + off.rd(s, kb));
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < PF; ++s) fetch(s);
 #pragma unroll
       for (int s = 0; s < C::DK; ++s) {
-        const int o = off.rd(s, kb);
-        sacc[kb] = E::mfma(lds_read16(kt + o), qf[s], sacc[kb]);
-        pacc[kb] = E::mfma(lds_read16(vt + o), dof[s], pacc[kb]);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          sacc[kb] = E::mfma(rk[s][kb], qf[s], sacc[kb]);
+          pacc[kb] = E::mfma(rv[s][kb], dof[s], pacc[kb]);
+        }
+        if (s + PF < C::DK) fetch(s + PF);
+        sched_fence();
       }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < C::DK; ++s) {
+          const int o = off.rd(s, kb);
+          sacc[kb] = E::mfma(lds_read16(kt + o), qf[s], sacc[kb]);
+          pacc[kb] = E::mfma(lds_read16(vt + o), dof[s], pacc[kb]);
+        }
+      mfma_pipeline_hint<1, 2 * C::KB * C::DK, 2 * C::KB * C::DK, C::READ_AHEAD>();
     }
-    mfma_pipeline_hint<1, 2 * C::KB * C::DK, 2 * C::KB * C::DK, C::READ_AHEAD>();
+    // dQ products t: 16-key chunk t / NDB of feature block t % NDB, K^T by two
+    // transposed reads of the K tile (staged: the first ones go out before
+    // the exponentials)
+    constexpr int R16 = C::TileL::ROWS16;
+    constexpr int NT = (C::BC / 16) * C::NDB;
+    u32x4 rt[NT];
+    auto fetch_t = [&](int t) {
+      const int c = t / C::NDB, mb = t % C::NDB;
+      rt[t] = lds_read_tr(kt + tro[0][mb] + c * R16, kt + tro[1][mb] + c * R16);
+    };
+    if constexpr (C::STAGED)
+#pragma unroll
+      for (int t = 0; t < C::DQ_PF; ++t) fetch_t(t);
     if (mask) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -801,17 +850,25 @@ struct DqWave {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) dsw[kb][i >> 1] = E::pack2(pacc[kb][i], pacc[kb][i + 1]);
     }
-    // dQ^T (d x query) += K^T (d x 16 keys) dS^T (16 keys x query), K^T by two
-    // transposed reads of the K tile.
-    constexpr int R16 = C::TileL::ROWS16;
+    // dQ^T (d x query) += K^T (d x 16 keys) dS^T (16 keys x query)
+    if constexpr (C::STAGED) {
+      sched_fence();
 #pragma unroll
-    for (int c = 0; c < C::BC / 16; ++c) {
-      const u32x4 b = acc_chunk(dsw[c >> 1], c & 1);
+      for (int t = 0; t < NT; ++t) {
+        const int c = t / C::NDB;
+        dqacc[t % C::NDB] = E::mfma(rt[t], acc_chunk(dsw[c >> 1], c & 1), dqacc[t % C::NDB]);
+        if (t + C::DQ_PF < NT) fetch_t(t + C::DQ_PF);
+        sched_fence();
+      }
+    } else {
 #pragma unroll
-      for (int mb = 0; mb < C::NDB; ++mb)
-        dqacc[mb] = E::mfma(lds_read_tr(kt + tro[0][mb] + c * R16, kt + tro[1][mb] + c * R16), b, dqacc[mb]);
+      for (int t = 0; t < NT; ++t) {
+        const int c = t / C::NDB;
+        fetch_t(t);
+        dqacc[t % C::NDB] = E::mfma(rt[t], acc_chunk(dsw[c >> 1], c & 1), dqacc[t % C::NDB]);
+      }
+      mfma_pipeline_hint<2, NT, 2 * NT, C::READ_AHEAD, 2>();
     }
-    mfma_pipeline_hint<2, (C::BC / 16) * C::NDB, 2 * (C::BC / 16) * C::NDB, C::READ_AHEAD, 2>();
   }
 };
 
