@@ -868,13 +868,16 @@ struct DqWave {
 #pragma unroll
       for (int t = 0; t < C::DQ_PF; ++t) fetch_t(t);
     if (mask) {
+      // register i of block kb: key key0 + 4 lh + (kb 32 + 8 (i / 4) + i % 4);
+      // one per-lane bound on the constant offset covers both tests (B4 H32
+      // N4096 d64 causal dQ -1.1 % on MI355X)
+      const int last = CAUSAL ? min(Nk - 1, key_last) : Nk - 1;
+      const int lim = last - key0 - 4 * lh;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= Nk || (CAUSAL && key > key_last)) sacc[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[kb][i] = -INFINITY;
     }
     uint32_t dsw[C::KB][8];
 #pragma unroll
