@@ -77,30 +77,30 @@ def parse():
 # plain copy of known size (bench.py --calibrate-copy).  Valid only for the
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
-    ("a8e4a6120c380750", "c1", "bwd_dkdv"): 119294,
-    ("a8e4a6120c380750", "c1", "bwd_dq"): 100990,
-    ("a8e4a6120c380750", "c1", "bwd_preprocess"): 93694,
-    ("a8e4a6120c380750", "c1", "fwd"): 92158,
-    ("a8e4a6120c380750", "c2", "bwd_dkdv"): 1360359315,
-    ("a8e4a6120c380750", "c2", "bwd_dq"): 740450971,
-    ("a8e4a6120c380750", "c2", "bwd_preprocess"): 137429479,
-    ("a8e4a6120c380750", "c2", "fwd"): 672340655,
-    ("a8e4a6120c380750", "c3", "bwd_dkdv"): 1339115591,
-    ("a8e4a6120c380750", "c3", "bwd_dq"): 809635143,
-    ("a8e4a6120c380750", "c3", "bwd_preprocess"): 140569847,
-    ("a8e4a6120c380750", "c3", "fwd"): 757398445,
-    ("a8e4a6120c380750", "c4", "bwd_dkdv"): 870636345,
-    ("a8e4a6120c380750", "c4", "bwd_dq"): 698406205,
-    ("a8e4a6120c380750", "c4", "bwd_preprocess"): 137430567,
-    ("a8e4a6120c380750", "c4", "fwd"): 606720587,
-    ("a8e4a6120c380750", "c5", "bwd_dkdv"): 1784568290,
-    ("a8e4a6120c380750", "c5", "bwd_dq"): 1018117240,
-    ("a8e4a6120c380750", "c5", "bwd_preprocess"): 174112493,
-    ("a8e4a6120c380750", "c5", "fwd"): 1674651842,
-    ("a8e4a6120c380750", "d256", "bwd_dkdv"): 886978772,
-    ("a8e4a6120c380750", "d256", "bwd_dq"): 655155731,
-    ("a8e4a6120c380750", "d256", "bwd_preprocess"): 135862352,
-    ("a8e4a6120c380750", "d256", "fwd"): 602984148,
+    ("b00b245663fe3d0e", "c1", "bwd_dkdv"): 121342,
+    ("b00b245663fe3d0e", "c1", "bwd_dq"): 100478,
+    ("b00b245663fe3d0e", "c1", "bwd_preprocess"): 93694,
+    ("b00b245663fe3d0e", "c1", "fwd"): 93566,
+    ("b00b245663fe3d0e", "c2", "bwd_dkdv"): 1359247132,
+    ("b00b245663fe3d0e", "c2", "bwd_dq"): 740454956,
+    ("b00b245663fe3d0e", "c2", "bwd_preprocess"): 137428868,
+    ("b00b245663fe3d0e", "c2", "fwd"): 672339697,
+    ("b00b245663fe3d0e", "c3", "bwd_dkdv"): 1341045979,
+    ("b00b245663fe3d0e", "c3", "bwd_dq"): 809622758,
+    ("b00b245663fe3d0e", "c3", "bwd_preprocess"): 140569876,
+    ("b00b245663fe3d0e", "c3", "fwd"): 769709183,
+    ("b00b245663fe3d0e", "c4", "bwd_dkdv"): 868863091,
+    ("b00b245663fe3d0e", "c4", "bwd_dq"): 704096427,
+    ("b00b245663fe3d0e", "c4", "bwd_preprocess"): 137430628,
+    ("b00b245663fe3d0e", "c4", "fwd"): 611988075,
+    ("b00b245663fe3d0e", "c5", "bwd_dkdv"): 1784537709,
+    ("b00b245663fe3d0e", "c5", "bwd_dq"): 1019088417,
+    ("b00b245663fe3d0e", "c5", "bwd_preprocess"): 174112338,
+    ("b00b245663fe3d0e", "c5", "fwd"): 1673732790,
+    ("b00b245663fe3d0e", "d256", "bwd_dkdv"): 886902822,
+    ("b00b245663fe3d0e", "d256", "bwd_dq"): 651797511,
+    ("b00b245663fe3d0e", "d256", "bwd_preprocess"): 135862765,
+    ("b00b245663fe3d0e", "d256", "fwd"): 631056256,
 }
 
 
