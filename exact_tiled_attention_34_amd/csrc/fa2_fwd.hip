@@ -50,8 +50,10 @@ namespace {
 // D = 64 (four wavefronts per SIMD in 124 VGPRs); at D = 80 two workgroups of
 // 4 wavefronts are as fast as 12 wavefronts and 5 % faster than 8.  At D = 256
 // a wavefront's Q operands (64 registers) and O accumulators (128) leave room
-// for one wavefront per SIMD only: 4 wavefronts, 32-key tiles (the 64-key
-// K and V^T tiles would not fit LDS twice).
+// for one wavefront per SIMD only: 4 wavefronts.  Its 64-key K and V tiles
+// take 128 KiB of LDS double-buffered; against 32-key tiles, whose score
+// products were one dependent chain of MFMAs per tile, B1 H16 N8192 d256
+// causal forward -4.5 % on MI355X.
 template <int D, bool CAUSAL = false>
 struct FwdCfg {
   static constexpr int WAVES = D == 96 ? 12 : D == 80 || D == 256 ? 4 : 8;
@@ -59,7 +61,7 @@ struct FwdCfg {
   static constexpr int WAVES_PER_SIMD = WAVES * WGS_PER_CU / 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BC = D == 256 ? 32 : 64;   // keys per K/V tile (32 or 64)
+  static constexpr int BC = 64;                   // keys per K/V tile
   static constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
   static constexpr int DP = (D + 31) / 32 * 32;   // O^T rows padded to whole 32-row MFMA blocks
   static constexpr int NDB = DP / 32;
