@@ -744,12 +744,13 @@ __global__ __launch_bounds__(DkdvSplitCfg<D>::THREADS, 1) void bwd_dkdv_split_ke
 template <int D>
 struct DqCfg {
   // At D = 256 the Q and dO operands (128 registers) and dQ accumulators (128)
-  // leave room for one wavefront per SIMD: 4 wavefronts and 32-key tiles (so
-  // that the K, V and K^T tiles fit LDS twice).
+  // leave room for one wavefront per SIMD: 4 wavefronts.  Its 64-key K and V
+  // tiles take 128 KiB of LDS double-buffered (B1 H16 N8192 d256 causal dQ
+  // -1 % against 32-key tiles on MI355X).
   static constexpr int WAVES = D == 256 ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BR = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BC = D == 256 ? 32 : 64;   // keys per K/V tile (32 or 64)
+  static constexpr int BC = 64;                   // keys per K/V tile
   static constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
