@@ -77,30 +77,30 @@ def parse():
 # plain copy of known size (bench.py --calibrate-copy).  Valid only for the
 # kernel sources it was measured on: keyed by their hash, else reported null.
 MEASURED_TRAFFIC = {
-    ("b00b245663fe3d0e", "c1", "bwd_dkdv"): 121342,
-    ("b00b245663fe3d0e", "c1", "bwd_dq"): 100478,
-    ("b00b245663fe3d0e", "c1", "bwd_preprocess"): 93694,
-    ("b00b245663fe3d0e", "c1", "fwd"): 93566,
-    ("b00b245663fe3d0e", "c2", "bwd_dkdv"): 1359247132,
-    ("b00b245663fe3d0e", "c2", "bwd_dq"): 740454956,
-    ("b00b245663fe3d0e", "c2", "bwd_preprocess"): 137428868,
-    ("b00b245663fe3d0e", "c2", "fwd"): 672339697,
-    ("b00b245663fe3d0e", "c3", "bwd_dkdv"): 1341045979,
-    ("b00b245663fe3d0e", "c3", "bwd_dq"): 809622758,
-    ("b00b245663fe3d0e", "c3", "bwd_preprocess"): 140569876,
-    ("b00b245663fe3d0e", "c3", "fwd"): 769709183,
-    ("b00b245663fe3d0e", "c4", "bwd_dkdv"): 868863091,
-    ("b00b245663fe3d0e", "c4", "bwd_dq"): 704096427,
-    ("b00b245663fe3d0e", "c4", "bwd_preprocess"): 137430628,
-    ("b00b245663fe3d0e", "c4", "fwd"): 611988075,
-    ("b00b245663fe3d0e", "c5", "bwd_dkdv"): 1784537709,
-    ("b00b245663fe3d0e", "c5", "bwd_dq"): 1019088417,
-    ("b00b245663fe3d0e", "c5", "bwd_preprocess"): 174112338,
-    ("b00b245663fe3d0e", "c5", "fwd"): 1673732790,
-    ("b00b245663fe3d0e", "d256", "bwd_dkdv"): 886902822,
-    ("b00b245663fe3d0e", "d256", "bwd_dq"): 651797511,
-    ("b00b245663fe3d0e", "d256", "bwd_preprocess"): 135862765,
-    ("b00b245663fe3d0e", "d256", "fwd"): 631056256,
+    ("89942ee7b2195fc5", "c1", "bwd_dkdv"): 121342,
+    ("89942ee7b2195fc5", "c1", "bwd_dq"): 100606,
+    ("89942ee7b2195fc5", "c1", "bwd_preprocess"): 93694,
+    ("89942ee7b2195fc5", "c1", "fwd"): 93566,
+    ("89942ee7b2195fc5", "c2", "bwd_dkdv"): 1359901029,
+    ("89942ee7b2195fc5", "c2", "bwd_dq"): 740455291,
+    ("89942ee7b2195fc5", "c2", "bwd_preprocess"): 137429662,
+    ("89942ee7b2195fc5", "c2", "fwd"): 672340236,
+    ("89942ee7b2195fc5", "c3", "bwd_dkdv"): 1342110497,
+    ("89942ee7b2195fc5", "c3", "bwd_dq"): 809622315,
+    ("89942ee7b2195fc5", "c3", "bwd_preprocess"): 140569917,
+    ("89942ee7b2195fc5", "c3", "fwd"): 771783033,
+    ("89942ee7b2195fc5", "c4", "bwd_dkdv"): 868659260,
+    ("89942ee7b2195fc5", "c4", "bwd_dq"): 697638631,
+    ("89942ee7b2195fc5", "c4", "bwd_preprocess"): 137430718,
+    ("89942ee7b2195fc5", "c4", "fwd"): 604311883,
+    ("89942ee7b2195fc5", "c5", "bwd_dkdv"): 1784485791,
+    ("89942ee7b2195fc5", "c5", "bwd_dq"): 1018881464,
+    ("89942ee7b2195fc5", "c5", "bwd_preprocess"): 174112677,
+    ("89942ee7b2195fc5", "c5", "fwd"): 1687294868,
+    ("89942ee7b2195fc5", "d256", "bwd_dkdv"): 889234867,
+    ("89942ee7b2195fc5", "d256", "bwd_dq"): 666411706,
+    ("89942ee7b2195fc5", "d256", "bwd_preprocess"): 135863990,
+    ("89942ee7b2195fc5", "d256", "fwd"): 749313910,
 }
 
 
