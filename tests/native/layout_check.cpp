@@ -215,11 +215,11 @@ int main() {
     check_dma<64, 32, 512>(max_n, 64 * mult);
     check_dma<128, 32, 512>(max_n, 128 * mult);
   }
-  // head dim 256: 32-key tiles of the forward and dQ kernels (256 threads)
+  // head dim 256: 64-key K (forward, dQ) and V (dQ) tiles, 256 threads
   for (int mult : {1, 2, 3}) {
-    check_dma<256, 32, 256>(max_n, 256 * mult);
+    check_dma<256, 64, 256>(max_n, 256 * mult);
   }
-  check_dma<256, 32, 256>(max_n, 264);
+  check_dma<256, 64, 256>(max_n, 264);
   // V tiles of the forward (TrRowTile): the thread counts of its workgroups
   for (int mult : {1, 2, 3}) {
     check_dma<64, 64, 512, TrRowTile<64>>(max_n, 64 * mult);
@@ -227,16 +227,16 @@ int main() {
     check_dma<80, 64, 256, TrRowTile<80>>(max_n, 80 * mult);
     check_dma<96, 64, 768, TrRowTile<96>>(max_n, 96 * mult);
     check_dma<128, 64, 512, TrRowTile<128>>(max_n, 128 * mult);
-    check_dma<256, 32, 256, TrRowTile<256>>(max_n, 256 * mult);
+    check_dma<256, 64, 256, TrRowTile<256>>(max_n, 256 * mult);
   }
-  check_dma<256, 32, 256, TrRowTile<256>>(max_n, 264);
+  check_dma<256, 64, 256, TrRowTile<256>>(max_n, 264);
   check_dma<80, 64, 256, TrRowTile<80>>(max_n, 88);
   check_tr_reads<64, 64>();
   check_tr_reads<64, 128>();
   check_tr_reads<80, 64>();
   check_tr_reads<96, 64>();
   check_tr_reads<128, 64>();
-  check_tr_reads<256, 32>();
+  check_tr_reads<256, 64>();
   // Q and dO tiles of the dK/dV pass (copied, read row-wise and transposed)
   for (int mult : {1, 2, 3}) {
     check_dma<64, 64, 256, RowTile<64>>(max_n, 64 * mult);
